@@ -1,0 +1,206 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: paged KV-cache write and PagedAttention
+ * decode for AMD Instinct MI355X (gfx950).
+ *
+ * The method: the KV cache lives in a pool of fixed-size physical blocks
+ * (default 16 tokens each), allocated once; every sequence reaches its
+ * blocks through a block table that maps logical block j to a physical block,
+ * so a sequence's storage need not be contiguous and blocks can be shared
+ * between sequences (dpshk.com PagedAttention article "企业官网建设流程全解析",
+ * sections 2.1 Block / BlockTable, 2.3 sharing by reference count, 3.2 block
+ * pre-allocation and FP8 storage; page "vLLM的诞生背景：大模型推理的痛点与
+ * PagedAttention的破局", section "PagedAttention的破局思路"; page
+ * "PagedAttention 与连续批处理：LLM Serving 的底层架构拆解", section
+ * "PagedAttention：把显存做成虚拟内存").  Decode attention is
+ * softmax(q K^T * scale) V over the whole context (dpshk.com article,
+ * section 2.2), computed one block at a time with a running max and sum.
+ *
+ * Conventions for every call
+ *   - All array pointers are DEVICE pointers (hipMalloc / torch CUDA tensors),
+ *     row-major and densely packed in the layouts given below.
+ *   - The caller owns and allocates every buffer, including the pool and the
+ *     workspace; the library allocates and frees nothing and keeps no state
+ *     between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without synchronising.  Buffers must stay alive
+ *     until the stream has passed the call.  Calls are thread-safe.
+ *   - All argument checks happen on the host before anything is enqueued; a
+ *     failing check returns a status and touches no memory.  A failed launch
+ *     returns PKV_ERR_HIP.  Nothing is thrown across the ABI.
+ *   - Block ids in block tables and slots in slot mappings must lie inside the
+ *     pool; context_lens[i] must not exceed max_blocks_per_seq * block_size.
+ *     These are the caller's contract and are not checked on the device.
+ *
+ * Layouts (S sequences, H query heads, H_kv KV heads, D head size,
+ * bs block size, T new tokens):
+ *   query, out              [S][H][D]
+ *   key_cache, value_cache  [num_blocks][H_kv][bs][D]   token rows of D
+ *                           elements per (block, KV head) tile
+ *   key_scale, value_scale  [num_blocks][H_kv] float32 (FP8 caches only)
+ *   block_tables            int32 [S][max_blocks_per_seq]
+ *   context_lens            int32 [S]   tokens in the cache, the current
+ *                           step's token included (it must be written first)
+ *   key, value (new rows)   [T][H_kv][D]
+ *   slot_mapping            int32 [T]   slot = physical_block * bs + offset;
+ *                           a negative slot skips the token
+ *
+ * Supported: D in {64, 128}; bs in {8, 16, 32}; H a multiple of H_kv.
+ * Query head h reads KV head h / (H / H_kv).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_F32 = 0,       /* IEEE binary32 */
+  PKV_BF16 = 1,      /* bfloat16 */
+  PKV_FP8_E4M3 = 2   /* OCP FP8 E4M3FN codes (cache only) */
+} pkv_dtype_t;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,       /* a required pointer is NULL */
+  PKV_ERR_SHAPE = 2,      /* unsupported or inconsistent size */
+  PKV_ERR_DTYPE = 3,      /* unsupported dtype or dtype combination */
+  PKV_ERR_WORKSPACE = 4,  /* workspace missing or too small */
+  PKV_ERR_HIP = 5         /* a HIP launch failed */
+} pkv_status_t;
+
+/*
+ * paged_kv_cache_write -- scatter each new token's K and V rows into its
+ * paged slot.  For token t with slot s = slot_mapping[t] >= 0, block
+ * b = s / bs and offset o = s % bs, and every KV head h:
+ *   key_cache[b][h][o][:] = key[t][h][:],  value_cache likewise.
+ * (Block/BlockTable structure: dpshk.com article, section 2.1; the slot
+ * mapping is the write side of the block table.)
+ *
+ *   src_dtype == cache_dtype in {PKV_F32, PKV_BF16}: the bits are copied
+ *     unchanged; key_scale, value_scale and workspace are ignored (may be
+ *     NULL).
+ *   cache_dtype == PKV_FP8_E4M3, src_dtype in {PKV_BF16, PKV_F32}: FP8
+ *     storage of blocks (dpshk.com article, section 3.2).  One float32 scale
+ *     per (block, KV head), separately for K and V.  If this call writes
+ *     offset 0 of block b, the scales of b are set from the largest magnitude
+ *     among the tokens this call writes into b:
+ *       scale = max(amax / 448, FLT_MIN)          (float32 arithmetic)
+ *     otherwise the stored scales of b are kept.  Each element is stored as
+ *     the E4M3FN code of the float32 quotient x / scale, rounded to nearest
+ *     even, saturated to +-448 (NaN -> 0x7F).  A block's first write must
+ *     include its offset 0.  Requires workspace of at least
+ *     paged_kv_cache_write_workspace_size(...) bytes (any contents).
+ *
+ * Slots within one call must be distinct; duplicate slots race.
+ */
+pkv_status_t paged_kv_cache_write(
+    const void* key, const void* value,
+    void* key_cache, void* value_cache,
+    float* key_scale, float* value_scale,
+    const int32_t* slot_mapping,
+    int32_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t num_blocks,
+    int32_t src_dtype, int32_t cache_dtype,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/* Workspace bytes paged_kv_cache_write needs (0 unless the cache is FP8). */
+size_t paged_kv_cache_write_workspace_size(
+    int32_t num_tokens, int32_t num_kv_heads, int32_t num_blocks,
+    int32_t cache_dtype);
+
+/*
+ * paged_attention_decode -- one query token per sequence attends over its
+ * paged context (dpshk.com article, section 2.2: softmax(QK^T/sqrt(d))V,
+ * evaluated over the whole context; page "PagedAttention 与连续批处理…",
+ * section "PagedAttention：把显存做成虚拟内存": each page is found through
+ * the page table).  For sequence i with n = context_lens[i] and head h:
+ *   out[i][h][:] = sum_t softmax_t(scale * q[i][h] . K[t]) V[t],
+ * t = 0..n-1, where token t of sequence i is row t % bs of physical block
+ * block_tables[i][t / bs], KV head h / (H / H_kv).  n = 0 gives zeros.
+ * Accumulation is float32; out has the query dtype (bf16 rounded to
+ * nearest even).
+ *
+ *   q_dtype/cache_dtype pairs: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ *   FP8 caches are dequantised as code_value * key_scale[b][h] (value_scale
+ *   likewise); scales are ignored otherwise (may be NULL).
+ *   max_context_len must be >= every context_lens[i]; it sizes the grid so
+ *   the host never reads device memory.
+ *   partition_size (tokens, multiple of bs, or 0 = library choice): contexts
+ *   longer than one partition are split, each partition is attended on its
+ *   own, and a second kernel merges the partial results.
+ *   workspace: at least paged_attention_decode_workspace_size(...) bytes
+ *   (any contents; may be NULL when that size is 0).
+ */
+pkv_status_t paged_attention_decode(
+    void* out, const void* query,
+    const void* key_cache, const void* value_cache,
+    const float* key_scale, const float* value_scale,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t max_context_len,
+    float scale, int32_t q_dtype, int32_t cache_dtype,
+    int32_t partition_size,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/* The partition size paged_attention_decode uses for these arguments
+ * (resolves partition_size == 0 to the library's choice); negative on
+ * invalid arguments. */
+int32_t paged_attention_decode_partition_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_context_len,
+    int32_t q_dtype, int32_t cache_dtype, int32_t partition_size);
+
+/* Workspace bytes paged_attention_decode needs for these arguments. */
+size_t paged_attention_decode_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_context_len,
+    int32_t q_dtype, int32_t cache_dtype, int32_t partition_size);
+
+/*
+ * The two phases of paged_attention_decode, for callers that schedule or
+ * time them apart.  Same arguments and the same partition choice.
+ * _partitions attends every (sequence, KV head, partition); sequences that
+ * fit in one partition get their final output here.  _reduce then merges the
+ * partitions of the longer sequences (a no-op launch-free return when no
+ * sequence can span two partitions).  Calling _partitions then _reduce on
+ * one stream equals one paged_attention_decode call.
+ */
+pkv_status_t paged_attention_decode_partitions(
+    void* out, const void* query,
+    const void* key_cache, const void* value_cache,
+    const float* key_scale, const float* value_scale,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t max_context_len,
+    float scale, int32_t q_dtype, int32_t cache_dtype,
+    int32_t partition_size,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
+pkv_status_t paged_attention_decode_reduce(
+    void* out, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_context_len,
+    int32_t q_dtype, int32_t cache_dtype, int32_t partition_size,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* pkv_status_string(int32_t status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,33 @@
+"""PagedAttention decode and paged KV write for AMD MI355X (gfx950).
+
+The compute lives in libpagedkv.so (hand-written HIP kernels behind a C ABI,
+declared in include/pagedkv.h); this package is its thin Python binding plus
+host-side block bookkeeping.  There is no fallback: if the library is not
+built, every call raises.
+"""
+
+from ._lib import (
+    PKV_BF16,
+    PKV_F32,
+    PKV_FP8_E4M3,
+    PagedKVError,
+    decode_partition_size,
+    decode_workspace_size,
+    dtype_code,
+    load,
+    paged_attention_decode,
+    paged_attention_decode_partitions,
+    paged_attention_decode_reduce,
+    paged_kv_cache_write,
+    status_string,
+    write_workspace_size,
+)
+from .block_manager import BlockManager, OutOfBlocks
+
+__all__ = [
+    "PKV_BF16", "PKV_F32", "PKV_FP8_E4M3", "PagedKVError", "BlockManager", "OutOfBlocks",
+    "decode_partition_size", "decode_workspace_size", "dtype_code", "load",
+    "paged_attention_decode", "paged_attention_decode_partitions",
+    "paged_attention_decode_reduce", "paged_kv_cache_write", "status_string",
+    "write_workspace_size",
+]

@@ -1,0 +1,251 @@
+// C ABI of libpagedkv: host-side argument checks, partition choice, workspace
+// layout and kernel dispatch.  Nothing here touches device memory; every
+// check happens before the first launch.
+#include <hip/hip_runtime.h>
+
+#include "pkv_internal.h"
+
+using namespace pkv;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kDefaultPartition = 512;
+
+bool valid_d(int D) { return D == 64 || D == 128; }
+bool valid_bs(int bs) { return bs == 8 || bs == 16 || bs == 32; }
+
+bool decode_pair_ok(int q, int c) {
+  return (q == PKV_F32 && c == PKV_F32) || (q == PKV_BF16 && c == PKV_BF16) ||
+         (q == PKV_BF16 && c == PKV_FP8_E4M3);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Partition size in tokens, or -1.  A context that fits one partition is
+// finished by the partition kernel itself; longer contexts are split into
+// partitions of kDefaultPartition tokens so that long sequences spread over
+// many workgroups.
+int resolve_partition(int bs, int max_ctx, int requested) {
+  if (requested < 0) return -1;
+  if (requested > 0) return requested % bs == 0 ? requested : -1;
+  if (max_ctx <= kDefaultPartition) {
+    const int p = ((max_ctx + bs - 1) / bs) * bs;
+    return p < bs ? bs : p;
+  }
+  return kDefaultPartition;
+}
+
+int num_partitions(int max_ctx, int P) {
+  const int np = (max_ctx + P - 1) / P;
+  return np < 1 ? 1 : np;
+}
+
+pkv_status_t check_decode_shape(int S, int H, int H_kv, int D, int bs, int max_ctx, int q,
+                                int c) {
+  if (S < 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0) return PKV_ERR_SHAPE;
+  if (!valid_d(D) || !valid_bs(bs) || max_ctx < 0) return PKV_ERR_SHAPE;
+  if (!decode_pair_ok(q, c)) return PKV_ERR_DTYPE;
+  return PKV_OK;
+}
+
+size_t decode_workspace(int S, int H, int D, int max_ctx, int P) {
+  const int np = num_partitions(max_ctx, P);
+  if (np <= 1) return 0;
+  const size_t rows = (size_t)S * H * np;
+  return 2 * align256(rows * sizeof(float)) + align256(rows * D * sizeof(float));
+}
+
+struct DecodeSetup {
+  pkv_status_t status;
+  DecodeArgs a;
+};
+
+DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
+                         const void* value_cache, const float* key_scale,
+                         const float* value_scale, const int32_t* block_tables,
+                         const int32_t* context_lens, int S, int H, int H_kv, int D, int bs,
+                         int max_blocks, int max_ctx, float scale, int q, int c, int partition,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         bool need_inputs) {
+  DecodeSetup r{};
+  r.status = check_decode_shape(S, H, H_kv, D, bs, max_ctx, q, c);
+  if (r.status != PKV_OK) return r;
+  if (need_inputs && (max_blocks <= 0 || (long long)max_blocks * bs < max_ctx)) {
+    r.status = PKV_ERR_SHAPE;
+    return r;
+  }
+  const int P = resolve_partition(bs, max_ctx, partition);
+  if (P <= 0) {
+    r.status = PKV_ERR_SHAPE;
+    return r;
+  }
+  if (!out || !context_lens) {
+    r.status = PKV_ERR_NULL;
+    return r;
+  }
+  if (need_inputs) {
+    if (!query || !key_cache || !value_cache || !block_tables) {
+      r.status = PKV_ERR_NULL;
+      return r;
+    }
+    if (c == PKV_FP8_E4M3 && (!key_scale || !value_scale)) {
+      r.status = PKV_ERR_NULL;
+      return r;
+    }
+  }
+  const size_t need = decode_workspace(S, H, D, max_ctx, P);
+  if (need > 0 && (!workspace || workspace_bytes < need)) {
+    r.status = PKV_ERR_WORKSPACE;
+    return r;
+  }
+  DecodeArgs& a = r.a;
+  a.out = out; a.q = query; a.key_cache = key_cache; a.value_cache = value_cache;
+  a.key_scale = key_scale; a.value_scale = value_scale;
+  a.tables = block_tables; a.lens = context_lens;
+  a.S = S; a.H = H; a.H_kv = H_kv; a.D = D; a.bs = bs; a.max_blocks = max_blocks;
+  a.max_ctx = max_ctx; a.scale = scale; a.q_dtype = q; a.cache_dtype = c;
+  a.P = P; a.NP = num_partitions(max_ctx, P);
+  if (need > 0) {
+    const size_t rows = (size_t)S * H * a.NP;
+    char* ws = reinterpret_cast<char*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(ws);
+    a.ws_l = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+    a.ws_acc = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  }
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  return r;
+}
+
+pkv_status_t hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int32_t s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "unsupported or inconsistent size";
+    case PKV_ERR_DTYPE: return "unsupported dtype combination";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t pkv_version(void) { return kVersion; }
+
+size_t paged_kv_cache_write_workspace_size(int32_t num_tokens, int32_t num_kv_heads,
+                                           int32_t num_blocks, int32_t cache_dtype) {
+  (void)num_tokens;
+  if (cache_dtype != PKV_FP8_E4M3 || num_blocks <= 0 || num_kv_heads <= 0) return 0;
+  return kv_write_fp8_workspace(num_blocks, num_kv_heads);
+}
+
+pkv_status_t paged_kv_cache_write(const void* key, const void* value, void* key_cache,
+                                  void* value_cache, float* key_scale, float* value_scale,
+                                  const int32_t* slot_mapping, int32_t num_tokens,
+                                  int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                  int32_t num_blocks, int32_t src_dtype, int32_t cache_dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (!valid_d(head_size) || !valid_bs(block_size)) return PKV_ERR_SHAPE;
+  const bool copy = (src_dtype == cache_dtype) && (src_dtype == PKV_F32 || src_dtype == PKV_BF16);
+  const bool fp8 = cache_dtype == PKV_FP8_E4M3 && (src_dtype == PKV_BF16 || src_dtype == PKV_F32);
+  if (!copy && !fp8) return PKV_ERR_DTYPE;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_NULL;
+  if (fp8 && (!key_scale || !value_scale)) return PKV_ERR_NULL;
+  if (fp8) {
+    const size_t need = kv_write_fp8_workspace(num_blocks, num_kv_heads);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  }
+  if (num_tokens == 0) return PKV_OK;
+  WriteArgs a;
+  a.key = key; a.value = value; a.key_cache = key_cache; a.value_cache = value_cache;
+  a.key_scale = key_scale; a.value_scale = value_scale; a.slots = slot_mapping;
+  a.T = num_tokens; a.H_kv = num_kv_heads; a.D = head_size; a.bs = block_size;
+  a.num_blocks = num_blocks; a.src_dtype = src_dtype; a.cache_dtype = cache_dtype;
+  a.workspace = workspace; a.stream = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(copy ? launch_kv_write_copy(a) : launch_kv_write_fp8(a));
+}
+
+int32_t paged_attention_decode_partition_size(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_size,
+                                              int32_t block_size, int32_t max_context_len,
+                                              int32_t q_dtype, int32_t cache_dtype,
+                                              int32_t partition_size) {
+  if (check_decode_shape(num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                         max_context_len, q_dtype, cache_dtype) != PKV_OK)
+    return -1;
+  return resolve_partition(block_size, max_context_len, partition_size);
+}
+
+size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                             int32_t num_kv_heads, int32_t head_size,
+                                             int32_t block_size, int32_t max_context_len,
+                                             int32_t q_dtype, int32_t cache_dtype,
+                                             int32_t partition_size) {
+  const int P = paged_attention_decode_partition_size(num_seqs, num_heads, num_kv_heads,
+                                                      head_size, block_size, max_context_len,
+                                                      q_dtype, cache_dtype, partition_size);
+  if (P <= 0) return 0;
+  return decode_workspace(num_seqs, num_heads, head_size, max_context_len, P);
+}
+
+pkv_status_t paged_attention_decode_partitions(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const float* key_scale, const float* value_scale, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
+    float scale, int32_t q_dtype, int32_t cache_dtype, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  DecodeSetup s = setup_decode(out, query, key_cache, value_cache, key_scale, value_scale,
+                               block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                               head_size, block_size, max_blocks_per_seq, max_context_len, scale,
+                               q_dtype, cache_dtype, partition_size, workspace, workspace_bytes,
+                               stream, true);
+  if (s.status != PKV_OK) return s.status;
+  if (num_seqs == 0) return PKV_OK;
+  return hip_status(launch_decode_valu(s.a));
+}
+
+pkv_status_t paged_attention_decode_reduce(void* out, const int32_t* context_lens,
+                                           int32_t num_seqs, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_size,
+                                           int32_t block_size, int32_t max_context_len,
+                                           int32_t q_dtype, int32_t cache_dtype,
+                                           int32_t partition_size, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  DecodeSetup s = setup_decode(out, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               context_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                               block_size, 0, max_context_len, 1.0f, q_dtype, cache_dtype,
+                               partition_size, workspace, workspace_bytes, stream, false);
+  if (s.status != PKV_OK) return s.status;
+  if (num_seqs == 0 || s.a.NP <= 1) return PKV_OK;
+  return hip_status(launch_decode_reduce(s.a));
+}
+
+pkv_status_t paged_attention_decode(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const float* key_scale,
+                                    const float* value_scale, const int32_t* block_tables,
+                                    const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                    int32_t block_size, int32_t max_blocks_per_seq,
+                                    int32_t max_context_len, float scale, int32_t q_dtype,
+                                    int32_t cache_dtype, int32_t partition_size,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_status_t st = paged_attention_decode_partitions(
+      out, query, key_cache, value_cache, key_scale, value_scale, block_tables, context_lens,
+      num_seqs, num_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
+      max_context_len, scale, q_dtype, cache_dtype, partition_size, workspace, workspace_bytes,
+      stream);
+  if (st != PKV_OK) return st;
+  return paged_attention_decode_reduce(out, context_lens, num_seqs, num_heads, num_kv_heads,
+                                       head_size, block_size, max_context_len, q_dtype,
+                                       cache_dtype, partition_size, workspace, workspace_bytes,
+                                       stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+// Paged KV write: scatter new K/V rows into their slots (copy), or quantise
+// them to OCP E4M3FN with per-(block, KV head) scales.
+//
+// Block structure: dpshk.com PagedAttention article ("企业官网建设流程全解析"),
+// section 2.1 (fixed-size blocks of token rows); FP8 storage of blocks: same
+// article, section 3.2.  The slot mapping (slot = block * bs + offset) is the
+// write side of the block table (page "vLLM的诞生背景…", section
+// "PagedAttention的破局思路").
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+// One workgroup per token: both K and V rows of every KV head, 16 bytes per
+// lane.  Row bytes (D * elem) are 128..512, a multiple of 16.
+__global__ __launch_bounds__(256) void kv_write_copy_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value,
+    uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+    const int32_t* __restrict__ slots, int H_kv, int row_vec, int bs) {
+  const int t = blockIdx.x;
+  const int s = slots[t];
+  if (s < 0) return;
+  const int b = s / bs;
+  const int o = s - b * bs;
+  const int per_token = H_kv * row_vec;  // 16-byte vectors per token per K or V
+  for (int i = threadIdx.x; i < 2 * per_token; i += blockDim.x) {
+    const bool is_v = i >= per_token;
+    const int j = is_v ? i - per_token : i;
+    const int h = j / row_vec;
+    const int v = j - h * row_vec;
+    const size_t src = (size_t)t * per_token + j;
+    const size_t dst = (((size_t)b * H_kv + h) * bs + o) * row_vec + v;
+    if (is_v) value_cache[dst] = value[src];
+    else key_cache[dst] = key[src];
+  }
+}
+
+// ---------------------------------------------------------------- FP8 path
+// Workspace: fresh[num_blocks] (int32) then amax[num_blocks][H_kv][2]
+// (float bits; index 0 = K, 1 = V).  Three launches:
+//   1. clear the entries of every block this call touches;
+//   2. mark blocks whose offset 0 is written ("fresh") and take amax per
+//      (block, KV head, K|V) with atomicMax on the float bits (non-negative
+//      floats order like their unsigned bit patterns);
+//   3. pick the scale (fresh: from amax; else the stored one) and encode.
+
+__global__ __launch_bounds__(64) void fp8_clear_kernel(
+    const int32_t* __restrict__ slots, int T, int bs, int H_kv,
+    int32_t* __restrict__ fresh, uint32_t* __restrict__ amax) {
+  const int t = blockIdx.x;
+  if (t >= T) return;
+  const int s = slots[t];
+  if (s < 0) return;
+  const int b = s / bs;
+  for (int i = threadIdx.x; i < 2 * H_kv; i += blockDim.x) amax[(size_t)b * 2 * H_kv + i] = 0u;
+  if (threadIdx.x == 0) fresh[b] = 0;
+}
+
+template <typename ST, int D>
+__device__ __forceinline__ float src_elem(const ST* p, int i) {
+  if constexpr (sizeof(ST) == 4) return p[i];
+  else return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+// One wave per (token, KV head); lanes stride over D for K and V.
+template <typename ST, int D>
+__global__ __launch_bounds__(256) void fp8_amax_kernel(
+    const ST* __restrict__ key, const ST* __restrict__ value,
+    const int32_t* __restrict__ slots, int T, int bs, int H_kv,
+    int32_t* __restrict__ fresh, uint32_t* __restrict__ amax) {
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (wave >= T * H_kv) return;
+  const int t = wave / H_kv;
+  const int h = wave - t * H_kv;
+  const int s = slots[t];
+  if (s < 0) return;
+  const int b = s / bs;
+  const int o = s - b * bs;
+  const ST* kp = key + ((size_t)t * H_kv + h) * D;
+  const ST* vp = value + ((size_t)t * H_kv + h) * D;
+  float mk = 0.f, mv = 0.f;
+#pragma unroll
+  for (int d = lane; d < D; d += 64) {
+    mk = fmaxf(mk, fabsf(src_elem<ST, D>(kp, d)));
+    mv = fmaxf(mv, fabsf(src_elem<ST, D>(vp, d)));
+  }
+  // NaN must win the maximum, as it does in an ordinary max over the values.
+  const float nk = (mk != mk) ? 1.f : 0.f, nv = (mv != mv) ? 1.f : 0.f;
+  mk = wave_max(mk);
+  mv = wave_max(mv);
+  const float any_nk = wave_max(nk), any_nv = wave_max(nv);
+  if (lane == 0) {
+    uint32_t bk = any_nk > 0.f ? 0x7fc00000u : __float_as_uint(mk);
+    uint32_t bv = any_nv > 0.f ? 0x7fc00000u : __float_as_uint(mv);
+    atomicMax(&amax[((size_t)b * H_kv + h) * 2 + 0], bk);
+    atomicMax(&amax[((size_t)b * H_kv + h) * 2 + 1], bv);
+    if (o == 0 && h == 0) fresh[b] = 1;
+  }
+}
+
+__device__ __forceinline__ float fp8_scale_from_amax(uint32_t bits) {
+  const float s = __uint_as_float(bits) / 448.0f;
+  const float flt_min = 1.17549435e-38f;
+  return (s < flt_min) ? flt_min : s;  // NaN stays NaN
+}
+
+// One wave per (token, KV head): encode D elements of K and of V.
+template <typename ST, int D>
+__global__ __launch_bounds__(256) void fp8_quant_kernel(
+    const ST* __restrict__ key, const ST* __restrict__ value,
+    uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
+    float* __restrict__ key_scale, float* __restrict__ value_scale,
+    const int32_t* __restrict__ slots, int T, int bs, int H_kv,
+    const int32_t* __restrict__ fresh, const uint32_t* __restrict__ amax) {
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (wave >= T * H_kv) return;
+  const int t = wave / H_kv;
+  const int h = wave - t * H_kv;
+  const int s = slots[t];
+  if (s < 0) return;
+  const int b = s / bs;
+  const int o = s - b * bs;
+  const size_t sidx = (size_t)b * H_kv + h;
+  float sk, sv;
+  if (fresh[b]) {
+    sk = fp8_scale_from_amax(amax[sidx * 2 + 0]);
+    sv = fp8_scale_from_amax(amax[sidx * 2 + 1]);
+    if (lane == 0) {  // every token of the block stores the same value
+      key_scale[sidx] = sk;
+      value_scale[sidx] = sv;
+    }
+  } else {
+    sk = key_scale[sidx];
+    sv = value_scale[sidx];
+  }
+  const ST* kp = key + ((size_t)t * H_kv + h) * D;
+  const ST* vp = value + ((size_t)t * H_kv + h) * D;
+  uint8_t* kd = key_cache + (sidx * bs + o) * D;
+  uint8_t* vd = value_cache + (sidx * bs + o) * D;
+  // Correctly rounded float32 quotient: the double quotient rounded once more
+  // to float equals the float quotient (53 >= 2*24 + 2).
+  const double dk = (double)sk, dv = (double)sv;
+#pragma unroll
+  for (int d = lane; d < D; d += 64) {
+    kd[d] = (uint8_t)f32_to_e4m3((float)((double)src_elem<ST, D>(kp, d) / dk));
+    vd[d] = (uint8_t)f32_to_e4m3((float)((double)src_elem<ST, D>(vp, d) / dv));
+  }
+}
+
+template <typename ST, int D>
+hipError_t fp8_launch(const WriteArgs& a) {
+  int32_t* fresh = reinterpret_cast<int32_t*>(a.workspace);
+  uint32_t* amax = reinterpret_cast<uint32_t*>(fresh + ((a.num_blocks + 63) / 64) * 64);
+  const ST* key = reinterpret_cast<const ST*>(a.key);
+  const ST* value = reinterpret_cast<const ST*>(a.value);
+  hipLaunchKernelGGL(fp8_clear_kernel, dim3(a.T), dim3(64), 0, a.stream, a.slots, a.T, a.bs,
+                     a.H_kv, fresh, amax);
+  const int waves = a.T * a.H_kv;
+  const int blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((fp8_amax_kernel<ST, D>), dim3(blocks), dim3(256), 0, a.stream, key, value,
+                     a.slots, a.T, a.bs, a.H_kv, fresh, amax);
+  hipLaunchKernelGGL((fp8_quant_kernel<ST, D>), dim3(blocks), dim3(256), 0, a.stream, key, value,
+                     reinterpret_cast<uint8_t*>(a.key_cache),
+                     reinterpret_cast<uint8_t*>(a.value_cache), a.key_scale, a.value_scale,
+                     a.slots, a.T, a.bs, a.H_kv, fresh, amax);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t kv_write_fp8_workspace(int num_blocks, int H_kv) {
+  const size_t fresh = ((size_t)(num_blocks + 63) / 64) * 64 * sizeof(int32_t);
+  return fresh + (size_t)num_blocks * H_kv * 2 * sizeof(uint32_t);
+}
+
+hipError_t launch_kv_write_copy(const WriteArgs& a) {
+  const int elem = a.cache_dtype == PKV_F32 ? 4 : 2;
+  const int row_vec = a.D * elem / 16;
+  hipLaunchKernelGGL(kv_write_copy_kernel, dim3(a.T), dim3(256), 0, a.stream,
+                     reinterpret_cast<const uint4*>(a.key), reinterpret_cast<const uint4*>(a.value),
+                     reinterpret_cast<uint4*>(a.key_cache), reinterpret_cast<uint4*>(a.value_cache),
+                     a.slots, a.H_kv, row_vec, a.bs);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write_fp8(const WriteArgs& a) {
+  if (a.src_dtype == PKV_BF16) {
+    return a.D == 64 ? fp8_launch<uint16_t, 64>(a) : fp8_launch<uint16_t, 128>(a);
+  }
+  return a.D == 64 ? fp8_launch<float, 64>(a) : fp8_launch<float, 128>(a);
+}
+
+}  // namespace pkv

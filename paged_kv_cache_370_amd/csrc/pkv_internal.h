@@ -1,0 +1,55 @@
+// Host-side declarations shared by the translation units of libpagedkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+struct WriteArgs {
+  const void* key;
+  const void* value;
+  void* key_cache;
+  void* value_cache;
+  float* key_scale;
+  float* value_scale;
+  const int32_t* slots;
+  int T, H_kv, D, bs, num_blocks;
+  int src_dtype, cache_dtype;
+  void* workspace;
+  hipStream_t stream;
+};
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* key_cache;
+  const void* value_cache;
+  const float* key_scale;
+  const float* value_scale;
+  const int32_t* tables;
+  const int32_t* lens;
+  int S, H, H_kv, D, bs, max_blocks, max_ctx;
+  float scale;
+  int q_dtype, cache_dtype;
+  int P;   // partition size in tokens (multiple of bs)
+  int NP;  // partitions per sequence the grid covers: ceil(max_ctx / P)
+  float* ws_m;    // [S][H][NP]  running max (base-2 units) per partition
+  float* ws_l;    // [S][H][NP]  running sum per partition
+  float* ws_acc;  // [S][H][NP][D]  unnormalised output per partition
+  hipStream_t stream;
+};
+
+hipError_t launch_kv_write_copy(const WriteArgs& a);
+hipError_t launch_kv_write_fp8(const WriteArgs& a);
+size_t kv_write_fp8_workspace(int num_blocks, int H_kv);
+
+hipError_t launch_decode_valu(const DecodeArgs& a);
+bool decode_mfma_supported(const DecodeArgs& a);
+hipError_t launch_decode_mfma(const DecodeArgs& a);
+hipError_t launch_decode_reduce(const DecodeArgs& a);
+
+}  // namespace pkv

@@ -1,0 +1,121 @@
+"""The C ABI on the host (no GPU needed): every function include/pagedkv.h
+declares is exported, status codes, workspace and partition queries, and the
+argument checks that return before anything is enqueued."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_370_amd as pkv
+from paged_kv_cache_370_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    keywords = {"if", "sizeof", "defined"}
+    return sorted({n for n in names if n not in keywords})
+
+
+def test_header_functions_are_exported():
+    lib = pkv.load()
+    declared = _declared()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared:
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings_and_version():
+    assert pkv.status_string(0) == "ok"
+    for s in range(1, 6):
+        assert pkv.status_string(s) != "ok"
+    assert pkv.status_string(99) == "unknown status"
+    assert pkv.load().pkv_version() >= 100
+
+
+def test_partition_and_workspace_queries():
+    # context fits one partition: no workspace
+    assert pkv.decode_partition_size(4, 8, 8, 128, 16, 300, 1, 1, 0) == 304
+    assert pkv.decode_workspace_size(4, 8, 8, 128, 16, 300, 1, 1, 0) == 0
+    # long contexts: 512-token partitions, partials for m, l and acc
+    assert pkv.decode_partition_size(8, 64, 8, 128, 8, 32768, 1, 1, 512) == 512
+    rows = 8 * 64 * 64
+    expect = 2 * ((rows * 4 + 255) // 256 * 256) + (rows * 128 * 4 + 255) // 256 * 256
+    assert pkv.decode_workspace_size(8, 64, 8, 128, 8, 32768, 1, 1, 512) == expect
+    # partition not a multiple of the block size, bad head size, bad dtype pair
+    assert pkv.decode_partition_size(8, 64, 8, 128, 16, 32768, 1, 1, 40) < 0
+    assert pkv.decode_partition_size(8, 64, 8, 96, 16, 32768, 1, 1, 0) < 0
+    assert pkv.decode_partition_size(8, 64, 8, 128, 16, 100, 0, 1, 0) < 0
+    assert pkv.write_workspace_size(10, 8, 100, 1) == 0
+    assert pkv.write_workspace_size(10, 8, 100, 2) >= 100 * (1 + 16) * 4
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: each call fails its checks first
+
+
+def _decode(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None, tables=FAKE, lens=FAKE, S=2,
+             H=8, H_kv=2, D=128, bs=16, max_blocks=8, max_ctx=100, scale=0.1, qd=1, cd=1, ps=0,
+             ws=None, wsb=0)
+    a.update(kw)
+    return pkv.load().paged_attention_decode(
+        a["out"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["tables"], a["lens"], a["S"],
+        a["H"], a["H_kv"], a["D"], a["bs"], a["max_blocks"], a["max_ctx"], a["scale"], a["qd"],
+        a["cd"], a["ps"], a["ws"], a["wsb"], None)
+
+
+def test_decode_argument_checks():
+    assert _decode(out=None) == 1
+    assert _decode(q=None) == 1
+    assert _decode(cd=2) == 1                         # FP8 without scales
+    assert _decode(D=96) == 2
+    assert _decode(bs=4) == 2
+    assert _decode(H=7) == 2
+    assert _decode(max_ctx=1000) == 2                 # exceeds max_blocks * bs
+    assert _decode(ps=24) == 2
+    assert _decode(qd=0, cd=1) == 3
+    assert _decode(qd=0, cd=2) == 3
+    assert _decode(max_ctx=128, max_blocks=8, ps=16) == 4   # needs workspace
+    assert _decode(max_ctx=128, ps=16, ws=FAKE, wsb=10) == 4
+
+
+def _write(**kw):
+    a = dict(k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None, slots=FAKE, T=4, H_kv=2, D=128,
+             bs=16, nb=10, sd=1, cd=1, ws=None, wsb=0)
+    a.update(kw)
+    return pkv.load().paged_kv_cache_write(
+        a["k"], a["v"], a["kc"], a["vc"], a["ks"], a["vs"], a["slots"], a["T"], a["H_kv"],
+        a["D"], a["bs"], a["nb"], a["sd"], a["cd"], a["ws"], a["wsb"], None)
+
+
+def test_write_argument_checks():
+    assert _write(k=None) == 1
+    assert _write(slots=None) == 1
+    assert _write(D=80) == 2
+    assert _write(nb=0) == 2
+    assert _write(sd=0, cd=1) == 3
+    assert _write(sd=2, cd=2) == 3
+    assert _write(sd=1, cd=2) == 1                    # FP8 without scales
+    assert _write(sd=1, cd=2, ks=FAKE, vs=FAKE) == 4  # FP8 without workspace
+    assert _write(T=0) == 0                           # nothing to do
+
+
+def test_product_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "paged_kv_cache_370_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith(".py"):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", src, re.M), f
+                assert "workloads" not in src, f

@@ -131,6 +131,7 @@ def build_workload(name, S, H, H_kv, D, block_size, q_dtype, cache_dtype, lens,
     used = pb + int(private.sum())
     if num_blocks is None:
         num_blocks = int(np.ceil(used * (1.0 + free_frac))) if free_frac else used
+        num_blocks = max(num_blocks, 1)
     assert num_blocks >= used
     mb = int(max_blocks or max(1, int(nb.max()) if S else 1))
 
@@ -157,11 +158,13 @@ def build_workload(name, S, H, H_kv, D, block_size, q_dtype, cache_dtype, lens,
             kc[free_ids] = poison
             vc[free_ids] = poison
         for i in range(S):
+            if lens[i] == 0:
+                continue
             last = tables[i, nb[i] - 1]
             start = int(lens[i] - 1 - (nb[i] - 1) * bs)   # row of position n-1
             kc[last, :, start:, :] = poison
             vc[last, :, start:, :] = poison
-        positions = [np.array([n - 1]) for n in lens]
+        positions = [np.arange(n - 1, n) if n > 0 else np.zeros(0, np.int64) for n in lens]
         writes = [_step_write(rng_val, tables, positions, H_kv, D, bs, src_dtype)]
     else:
         kc = np.full(pool_shape, _poison(cache_dtype), dtype=_np_dtype(cache_dtype))
@@ -169,7 +172,8 @@ def build_workload(name, S, H, H_kv, D, block_size, q_dtype, cache_dtype, lens,
         if fill == "write-all":
             groups = [[np.arange(n) for n in lens]]
         else:
-            groups = [[np.arange(n - 1) for n in lens], [np.array([n - 1]) for n in lens]]
+            groups = [[np.arange(max(n - 1, 0)) for n in lens],
+                      [np.arange(n - 1, n) if n > 0 else np.zeros(0, np.int64) for n in lens]]
         writes = []
         for g_idx, positions in enumerate(groups):
             if pb and g_idx == 0:
