@@ -1,0 +1,295 @@
+"""Benchmark one decode step (paged KV write of the step's tokens + paged
+attention decode) on one MI355X and print ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7b-decode-bf16]
+
+A step is the whole hot path over one batch: paged_kv_cache_write of each
+sequence's newest token, the decode partition kernel and the split reduce.
+Inputs are seeded synthetic tensors already resident in HBM.  `value` is the
+algorithmic KV bytes the decode reads per step divided by the step time
+(GB/s); `roofline` is the partition kernel's algorithmic bytes over its own
+event-timed duration against the 8 TB/s HBM peak; `cpu_baseline` times the
+CPU oracle (float64 numpy, one BLAS thread) on a bounded sample of the same
+workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-decode attention: KV bytes read GB/s (% of HBM peak); seq-heads/s"
+HBM_PEAK_GBS = 8000.0
+WORKLOADS = {"tiny-fp32": 1, "7b-decode-bf16": 2, "32k-gqa-bf16": 3,
+             "shared-prefix-bf16": 4, "fp8-kv": 5}
+DEFAULT_WORKLOAD = "7b-decode-bf16"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
+KERNEL_SOURCES = ("decode_valu.hip", "decode_mfma.hip", "pkv_device.h")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="tokens per partition; -1 = the workload's own, 0 = library choice")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget for the oracle sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB (5 times), to scale "
+                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes")
+    return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes_each_way": n * 4, "launches": 5}), flush=True)
+
+
+def kv_bytes(w):
+    """Algorithmic bytes a decode reads: every distinct (physical block, KV
+    head) tile once, valid token rows only, K and V, plus FP8 scales."""
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
+    rows = {}
+    for i in range(w.S):
+        n = int(w.context_lens[i])
+        nb = -(-n // w.block_size)
+        for j in range(nb):
+            b = int(w.block_tables[i, j])
+            rows[b] = max(rows.get(b, 0), min(w.block_size, n - j * w.block_size))
+    tokens = sum(rows.values())
+    total = tokens * w.H_kv * w.D * elem * 2
+    if w.cache_dtype == "fp8":
+        total += len(rows) * w.H_kv * 4 * 2
+    return total, len(rows)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        p = os.path.join(ROOT, "paged_kv_cache_370_amd", "csrc", name)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per partition-kernel launch from the committed rocprofv3 PMC
+    summary, if it was taken on the current kernel sources; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    src = kernel_source_hash()
+    for line in open(COUNTERS_FILE):
+        parts = line.split()
+        if len(parts) >= 4 and parts[0] == "traffic" and parts[1] == workload and parts[2] == src:
+            return float(parts[3])
+    return None
+
+
+def cpu_baseline(w, budget_s):
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    kc, vc, ks, vs = w.key_cache, w.value_cache, w.key_scale, w.value_scale
+    t_total = 0.0
+    done_bytes = 0
+    done = 0
+    order = list(range(w.S))
+    with threadpool_limits(limits=1):
+        for i in order:
+            n = int(w.context_lens[i])
+            nb = -(-n // w.block_size)
+            sub_tab = w.block_tables[i:i + 1]
+            t0 = time.perf_counter()
+            oracle.paged_attention_decode(w.q[i:i + 1], kc, vc, sub_tab, w.context_lens[i:i + 1],
+                                          w.scale, w.block_size, ks, vs)
+            t_total += time.perf_counter() - t0
+            elem = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
+            done_bytes += n * w.H_kv * w.D * elem * 2
+            done += 1
+            if t_total >= budget_s:
+                break
+    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 numpy oracle decode of the first {done} of {w.S} sequences "
+                      f"({done * w.H} seq-heads, {done_bytes / 1e6:.1f} MB of KV) in "
+                      f"{t_total:.1f} s on one host thread",
+            "seq_heads_per_s": done * w.H / t_total}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
+
+    import torch
+    import paged_kv_cache_370_amd as pkv
+    import workloads
+
+    pkv.load()
+    cfg = WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    w = workloads.make_config(cfg)
+    gen_s = time.perf_counter() - t0
+    total_bytes, nblocks = kv_bytes(w)
+    ps = w.partition_size if args.partition_size < 0 else args.partition_size
+
+    dev = torch.device("cuda:0")
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q = t(w.q)
+    kc, vc = t(w.key_cache), t(w.value_cache)
+    ks = t(w.key_scale) if w.key_scale is not None else None
+    vs = t(w.value_scale) if w.value_scale is not None else None
+    tables, lens = t(w.block_tables), t(w.context_lens)
+    writes = [(t(k), t(v), t(s)) for k, v, s in w.writes]
+    out = torch.empty_like(q)
+    qc, cc = pkv.dtype_code(q), pkv.dtype_code(kc)
+    P = pkv.decode_partition_size(w.S, w.H, w.H_kv, w.D, w.block_size, w.max_context_len, qc, cc, ps)
+    ws_bytes = pkv.decode_workspace_size(w.S, w.H, w.H_kv, w.D, w.block_size, w.max_context_len,
+                                         qc, cc, ps)
+    dws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    wws_bytes = pkv.write_workspace_size(max(len(x[2]) for x in writes), w.H_kv, w.num_blocks, cc)
+    wws = torch.empty(max(wws_bytes, 1), dtype=torch.uint8, device=dev) if wws_bytes else None
+
+    # Setup writes (FP8: the bulk write of positions 0..n-2) are not part of a step.
+    setup = writes[:-1]
+    step_write = writes[-1]
+    setup_ms = None
+    if setup:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k, v, s in setup:
+            pkv.paged_kv_cache_write(k, v, kc, vc, s, ks, vs, workspace=wws)
+        e1.record()
+        torch.cuda.synchronize()
+        setup_ms = e0.elapsed_time(e1)
+
+    def step(ev=None):
+        k, v, s = step_write
+        if ev: ev[0].record()
+        pkv.paged_kv_cache_write(k, v, kc, vc, s, ks, vs, workspace=wws)
+        if ev: ev[1].record()
+        pkv.paged_attention_decode_partitions(out, q, kc, vc, tables, lens, w.max_context_len,
+                                              w.scale, ks, vs, partition_size=ps, workspace=dws)
+        if ev: ev[2].record()
+        pkv.paged_attention_decode_reduce(out, lens, w.H_kv, w.block_size, w.max_context_len, cc,
+                                          partition_size=ps, workspace=dws)
+        if ev: ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    write_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    part_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    red_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    value = total_bytes / (ms_step * 1e-3) / 1e9
+    achieved = total_bytes / (part_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(args.workload)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8e4m3-kv/bf16-q"}[w.cache_dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "seqs": w.S, "q_heads": w.H, "kv_heads": w.H_kv,
+            "head_size": w.D, "block_size": w.block_size, "max_context": w.max_context_len,
+            "mean_context": round(float(np.mean(w.context_lens)), 1),
+            "partition_size": P, "kv_bytes_per_step": total_bytes, "kv_blocks_read": nblocks,
+            "step": "paged_kv_cache_write + decode partitions + reduce",
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seq_heads_per_s": round(w.S * w.H / (ms_step * 1e-3), 1),
+        "kernel_ms": {"write": round(write_ms, 5), "decode_partitions": round(part_ms, 5),
+                      "decode_reduce": round(red_ms, 5)},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode partition kernel",
+            "kernel_sources": kernel_source_hash(),
+        },
+        "input_generation_s": round(gen_s, 2),
+    }
+    if setup_ms is not None:
+        setup_bytes = sum(x[0].numel() * x[0].element_size() * 2 for x in setup)
+        result["setup_write"] = {"ms": round(setup_ms, 3),
+                                 "source_bytes": setup_bytes,
+                                 "GB_per_s_source_read": round(setup_bytes / setup_ms / 1e6, 1)}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_for(w, writes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_for(w, writes, budget):
+    """The oracle first performs the workload's writes itself (untimed), so it
+    decodes the same cache state the GPU step decodes."""
+    import oracle
+    kc, vc, ks, vs = w.key_cache, w.value_cache, w.key_scale, w.value_scale
+    for k, v, s in w.writes:
+        if w.cache_dtype == "fp8":
+            kc, vc, ks, vs = oracle.paged_kv_cache_write(k, v, kc, vc, s, w.block_size, ks, vs)
+        else:
+            kc, vc = oracle.paged_kv_cache_write(k, v, kc, vc, s, w.block_size)
+    w = workloads_replace(w, key_cache=kc, value_cache=vc, key_scale=ks, value_scale=vs)
+    return cpu_baseline(w, budget)
+
+
+def workloads_replace(w, **kw):
+    import workloads
+    return workloads.Workload(**{**w.__dict__, **kw})
+
+
+if __name__ == "__main__":
+    main()
