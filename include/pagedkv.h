@@ -96,6 +96,8 @@ typedef enum {
  *     paged_kv_cache_write_workspace_size(...) bytes (any contents).
  *
  * Slots within one call must be distinct; duplicate slots race.
+ * num_tokens == 0 returns PKV_OK after the size and dtype checks without
+ * inspecting any pointer.
  */
 pkv_status_t paged_kv_cache_write(
     const void* key, const void* value,
@@ -135,6 +137,8 @@ size_t paged_kv_cache_write_workspace_size(
  *   own, and a second kernel merges the partial results.
  *   workspace: at least paged_attention_decode_workspace_size(...) bytes
  *   (any contents; may be NULL when that size is 0).
+ *   num_seqs == 0 returns PKV_OK after the size and dtype checks without
+ *   inspecting any pointer.
  */
 pkv_status_t paged_attention_decode(
     void* out, const void* query,

@@ -58,6 +58,7 @@ size_t decode_workspace(int S, int H, int D, int max_ctx, int P) {
 
 struct DecodeSetup {
   pkv_status_t status;
+  bool empty;  // no sequences: nothing to launch, pointers not inspected
   DecodeArgs a;
 };
 
@@ -78,6 +79,10 @@ DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
   const int P = resolve_partition(bs, max_ctx, partition);
   if (P <= 0) {
     r.status = PKV_ERR_SHAPE;
+    return r;
+  }
+  if (S == 0) {
+    r.empty = true;
     return r;
   }
   if (!out || !context_lens) {
@@ -155,13 +160,15 @@ pkv_status_t paged_kv_cache_write(const void* key, const void* value, void* key_
   const bool copy = (src_dtype == cache_dtype) && (src_dtype == PKV_F32 || src_dtype == PKV_BF16);
   const bool fp8 = cache_dtype == PKV_FP8_E4M3 && (src_dtype == PKV_BF16 || src_dtype == PKV_F32);
   if (!copy && !fp8) return PKV_ERR_DTYPE;
+  // Nothing is read or written for an empty batch, so its (possibly NULL)
+  // pointers are not inspected.
+  if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_NULL;
   if (fp8 && (!key_scale || !value_scale)) return PKV_ERR_NULL;
   if (fp8) {
     const size_t need = kv_write_fp8_workspace(num_blocks, num_kv_heads);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
   }
-  if (num_tokens == 0) return PKV_OK;
   WriteArgs a;
   a.key = key; a.value = value; a.key_cache = key_cache; a.value_cache = value_cache;
   a.key_scale = key_scale; a.value_scale = value_scale; a.slots = slot_mapping;
@@ -206,8 +213,7 @@ pkv_status_t paged_attention_decode_partitions(
                                head_size, block_size, max_blocks_per_seq, max_context_len, scale,
                                q_dtype, cache_dtype, partition_size, workspace, workspace_bytes,
                                stream, true);
-  if (s.status != PKV_OK) return s.status;
-  if (num_seqs == 0) return PKV_OK;
+  if (s.status != PKV_OK || s.empty) return s.status;
   return hip_status(launch_decode_valu(s.a));
 }
 
@@ -222,8 +228,7 @@ pkv_status_t paged_attention_decode_reduce(void* out, const int32_t* context_len
                                context_lens, num_seqs, num_heads, num_kv_heads, head_size,
                                block_size, 0, max_context_len, 1.0f, q_dtype, cache_dtype,
                                partition_size, workspace, workspace_bytes, stream, false);
-  if (s.status != PKV_OK) return s.status;
-  if (num_seqs == 0 || s.a.NP <= 1) return PKV_OK;
+  if (s.status != PKV_OK || s.empty || s.a.NP <= 1) return s.status;
   return hip_status(launch_decode_reduce(s.a));
 }
 

@@ -109,6 +109,14 @@ def test_write_argument_checks():
     assert _write(sd=1, cd=2) == 1                    # FP8 without scales
     assert _write(sd=1, cd=2, ks=FAKE, vs=FAKE) == 4  # FP8 without workspace
     assert _write(T=0) == 0                           # nothing to do
+    # an empty batch may come with NULL pointers (empty tensors)
+    assert _write(T=0, k=None, v=None, slots=None, kc=None, vc=None) == 0
+    assert _write(T=0, D=80) == 2                     # sizes are still checked
+
+
+def test_empty_decode_batch_needs_no_pointers():
+    assert _decode(S=0, out=None, q=None, kc=None, vc=None, tables=None, lens=None) == 0
+    assert _decode(S=0, D=96) == 2
 
 
 def test_product_never_imports_the_oracle():
