@@ -214,7 +214,8 @@ pkv_status_t paged_attention_decode_partitions(
                                q_dtype, cache_dtype, partition_size, workspace, workspace_bytes,
                                stream, true);
   if (s.status != PKV_OK || s.empty) return s.status;
-  return hip_status(launch_decode_valu(s.a));
+  return hip_status(decode_mfma_supported(s.a) ? launch_decode_mfma(s.a)
+                                               : launch_decode_valu(s.a));
 }
 
 pkv_status_t paged_attention_decode_reduce(void* out, const int32_t* context_lens,
