@@ -30,6 +30,9 @@ FLAGS = [
     "-Wno-unused-function",
     # keep hipcc from forming packed fp32 arithmetic on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the online softmax rescales them with
+    # vector ALU ops every chunk, and AGPRs would need copies both ways
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

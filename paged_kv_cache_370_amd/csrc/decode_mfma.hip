@@ -101,28 +101,54 @@ struct Geometry {
   static constexpr int VS = D + 16;             // LDS V row stride (bf16), padded
 };
 
+// Registers that carry one chunk from HBM to the products.  K and V have one
+// buffer each: within an iteration the V tile of chunk i goes to LDS before
+// the V loads of chunk i+NW are issued into the same registers, and the K
+// rows of chunk i feed the score products before the K loads of chunk i+NW
+// are issued, so both loads are in flight while chunk i finishes.
 template <typename CT, int D>
-struct Stage {
+struct KStage {
   using Gm = Geometry<CT, D>;
   uint4 k[2][Gm::KV4];
-  uint4 v[Gm::VI];
-  float ksc[2], vsc[2];
+  float ksc[2], vsc[2];  // FP8 scales of the lane's two 4-token groups
 };
 
+template <typename CT, int D>
+struct VStage {
+  uint4 v[Geometry<CT, D>::VI];
+};
+
+template <typename CT, int D>
+__device__ __forceinline__ void keep_live(const VStage<CT, D>& vs, const KStage<CT, D>& ks) {
+#pragma unroll
+  for (int j = 0; j < Geometry<CT, D>::VI; ++j)
+    asm volatile("" ::"v"(vs.v[j].x), "v"(vs.v[j].y), "v"(vs.v[j].z), "v"(vs.v[j].w));
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int i = 0; i < Geometry<CT, D>::KV4; ++i)
+      asm volatile("" ::"v"(ks.k[T][i].x), "v"(ks.k[T][i].y), "v"(ks.k[T][i].z),
+                   "v"(ks.k[T][i].w));
+}
+
+template <int BS>
+__device__ __forceinline__ size_t row_index(const int* s_tab, int t, int first_blk, int H_kv,
+                                            int kvh) {
+  const int phys = s_tab[t / BS - first_blk];
+  return ((size_t)phys * H_kv + kvh) * BS + (t % BS);
+}
+
 template <typename CT, int D, int BS>
-__device__ __forceinline__ void load_chunk(Stage<CT, D>& st, const MfmaParams& p, int c0,
-                                           int end, int first_blk, const int* s_tab, int kvh,
-                                           int lane) {
+__device__ __forceinline__ void load_k(KStage<CT, D>& st, const MfmaParams& p, int c0, int end,
+                                       int first_blk, const int* s_tab, int kvh, int lane) {
   using Gm = Geometry<CT, D>;
   using CS = typename CT::storage;
   const int q = lane >> 4, r = lane & 15;
   const CS* kc = reinterpret_cast<const CS*>(p.kc);
-  const CS* vc = reinterpret_cast<const CS*>(p.vc);
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
     const int t = min(c0 + 16 * T + r, end - 1);  // clamped: masked later
-    const int phys = s_tab[t / BS - first_blk];
-    const size_t row = ((size_t)phys * p.H_kv + kvh) * BS + (t % BS);
+    const size_t row = row_index<BS>(s_tab, t, first_blk, p.H_kv, kvh);
     const uint4* src = reinterpret_cast<const uint4*>(kc + row * D + Gm::DQ * q);
 #pragma unroll
     for (int i = 0; i < Gm::KV4; ++i) st.k[T][i] = src[i];
@@ -133,32 +159,42 @@ __device__ __forceinline__ void load_chunk(Stage<CT, D>& st, const MfmaParams& p
       st.vsc[T] = p.vs[si];
     }
   }
+}
+
+template <typename CT, int D, int BS>
+__device__ __forceinline__ void load_v(VStage<CT, D>& st, const MfmaParams& p, int c0, int end,
+                                       int first_blk, const int* s_tab, int kvh, int lane) {
+  using Gm = Geometry<CT, D>;
+  using CS = typename CT::storage;
+  const CS* vc = reinterpret_cast<const CS*>(p.vc);
 #pragma unroll
   for (int j = 0; j < Gm::VI; ++j) {
     const int t = min(c0 + j * Gm::RPI + lane / Gm::PR, end - 1);
-    const int phys = s_tab[t / BS - first_blk];
-    const size_t row = ((size_t)phys * p.H_kv + kvh) * BS + (t % BS);
+    const size_t row = row_index<BS>(s_tab, t, first_blk, p.H_kv, kvh);
     st.v[j] = reinterpret_cast<const uint4*>(vc + row * D)[lane % Gm::PR];
   }
 }
 
+// V rows of one chunk -> this wave's LDS tile as bf16 (rows past the end as
+// zeros).
 template <typename CT, int D>
-__device__ __forceinline__ void compute_chunk(const Stage<CT, D>& st, int c0, int end,
-                                              const bf16x8_t (&qf)[Geometry<CT, D>::NKC],
-                                              float scale_log2, uint16_t* s_v, f32x4_t (&acc)[Geometry<CT, D>::NMD],
-                                              float& m, float& lsum, int lane) {
+__device__ __forceinline__ void store_v(const VStage<CT, D>& st, int c0, int end, uint16_t* s_v,
+                                        int lane) {
   using Gm = Geometry<CT, D>;
-  const int q = lane >> 4, r = lane & 15;
   const bool full = c0 + kChunk <= end;
-
-  // 1. V rows -> LDS as bf16 (rows past the end as zeros).
   wave_lds_sync();  // the previous chunk's transpose reads are done
 #pragma unroll
   for (int j = 0; j < Gm::VI; ++j) {
     const int row = j * Gm::RPI + lane / Gm::PR;
     const int piece = lane % Gm::PR;
     uint4 v = st.v[j];
-    if (!full && c0 + row >= end) v = make_uint4(0u, 0u, 0u, 0u);
+    if (!full) {  // uniform: only the last chunk of a partition is ragged
+      const bool ok = c0 + row < end;
+      v.x = ok ? v.x : 0u;
+      v.y = ok ? v.y : 0u;
+      v.z = ok ? v.z : 0u;
+      v.w = ok ? v.w : 0u;
+    }
     if constexpr (Gm::ELEM == 2) {
       *reinterpret_cast<uint4*>(s_v + row * Gm::VS + piece * 8) = v;
     } else {
@@ -169,11 +205,16 @@ __device__ __forceinline__ void compute_chunk(const Stage<CT, D>& st, int c0, in
       dst[1] = make_uint4(c.x, c.y, d.x, d.y);
     }
   }
-
   wave_lds_sync();  // the tile is visible to every lane of the wave
+}
 
-  // 2. Scores S^T = K . Q^T for both 16-token tiles.
-  f32x4_t s[2];
+// Scores S^T = K . Q^T of both 16-token tiles: lane (q, r) gets head r,
+// tokens 16 T + 4 q + i.
+template <typename CT, int D>
+__device__ __forceinline__ void scores(const KStage<CT, D>& st,
+                                       const bf16x8_t (&qf)[Geometry<CT, D>::NKC],
+                                       f32x4_t (&s)[2]) {
+  using Gm = Geometry<CT, D>;
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
     s[T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -181,11 +222,9 @@ __device__ __forceinline__ void compute_chunk(const Stage<CT, D>& st, int c0, in
     for (int c = 0; c < Gm::NKC; ++c) {
       bf16x8_t a;
       if constexpr (Gm::ELEM == 2) {
-        // bytes 16c..16c+15 of the lane's row slice
-        a = as_bf16x8(st.k[T][c]);
+        a = as_bf16x8(st.k[T][c]);  // bytes 16c..16c+15 of the lane's row slice
       } else {
-        // bytes 8c..8c+7 of the lane's 32-byte slice
-        const uint4 w = st.k[T][c / 2];
+        const uint4 w = st.k[T][c / 2];  // bytes 8c..8c+7 of the lane's 32-byte slice
         const uint32_t w0 = (c & 1) ? w.z : w.x;
         const uint32_t w1 = (c & 1) ? w.w : w.y;
         const uint2 lo = fp8x4_to_bf16x4(w0), hi = fp8x4_to_bf16x4(w1);
@@ -194,18 +233,25 @@ __device__ __forceinline__ void compute_chunk(const Stage<CT, D>& st, int c0, in
       s[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], s[T], 0, 0, 0);
     }
   }
+}
 
-  // 3. Scale to base-2 units, mask, running max over this chunk.
+// Online softmax update with this chunk's scores, then O^T += V^T . P^T.
+template <int D>
+__device__ __forceinline__ void softmax_pv(const f32x4_t (&s)[2], const float (&fk)[2],
+                                           const float (&fv)[2], bool scaled_v, int c0, int end,
+                                           const uint16_t* s_v, f32x4_t (&acc)[D / 16], float& m,
+                                           float& lsum, int lane) {
+  constexpr int VS = D + 16;
+  const int q = lane >> 4, r = lane & 15;
+  const bool full = c0 + kChunk <= end;
   float x[2][4];
   float mc = kNegInf;
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
-    float f = scale_log2;
-    if constexpr (Gm::ELEM == 1) f *= st.ksc[T];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = full || (c0 + 16 * T + 4 * q + i < end);
-      x[T][i] = ok ? s[T][i] * f : kNegInf;
+      x[T][i] = ok ? s[T][i] * fk[T] : kNegInf;
       mc = fmaxf(mc, x[T][i]);
     }
   }
@@ -223,15 +269,14 @@ __device__ __forceinline__ void compute_chunk(const Stage<CT, D>& st, int c0, in
     for (int i = 0; i < 4; ++i) {
       const float e = __builtin_amdgcn_exp2f(x[T][i] - m_new);
       ps += e;
-      pv[T][i] = e;
-      if constexpr (Gm::ELEM == 1) pv[T][i] = e * st.vsc[T];
+      pv[T][i] = scaled_v ? e * fv[T] : e;
     }
   }
   lsum = fmaf(lsum, alpha, ps);
 #pragma unroll
-  for (int md = 0; md < Gm::NMD; ++md) acc[md] *= alpha;
+  for (int md = 0; md < D / 16; ++md) acc[md] *= alpha;
 
-  // 4. O^T += V^T . P^T.  P^T operand: tokens 4q..4q+3 then 16+4q..16+4q+3.
+  // P^T operand: tokens 4q..4q+3 then 16+4q..16+4q+3 of this chunk.
   const bf16x8_t pb = as_bf16x8(make_uint4(pack_bf16x2(pv[0][0], pv[0][1]),
                                            pack_bf16x2(pv[0][2], pv[0][3]),
                                            pack_bf16x2(pv[1][0], pv[1][1]),
@@ -239,9 +284,9 @@ __device__ __forceinline__ void compute_chunk(const Stage<CT, D>& st, int c0, in
   const int trow = 4 * q + (r >> 2);
   const int tcol = 4 * (r & 3);
 #pragma unroll
-  for (int md = 0; md < Gm::NMD; ++md) {
-    const uint16_t* p0 = s_v + trow * Gm::VS + 16 * md + tcol;
-    const uint16_t* p1 = p0 + 16 * Gm::VS;
+  for (int md = 0; md < D / 16; ++md) {
+    const uint16_t* p0 = s_v + trow * VS + 16 * md + tcol;
+    const uint16_t* p1 = p0 + 16 * VS;
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0));
     const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p1));
     const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
@@ -289,10 +334,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(MfmaParams p) {
     const uint4* qp = reinterpret_cast<const uint4*>(
         reinterpret_cast<const uint16_t*>(p.q) + ((size_t)seq * p.H + h0 + min(r, nh - 1)) * D +
         Gm::DQ * q);
+    const bool live = r < nh;
 #pragma unroll
     for (int c = 0; c < Gm::NKC; ++c) {
       uint4 v = qp[c];
-      if (r >= nh) v = make_uint4(0u, 0u, 0u, 0u);
+      v.x = live ? v.x : 0u;
+      v.y = live ? v.y : 0u;
+      v.z = live ? v.z : 0u;
+      v.w = live ? v.w : 0u;
       qf[c] = as_bf16x8(v);
     }
   }
@@ -307,28 +356,38 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(MfmaParams p) {
   const int nch = (end - start + kChunk - 1) / kChunk;
   int ci = wave;
   if (ci < nch) {
-    // Ping-pong register stages: the loads of chunk ci + NW are in flight
-    // while chunk ci is computed.  The prefetch index is clamped to a valid
-    // chunk so that the loads are unconditional (a redundant last prefetch
-    // hits the cache).
-    Stage<CT, D> sa, sb;
-    load_chunk<CT, D, BS>(sa, p, start + ci * kChunk, end, first_blk, s_tab, kvh, lane);
+    KStage<CT, D> ks;
+    VStage<CT, D> vs;
+    load_v<CT, D, BS>(vs, p, start + ci * kChunk, end, first_blk, s_tab, kvh, lane);
+    load_k<CT, D, BS>(ks, p, start + ci * kChunk, end, first_blk, s_tab, kvh, lane);
     while (true) {
-      int cn = ci + NW;
-      load_chunk<CT, D, BS>(sb, p, start + min(cn, nch - 1) * kChunk, end, first_blk, s_tab, kvh,
-                            lane);
-      compute_chunk<CT, D>(sa, start + ci * kChunk, end, qf, p.scale_log2, s_v, acc, m, lsum,
-                           lane);
-      ci = cn;
-      if (ci >= nch) break;
-      cn = ci + NW;
-      load_chunk<CT, D, BS>(sa, p, start + min(cn, nch - 1) * kChunk, end, first_blk, s_tab, kvh,
-                            lane);
-      compute_chunk<CT, D>(sb, start + ci * kChunk, end, qf, p.scale_log2, s_v, acc, m, lsum,
-                           lane);
-      ci = cn;
+      const int c0 = start + ci * kChunk;
+      // The next chunk index is clamped so that every load is unconditional
+      // (a redundant last prefetch hits the cache).
+      const int cn = start + min(ci + NW, nch - 1) * kChunk;
+      store_v<CT, D>(vs, c0, end, s_v, lane);
+      load_v<CT, D, BS>(vs, p, cn, end, first_blk, s_tab, kvh, lane);
+      f32x4_t sc[2];
+      scores<CT, D>(ks, qf, sc);
+      float fk[2], fv[2];
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        fk[T] = p.scale_log2;
+        fv[T] = 1.f;
+        if constexpr (Gm::ELEM == 1) {
+          fk[T] *= ks.ksc[T];
+          fv[T] = ks.vsc[T];
+        }
+      }
+      load_k<CT, D, BS>(ks, p, cn, end, first_blk, s_tab, kvh, lane);
+      softmax_pv<D>(sc, fk, fv, Gm::ELEM == 1, c0, end, s_v, acc, m, lsum, lane);
+      ci += NW;
       if (ci >= nch) break;
     }
+    // The last prefetch is dead on the exit path; this use keeps the compiler
+    // from sinking the prefetch loads into the next iteration, which would
+    // serialise every load with its use.
+    keep_live(vs, ks);
   }
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
