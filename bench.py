@@ -174,7 +174,7 @@ def main():
     P = pkv.decode_partition_size(w.S, w.H, w.H_kv, w.D, w.block_size, w.max_context_len, qc, cc, ps)
     ws_bytes = pkv.decode_workspace_size(w.S, w.H, w.H_kv, w.D, w.block_size, w.max_context_len,
                                          qc, cc, ps)
-    dws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    dws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # counters start at 0
     wws_bytes = pkv.write_workspace_size(max(len(x[2]) for x in writes), w.H_kv, w.num_blocks, cc)
     wws = torch.empty(max(wws_bytes, 1), dtype=torch.uint8, device=dev) if wws_bytes else None
 

@@ -136,7 +136,11 @@ size_t paged_kv_cache_write_workspace_size(
  *   longer than one partition are split, each partition is attended on its
  *   own, and a second kernel merges the partial results.
  *   workspace: at least paged_attention_decode_workspace_size(...) bytes
- *   (any contents; may be NULL when that size is 0).
+ *   (always >= 256).  Its first 256 bytes are work-queue counters: they must
+ *   be zero before the first call that uses the workspace (allocate it
+ *   zero-filled) and every call leaves them zero again; the rest may hold
+ *   anything.  Calls that may run at the same time must not share a
+ *   workspace.
  *   num_seqs == 0 returns PKV_OK after the size and dtype checks without
  *   inspecting any pointer.
  */

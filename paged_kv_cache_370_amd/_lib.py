@@ -161,8 +161,9 @@ def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
     _, H_kv, bs, _ = key_cache.shape
     qc, cc = dtype_code(query), dtype_code(key_cache)
     if workspace is None:
+        # zero-filled: the first 256 bytes are the library's work-queue counters
         need = decode_workspace_size(S, H, H_kv, D, bs, max_context_len, qc, cc, partition_size)
-        workspace = torch.empty(need, dtype=torch.uint8, device=query.device) if need else None
+        workspace = torch.zeros(need, dtype=torch.uint8, device=query.device) if need else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return (_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
             _ptr(value_scale), _ptr(block_tables), _ptr(context_lens), S, H, H_kv, D, bs,

@@ -49,11 +49,15 @@ pkv_status_t check_decode_shape(int S, int H, int H_kv, int D, int bs, int max_c
   return PKV_OK;
 }
 
+// Workspace: a 256-byte header of work-queue counters, then the split
+// partials (m, l, acc) when a context can span more than one partition.
+constexpr size_t kSchedBytes = 256;
+
 size_t decode_workspace(int S, int H, int D, int max_ctx, int P) {
   const int np = num_partitions(max_ctx, P);
-  if (np <= 1) return 0;
+  if (np <= 1) return kSchedBytes;
   const size_t rows = (size_t)S * H * np;
-  return 2 * align256(rows * sizeof(float)) + align256(rows * D * sizeof(float));
+  return kSchedBytes + 2 * align256(rows * sizeof(float)) + align256(rows * D * sizeof(float));
 }
 
 struct DecodeSetup {
@@ -100,7 +104,7 @@ DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
     }
   }
   const size_t need = decode_workspace(S, H, D, max_ctx, P);
-  if (need > 0 && (!workspace || workspace_bytes < need)) {
+  if (!workspace || workspace_bytes < need) {
     r.status = PKV_ERR_WORKSPACE;
     return r;
   }
@@ -111,12 +115,16 @@ DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
   a.S = S; a.H = H; a.H_kv = H_kv; a.D = D; a.bs = bs; a.max_blocks = max_blocks;
   a.max_ctx = max_ctx; a.scale = scale; a.q_dtype = q; a.cache_dtype = c;
   a.P = P; a.NP = num_partitions(max_ctx, P);
-  if (need > 0) {
-    const size_t rows = (size_t)S * H * a.NP;
+  {
     char* ws = reinterpret_cast<char*>(workspace);
-    a.ws_m = reinterpret_cast<float*>(ws);
-    a.ws_l = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
-    a.ws_acc = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+    a.sched = reinterpret_cast<int*>(ws);
+    if (a.NP > 1) {
+      const size_t rows = (size_t)S * H * a.NP;
+      char* part = ws + kSchedBytes;
+      a.ws_m = reinterpret_cast<float*>(part);
+      a.ws_l = reinterpret_cast<float*>(part + align256(rows * sizeof(float)));
+      a.ws_acc = reinterpret_cast<float*>(part + 2 * align256(rows * sizeof(float)));
+    }
   }
   a.stream = reinterpret_cast<hipStream_t>(stream);
   return r;

@@ -1,31 +1,49 @@
-// PagedAttention decode on the matrix cores: one workgroup per (sequence,
-// KV head, chunk of up to 16 of its query heads, context partition).
+// PagedAttention decode on the matrix cores, for query heads grouped over a
+// shared KV head.
 //
 // What is computed: softmax(q K^T * scale) V over the sequence's context
 // (dpshk.com PagedAttention article "企业官网建设流程全解析", section 2.2), K/V
 // reached block by block through the block table (page "PagedAttention 与连续
 // 批处理…", section "PagedAttention：把显存做成虚拟内存").  ONE softmax over
 // the whole context, carried across 32-token chunks with a running maximum
-// and sum; partitions are merged by the reduce kernel.
+// and sum; partitions of a long context are merged by the reduce kernel.
 //
-// Why MFMA here: the query heads that share a KV head turn both products
-// into small dense contractions, [16 tokens x D] . [D x 16 heads] for the
-// scores and [D x 32 tokens] . [32 tokens x 16 heads] for P V, so every K/V
-// byte fetched from HBM feeds up to 16 heads without vector-ALU dot
-// products.  Heads beyond the group are zero columns.
+// Work items are (KV head [x chunk of 16 of its query heads], sequence,
+// partition).  The grid is persistent (as many workgroups as are resident
+// at once): every workgroup first turns the context lengths into
+// per-sequence partition offsets (an LDS scan), then takes items from one
+// of 8 work queues with an atomic counter, so no workgroup is launched for a
+// partition past its sequence's end and uneven items balance dynamically.
+// Queue x holds the items congruent to x mod 8 and is served by workgroups
+// blockIdx.x = x mod 8, which the hardware places on XCD x; with the KV head
+// as the fastest item index each XCD's L2 then serves a fixed set of KV
+// heads (blocks shared between sequences come from HBM once per XCD).  The
+// last workgroup of a queue to finish resets its counters to zero for the
+// next call.
+//
+// Why MFMA: the query heads that share a KV head turn both products into
+// small dense contractions, [16 tokens x D] . [D x 16 heads] for the scores
+// and [D x 32 tokens] . [32 tokens x 16 heads] for P V, so every K/V byte
+// fetched from HBM feeds up to 16 heads without vector-ALU dot products.
+// Heads beyond the group are zero columns.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 (wave64; l = 16 q + r):
 //   A: lane l holds A[r][8q .. 8q+7]    B: lane l holds B[8q .. 8q+7][r]
 //   C: lane l holds C[4q .. 4q+3][r]
-// Scores S^T = K . Q^T take K rows as A straight from HBM: lane l loads
-// D/4 contiguous elements of token r, and the contraction index d is permuted
-// identically in K and Q (d = (D/4) q + 8 c + e for step c), which leaves the
-// dot products unchanged.  The result gives every lane ONE head (column r)
-// and four tokens, so the running max / sum are per lane.  For P V the lane's
-// eight probabilities (tokens 4q..4q+3 of both 16-token halves) are exactly
-// the B operand of O^T = V^T . P^T; V^T fragments come from the V tile staged
-// in LDS through ds_read_b64_tr_b16, which hands lane i of a 16-lane group
-// element (i % 4) of the 8-byte row addressed by lane 4 e + i / 4.
+// Every lane loads D/4 contiguous elements of ONE token (token r of a
+// 16-token tile, elements (D/4) q ..) from both K and V, so one block-table
+// lookup per tile addresses both.  The K slice is the A operand of
+// S^T = K . Q^T directly: the contraction index d is permuted identically in
+// K and Q (d = (D/4) q + 8 c + e at step c), which leaves every dot product
+// unchanged.  The result gives each lane ONE head (column r) and four tokens,
+// so the running max and sum are per lane.  For P V the lane's eight
+// probabilities (tokens 4q..4q+3 of two consecutive tiles) are exactly the B
+// operand of O^T = V^T . P^T; V^T fragments come from the V tile staged in
+// LDS as bf16 through ds_read_b64_tr_b16, which hands lane i of a 16-lane
+// group element (i % 4) of the 8-byte row addressed by lane 4 e + i / 4.
+// Tile rows are padded to D + 16 elements (a 288-byte stride for D = 128):
+// the 8 rows one transpose read touches then fall on distinct LDS banks, and
+// every address stays a per-lane base plus an immediate offset.
 //
 // Masking: loads use clamped (always valid) addresses and never branch; the
 // scores of tokens past the partition end are replaced by -inf and their V
@@ -41,8 +59,10 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int kChunk = 32;      // tokens per pipeline step (two 16-token tiles)
-constexpr int kMaxTable = 256;  // block-table entries one partition may span
+constexpr int kMaxTable = 256;      // block-table entries one partition may span
+constexpr int kMaxScanSeqs = 1024;  // sequences whose offsets a workgroup keeps in LDS
+constexpr int kNW = 4;              // waves per workgroup
+constexpr int kNT = 2;              // 16-token tiles per pipeline step
 
 struct MfmaParams {
   const void* q;
@@ -56,7 +76,8 @@ struct MfmaParams {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
-  int H, H_kv, G, chunks, max_blocks, P, NP;
+  int* sched;  // [0..7] next item per queue, [8..15] finished workgroups per queue
+  int S, H, H_kv, G, chunks, max_blocks, P, NP;
   float scale_log2;
 };
 
@@ -91,14 +112,14 @@ template <typename CT, int D>
 struct Geometry {
   using CS = typename CT::storage;
   static constexpr int ELEM = (int)sizeof(CS);
-  static constexpr int DQ = D / 4;              // d elements per lane per K row
-  static constexpr int NKC = D / 32;            // k-steps of the score MFMA
-  static constexpr int NMD = D / 16;            // 16-wide d tiles of the output
-  static constexpr int KV4 = DQ * ELEM / 16;    // uint4 per lane per K tile
-  static constexpr int PR = D * ELEM / 16;      // 16-byte pieces per V row
-  static constexpr int RPI = 64 / PR;           // V rows per wave load
-  static constexpr int VI = kChunk / RPI;       // V wave loads per chunk
-  static constexpr int VS = D + 16;             // LDS V row stride (bf16), padded
+  static constexpr int DQ = D / 4;            // elements per lane per token row
+  static constexpr int NKC = D / 32;          // k-steps of the score MFMA
+  static constexpr int NMD = D / 16;          // 16-wide d tiles of the output
+  static constexpr int KV4 = DQ * ELEM / 16;  // uint4 per lane per tile (K, and V)
+  static constexpr int CHUNK = 16 * kNT;      // tokens per pipeline step
+  static constexpr int PR = D * ELEM / 16;    // 16-byte pieces per cache row
+  static constexpr int RPI = 64 / PR;         // rows per wave load of V
+  static constexpr int VS = D + 16;           // LDS row stride of the V tile (bf16)
 };
 
 // Registers that carry one chunk from HBM to the products.  K and V have one
@@ -108,126 +129,138 @@ struct Geometry {
 // are issued, so both loads are in flight while chunk i finishes.
 template <typename CT, int D>
 struct KStage {
-  using Gm = Geometry<CT, D>;
-  uint4 k[2][Gm::KV4];
-  float ksc[2], vsc[2];  // FP8 scales of the lane's two 4-token groups
+  uint4 k[kNT][Geometry<CT, D>::KV4];
+  float ksc[kNT], vsc[kNT];  // FP8 scales of the lane's 4-token groups
 };
 
 template <typename CT, int D>
 struct VStage {
-  uint4 v[Geometry<CT, D>::VI];
+  uint4 v[kNT][Geometry<CT, D>::KV4];  // the chunk's V rows, kNT*KV4 wave loads
 };
+
+// One work item's view of its partition.
+struct Part {
+  int seq, kvh, h0, nh, start, end, first_blk;
+  const int* s_tab;
+};
+
+template <typename CT, int D, int BS>
+__device__ __forceinline__ size_t token_row(const MfmaParams& p, const Part& w, int t, int lane) {
+  const int phys = w.s_tab[t / BS - w.first_blk];
+  return (((size_t)phys * p.H_kv + w.kvh) * BS + (t % BS)) * D + Geometry<CT, D>::DQ * (lane >> 4);
+}
 
 template <typename CT, int D>
 __device__ __forceinline__ void keep_live(const VStage<CT, D>& vs, const KStage<CT, D>& ks) {
 #pragma unroll
-  for (int j = 0; j < Geometry<CT, D>::VI; ++j)
-    asm volatile("" ::"v"(vs.v[j].x), "v"(vs.v[j].y), "v"(vs.v[j].z), "v"(vs.v[j].w));
+  for (int T = 0; T < kNT; ++T)
 #pragma unroll
-  for (int T = 0; T < 2; ++T)
-#pragma unroll
-    for (int i = 0; i < Geometry<CT, D>::KV4; ++i)
+    for (int i = 0; i < Geometry<CT, D>::KV4; ++i) {
+      asm volatile("" ::"v"(vs.v[T][i].x), "v"(vs.v[T][i].y), "v"(vs.v[T][i].z),
+                   "v"(vs.v[T][i].w));
       asm volatile("" ::"v"(ks.k[T][i].x), "v"(ks.k[T][i].y), "v"(ks.k[T][i].z),
                    "v"(ks.k[T][i].w));
+    }
 }
 
-template <int BS>
-__device__ __forceinline__ size_t row_index(const int* s_tab, int t, int first_blk, int H_kv,
-                                            int kvh) {
-  const int phys = s_tab[t / BS - first_blk];
-  return ((size_t)phys * H_kv + kvh) * BS + (t % BS);
+// V rows are fetched whole: wave load j covers rows j*RPI .. of the chunk,
+// lane l the 16-byte piece l % PR of row j*RPI + l / PR, so every load
+// instruction reads whole token rows (fully used cache lines).
+template <typename CT, int D, int BS>
+__device__ __forceinline__ void load_v(VStage<CT, D>& st, const MfmaParams& p, const Part& w,
+                                       int c0, int lane) {
+  using CS = typename CT::storage;
+  using Gm = Geometry<CT, D>;
+  constexpr int PR = Gm::PR, RPI = Gm::RPI;
+  const CS* vc = reinterpret_cast<const CS*>(p.vc);
+  uint4* flat = &st.v[0][0];
+#pragma unroll
+  for (int j = 0; j < kNT * Gm::KV4; ++j) {
+    const int t = min(c0 + j * RPI + lane / PR, w.end - 1);  // clamped: masked later
+    const int phys = w.s_tab[t / BS - w.first_blk];
+    const size_t row = ((size_t)phys * p.H_kv + w.kvh) * BS + (t % BS);
+    flat[j] = reinterpret_cast<const uint4*>(vc + row * D)[lane % PR];
+  }
 }
 
 template <typename CT, int D, int BS>
-__device__ __forceinline__ void load_k(KStage<CT, D>& st, const MfmaParams& p, int c0, int end,
-                                       int first_blk, const int* s_tab, int kvh, int lane) {
-  using Gm = Geometry<CT, D>;
+__device__ __forceinline__ void load_k(KStage<CT, D>& st, const MfmaParams& p, const Part& w,
+                                       int c0, int lane) {
   using CS = typename CT::storage;
-  const int q = lane >> 4, r = lane & 15;
   const CS* kc = reinterpret_cast<const CS*>(p.kc);
 #pragma unroll
-  for (int T = 0; T < 2; ++T) {
-    const int t = min(c0 + 16 * T + r, end - 1);  // clamped: masked later
-    const size_t row = row_index<BS>(s_tab, t, first_blk, p.H_kv, kvh);
-    const uint4* src = reinterpret_cast<const uint4*>(kc + row * D + Gm::DQ * q);
+  for (int T = 0; T < kNT; ++T) {
+    const int t = min(c0 + 16 * T + (lane & 15), w.end - 1);  // clamped: masked later
+    const uint4* src = reinterpret_cast<const uint4*>(kc + token_row<CT, D, BS>(p, w, t, lane));
 #pragma unroll
-    for (int i = 0; i < Gm::KV4; ++i) st.k[T][i] = src[i];
-    if constexpr (Gm::ELEM == 1) {
-      const int ts = min(c0 + 16 * T + 4 * q, end - 1);
-      const size_t si = (size_t)s_tab[ts / BS - first_blk] * p.H_kv + kvh;
+    for (int i = 0; i < Geometry<CT, D>::KV4; ++i) st.k[T][i] = src[i];
+    if constexpr (Geometry<CT, D>::ELEM == 1) {
+      // the lane's scores are tokens 16T + 4q + i: one block for every bs >= 4
+      const int ts = min(c0 + 16 * T + 4 * (lane >> 4), w.end - 1);
+      const size_t si = (size_t)w.s_tab[ts / BS - w.first_blk] * p.H_kv + w.kvh;
       st.ksc[T] = p.ks[si];
       st.vsc[T] = p.vs[si];
     }
   }
 }
 
-template <typename CT, int D, int BS>
-__device__ __forceinline__ void load_v(VStage<CT, D>& st, const MfmaParams& p, int c0, int end,
-                                       int first_blk, const int* s_tab, int kvh, int lane) {
-  using Gm = Geometry<CT, D>;
-  using CS = typename CT::storage;
-  const CS* vc = reinterpret_cast<const CS*>(p.vc);
-#pragma unroll
-  for (int j = 0; j < Gm::VI; ++j) {
-    const int t = min(c0 + j * Gm::RPI + lane / Gm::PR, end - 1);
-    const size_t row = row_index<BS>(s_tab, t, first_blk, p.H_kv, kvh);
-    st.v[j] = reinterpret_cast<const uint4*>(vc + row * D)[lane % Gm::PR];
-  }
-}
-
-// V rows of one chunk -> this wave's LDS tile as bf16 (rows past the end as
-// zeros).
+// The chunk's V rows -> this wave's LDS tile as bf16 (rows past the end as
+// zeros), in the order load_v fetched them.
 template <typename CT, int D>
 __device__ __forceinline__ void store_v(const VStage<CT, D>& st, int c0, int end, uint16_t* s_v,
                                         int lane) {
   using Gm = Geometry<CT, D>;
-  const bool full = c0 + kChunk <= end;
+  const bool full = c0 + Gm::CHUNK <= end;
   wave_lds_sync();  // the previous chunk's transpose reads are done
 #pragma unroll
-  for (int j = 0; j < Gm::VI; ++j) {
-    const int row = j * Gm::RPI + lane / Gm::PR;
-    const int piece = lane % Gm::PR;
-    uint4 v = st.v[j];
-    if (!full) {  // uniform: only the last chunk of a partition is ragged
-      const bool ok = c0 + row < end;
-      v.x = ok ? v.x : 0u;
-      v.y = ok ? v.y : 0u;
-      v.z = ok ? v.z : 0u;
-      v.w = ok ? v.w : 0u;
-    }
-    if constexpr (Gm::ELEM == 2) {
-      *reinterpret_cast<uint4*>(s_v + row * Gm::VS + piece * 8) = v;
-    } else {
-      const uint2 a = fp8x4_to_bf16x4(v.x), b = fp8x4_to_bf16x4(v.y);
-      const uint2 c = fp8x4_to_bf16x4(v.z), d = fp8x4_to_bf16x4(v.w);
-      uint4* dst = reinterpret_cast<uint4*>(s_v + row * Gm::VS + piece * 16);
-      dst[0] = make_uint4(a.x, a.y, b.x, b.y);
-      dst[1] = make_uint4(c.x, c.y, d.x, d.y);
+  for (int T = 0; T < kNT; ++T) {
+#pragma unroll
+    for (int i = 0; i < Gm::KV4; ++i) {
+      const int j = T * Gm::KV4 + i;
+      const int row = j * Gm::RPI + lane / Gm::PR;
+      const int piece = lane % Gm::PR;
+      uint4 v = st.v[T][i];
+      if (!full) {
+        const bool ok = c0 + row < end;
+        v.x = ok ? v.x : 0u; v.y = ok ? v.y : 0u; v.z = ok ? v.z : 0u; v.w = ok ? v.w : 0u;
+      }
+      if constexpr (Gm::ELEM == 2) {
+        *reinterpret_cast<uint4*>(s_v + row * Gm::VS + piece * 8) = v;
+      } else {
+        const uint2 a = fp8x4_to_bf16x4(v.x), b = fp8x4_to_bf16x4(v.y);
+        const uint2 c = fp8x4_to_bf16x4(v.z), d = fp8x4_to_bf16x4(v.w);
+        uint4* dst = reinterpret_cast<uint4*>(s_v + row * Gm::VS + piece * 16);
+        dst[0] = make_uint4(a.x, a.y, b.x, b.y);
+        dst[1] = make_uint4(c.x, c.y, d.x, d.y);
+      }
     }
   }
   wave_lds_sync();  // the tile is visible to every lane of the wave
 }
 
-// Scores S^T = K . Q^T of both 16-token tiles: lane (q, r) gets head r,
+// Scores S^T = K . Q^T of the chunk's tiles: lane (q, r) gets head r,
 // tokens 16 T + 4 q + i.
 template <typename CT, int D>
-__device__ __forceinline__ void scores(const KStage<CT, D>& st,
-                                       const bf16x8_t (&qf)[Geometry<CT, D>::NKC],
-                                       f32x4_t (&s)[2]) {
+__device__ __forceinline__ void scores(const KStage<CT, D>& st, const uint4* s_qf,
+                                       f32x4_t (&s)[kNT], int lane) {
   using Gm = Geometry<CT, D>;
+  // Q operand fragments, kept in LDS to spare registers: lane (q, r) reads
+  // head r, elements (D/4) q + 8 c .. + 8, stored as s_qf[c][lane].
+  bf16x8_t qf[Gm::NKC];
 #pragma unroll
-  for (int T = 0; T < 2; ++T) {
+  for (int c = 0; c < Gm::NKC; ++c) qf[c] = as_bf16x8(s_qf[c * 64 + lane]);
+#pragma unroll
+  for (int T = 0; T < kNT; ++T) {
     s[T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < Gm::NKC; ++c) {
       bf16x8_t a;
       if constexpr (Gm::ELEM == 2) {
-        a = as_bf16x8(st.k[T][c]);  // bytes 16c..16c+15 of the lane's row slice
+        a = as_bf16x8(st.k[T][c]);  // bytes 16c..16c+15 of the lane's slice
       } else {
         const uint4 w = st.k[T][c / 2];  // bytes 8c..8c+7 of the lane's 32-byte slice
-        const uint32_t w0 = (c & 1) ? w.z : w.x;
-        const uint32_t w1 = (c & 1) ? w.w : w.y;
-        const uint2 lo = fp8x4_to_bf16x4(w0), hi = fp8x4_to_bf16x4(w1);
+        const uint2 lo = fp8x4_to_bf16x4((c & 1) ? w.z : w.x);
+        const uint2 hi = fp8x4_to_bf16x4((c & 1) ? w.w : w.y);
         a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
       s[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], s[T], 0, 0, 0);
@@ -237,17 +270,17 @@ __device__ __forceinline__ void scores(const KStage<CT, D>& st,
 
 // Online softmax update with this chunk's scores, then O^T += V^T . P^T.
 template <int D>
-__device__ __forceinline__ void softmax_pv(const f32x4_t (&s)[2], const float (&fk)[2],
-                                           const float (&fv)[2], bool scaled_v, int c0, int end,
+__device__ __forceinline__ void softmax_pv(const f32x4_t (&s)[kNT], const float (&fk)[kNT],
+                                           const float (&fv)[kNT], bool scaled_v, int c0, int end,
                                            const uint16_t* s_v, f32x4_t (&acc)[D / 16], float& m,
                                            float& lsum, int lane) {
   constexpr int VS = D + 16;
   const int q = lane >> 4, r = lane & 15;
-  const bool full = c0 + kChunk <= end;
-  float x[2][4];
+  const bool full = c0 + 16 * kNT <= end;
+  float x[kNT][4];
   float mc = kNegInf;
 #pragma unroll
-  for (int T = 0; T < 2; ++T) {
+  for (int T = 0; T < kNT; ++T) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = full || (c0 + 16 * T + 4 * q + i < end);
@@ -261,10 +294,10 @@ __device__ __forceinline__ void softmax_pv(const f32x4_t (&s)[2], const float (&
   const float alpha = __builtin_amdgcn_exp2f(m - m_new);
   m = m_new;
 
-  float pv[2][4];
+  float pv[kNT][4];
   float ps = 0.f;
 #pragma unroll
-  for (int T = 0; T < 2; ++T) {
+  for (int T = 0; T < kNT; ++T) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float e = __builtin_amdgcn_exp2f(x[T][i] - m_new);
@@ -273,181 +306,321 @@ __device__ __forceinline__ void softmax_pv(const f32x4_t (&s)[2], const float (&
     }
   }
   lsum = fmaf(lsum, alpha, ps);
+  // Unconditional: a branch around the rescale makes the register allocator
+  // reconcile the accumulators with copies, whose sources include registers
+  // the prefetch loads are filling, which forces a wait on those loads.
 #pragma unroll
   for (int md = 0; md < D / 16; ++md) acc[md] *= alpha;
 
-  // P^T operand: tokens 4q..4q+3 then 16+4q..16+4q+3 of this chunk.
-  const bf16x8_t pb = as_bf16x8(make_uint4(pack_bf16x2(pv[0][0], pv[0][1]),
-                                           pack_bf16x2(pv[0][2], pv[0][3]),
-                                           pack_bf16x2(pv[1][0], pv[1][1]),
-                                           pack_bf16x2(pv[1][2], pv[1][3])));
-  const int trow = 4 * q + (r >> 2);
-  const int tcol = 4 * (r & 3);
+  // Transpose reads: lane j of group q addresses row 4q + j/4 (and + 16) at
+  // d = 16 md + 4 (j % 4).
+  const uint16_t* rowp = s_v + (4 * q + (r >> 2)) * VS + 4 * (r & 3);
 #pragma unroll
-  for (int md = 0; md < D / 16; ++md) {
-    const uint16_t* p0 = s_v + trow * VS + 16 * md + tcol;
-    const uint16_t* p1 = p0 + 16 * VS;
-    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0));
-    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p1));
-    const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
-    const bf16x8_t a = as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
-    acc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[md], 0, 0, 0);
+  for (int u = 0; u < kNT / 2; ++u) {
+    // P^T operand: tokens 4q..4q+3 of tile 2u, then of tile 2u+1.
+    const bf16x8_t pb = as_bf16x8(make_uint4(pack_bf16x2(pv[2 * u][0], pv[2 * u][1]),
+                                             pack_bf16x2(pv[2 * u][2], pv[2 * u][3]),
+                                             pack_bf16x2(pv[2 * u + 1][0], pv[2 * u + 1][1]),
+                                             pack_bf16x2(pv[2 * u + 1][2], pv[2 * u + 1][3])));
+#pragma unroll
+    for (int md = 0; md < D / 16; ++md) {
+      const uint16_t* p0 = rowp + 32 * u * VS + 16 * md;
+      const uint16_t* p1 = p0 + 16 * VS;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p1));
+      const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+      const bf16x8_t a = as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+      acc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[md], 0, 0, 0);
+    }
+  }
+  // Interleave the transpose reads with the products (two reads, one MFMA)
+  // instead of issuing all reads first: that holds 2 fragments, not 2 * NMD.
+#pragma unroll
+  for (int i = 0; i < (kNT / 2) * (D / 16); ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
   }
 }
 
-template <typename CT, int D, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(MfmaParams p) {
+// s_off[i] = number of items (partitions) of sequences 0..i-1 (a sequence of
+// length 0 still has one, which writes zeros); s_len[i] = its length.
+// Returns s_off[S].  Every thread of the workgroup calls it.
+__device__ int build_offsets(const MfmaParams& p, int* s_off, int* s_len, int* s_red) {
+  constexpr int NTH = kNW * 64;
+  const int tid = threadIdx.x;
+  const int per = (p.S + NTH - 1) / NTH;
+  const int base = tid * per;
+  int local = 0;
+  for (int k = 0; k < per; ++k) {
+    const int i = base + k;
+    if (i < p.S) {
+      const int n = p.lens[i];
+      s_len[i] = n;
+      local += max(1, (n + p.P - 1) / p.P);
+    }
+  }
+  int x = local;  // inclusive scan over the workgroup
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_red[wave] = x;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) x += s_red[w];
+  int excl = x - local;
+  for (int k = 0; k < per; ++k) {
+    const int i = base + k;
+    if (i < p.S) {
+      s_off[i] = excl;
+      excl += max(1, (s_len[i] + p.P - 1) / p.P);
+    }
+  }
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) total += s_red[w];
+  if (tid == 0) s_off[p.S] = total;
+  __syncthreads();
+  return total;
+}
+
+// Largest i with s_off[i] <= rest (offsets strictly increase).
+__device__ __forceinline__ int find_seq(const int* s_off, int S, int rest) {
+  int lo = 0, hi = S;  // s_off[lo] <= rest < s_off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_off[mid] <= rest) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+template <typename CT, int D, int BS, bool SCAN>
+__global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   using Gm = Geometry<CT, D>;
-  constexpr int VTILE = kChunk * Gm::VS;        // bf16 elements per wave
-  constexpr int MERGE = NW * 16 * D;            // fp32 partial outputs
-  constexpr int UNION_BYTES = (VTILE * NW * 2 > MERGE * 4) ? VTILE * NW * 2 : MERGE * 4;
+  constexpr int VTILE = Gm::CHUNK * Gm::VS;  // bf16 elements per wave
+  constexpr int MERGE = kNW * 16 * D;   // fp32 partial outputs
+  constexpr int UNION_BYTES = (VTILE * kNW * 2 > MERGE * 4) ? VTILE * kNW * 2 : MERGE * 4;
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[UNION_BYTES];
   __shared__ int s_tab[kMaxTable];
-  __shared__ float s_m[NW][16];
-  __shared__ float s_l[NW][16];
-
-  const int part = blockIdx.x;
-  const int hc = blockIdx.y % p.chunks;
-  const int kvh = blockIdx.y / p.chunks;
-  const int seq = blockIdx.z;
-  const int n = p.lens[seq];
-  const int start = part * p.P;
-  if (part > 0 && start >= n) return;
-  const int end = min(n, start + p.P);
-  const int h0 = kvh * p.G + hc * 16;
-  const int nh = min(16, p.G - hc * 16);
+  __shared__ float s_m[kNW][16];
+  __shared__ float s_l[kNW][16];
+  __shared__ int s_red[kNW];
+  __shared__ uint4 s_qf[Gm::NKC * 64];
+  __shared__ int s_off[SCAN ? kMaxScanSeqs + 1 : 1];
+  __shared__ int s_len[SCAN ? kMaxScanSeqs : 1];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int q = lane >> 4, r = lane & 15;
+  const int Y = p.H_kv * p.chunks;
 
-  // Block ids of this partition, fetched once.
-  const int first_blk = start / BS;
-  const int nblk = end > start ? (end - 1) / BS - first_blk + 1 : 0;
-  const int32_t* trow = p.tables + (size_t)seq * p.max_blocks + first_blk;
-  for (int i = tid; i < nblk; i += NW * 64) s_tab[i] = trow[i];
+  int total;
+  if constexpr (SCAN) total = Y * build_offsets(p, s_off, s_len, s_red);
+  else total = Y * p.S * p.NP;
 
-  // Q operand: lane (q, r) holds head r, elements (D/4) q + 8 c .. + 8.
-  bf16x8_t qf[Gm::NKC];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(p.q) + ((size_t)seq * p.H + h0 + min(r, nh - 1)) * D +
-        Gm::DQ * q);
-    const bool live = r < nh;
-#pragma unroll
-    for (int c = 0; c < Gm::NKC; ++c) {
-      uint4 v = qp[c];
-      v.x = live ? v.x : 0u;
-      v.y = live ? v.y : 0u;
-      v.z = live ? v.z : 0u;
-      v.w = live ? v.w : 0u;
-      qf[c] = as_bf16x8(v);
+  __shared__ int s_item;
+  const int nq = min(8, (int)gridDim.x);
+  const int queue = blockIdx.x % nq;
+  const int queue_wgs = ((int)gridDim.x - queue + nq - 1) / nq;
+  while (true) {
+    if (tid == 0) s_item = atomicAdd(&p.sched[queue], 1) * nq + queue;
+    __syncthreads();
+    const int item = s_item;  // read by every thread before the item's barriers
+    if (item >= total) break;
+    const int y = item % Y;
+    const int rest = item / Y;
+    int seq, part, n;
+    if constexpr (SCAN) {
+      seq = find_seq(s_off, p.S, rest);
+      part = rest - s_off[seq];
+      n = s_len[seq];
+    } else {
+      seq = rest / p.NP;
+      part = rest - seq * p.NP;
+      n = p.lens[seq];
+      if (part > 0 && part * p.P >= n) {  // uniform over the workgroup
+        __syncthreads();  // s_item is rewritten only after every thread read it
+        continue;
+      }
     }
-  }
-  __syncthreads();
+    Part w;
+    w.seq = seq;
+    w.kvh = y / p.chunks;
+    const int hc = y - w.kvh * p.chunks;
+    w.h0 = w.kvh * p.G + hc * 16;
+    w.nh = min(16, p.G - hc * 16);
+    w.start = part * p.P;
+    w.end = min(n, w.start + p.P);
+    w.first_blk = w.start / BS;
+    w.s_tab = s_tab;
 
-  f32x4_t acc[Gm::NMD];
-#pragma unroll
-  for (int md = 0; md < Gm::NMD; ++md) acc[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf, lsum = 0.f;
+    // Block ids of this partition, fetched once (the previous item's readers
+    // of s_tab finished before its merge barrier).
+    const int nblk = w.end > w.start ? (w.end - 1) / BS - w.first_blk + 1 : 0;
+    const int32_t* trow = p.tables + (size_t)seq * p.max_blocks + w.first_blk;
+    for (int i = tid; i < nblk; i += kNW * 64) s_tab[i] = trow[i];
 
-  uint16_t* s_v = reinterpret_cast<uint16_t*>(s_raw) + wave * VTILE;
-  const int nch = (end - start + kChunk - 1) / kChunk;
-  int ci = wave;
-  if (ci < nch) {
-    KStage<CT, D> ks;
-    VStage<CT, D> vs;
-    load_v<CT, D, BS>(vs, p, start + ci * kChunk, end, first_blk, s_tab, kvh, lane);
-    load_k<CT, D, BS>(ks, p, start + ci * kChunk, end, first_blk, s_tab, kvh, lane);
-    while (true) {
-      const int c0 = start + ci * kChunk;
-      // The next chunk index is clamped so that every load is unconditional
-      // (a redundant last prefetch hits the cache).
-      const int cn = start + min(ci + NW, nch - 1) * kChunk;
-      store_v<CT, D>(vs, c0, end, s_v, lane);
-      load_v<CT, D, BS>(vs, p, cn, end, first_blk, s_tab, kvh, lane);
-      f32x4_t sc[2];
-      scores<CT, D>(ks, qf, sc);
-      float fk[2], fv[2];
+    // Q operand fragments -> LDS: s_qf[c][l] for lane l = (q, r) holds head
+    // r, elements (D/4) q + 8 c .. + 8 (zeros for heads past the group).
+    for (int i = tid; i < Gm::NKC * 64; i += kNW * 64) {
+      const int c = i >> 6, l = i & 63;
+      const int hq = l & 15;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (hq < w.nh)
+        v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) +
+                                            ((size_t)seq * p.H + w.h0 + hq) * D +
+                                            Gm::DQ * (l >> 4) + 8 * c);
+      s_qf[i] = v;
+    }
+    __syncthreads();
+
+    f32x4_t acc[Gm::NMD];
 #pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        fk[T] = p.scale_log2;
-        fv[T] = 1.f;
-        if constexpr (Gm::ELEM == 1) {
-          fk[T] *= ks.ksc[T];
-          fv[T] = ks.vsc[T];
+    for (int md = 0; md < Gm::NMD; ++md) acc[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, lsum = 0.f;
+
+    uint16_t* s_v = reinterpret_cast<uint16_t*>(s_raw) + wave * VTILE;
+    const int nch = (w.end - w.start + Gm::CHUNK - 1) / Gm::CHUNK;
+    int ci = wave;
+    if (ci < nch) {
+      KStage<CT, D> ks;
+      VStage<CT, D> vs;
+      load_v<CT, D, BS>(vs, p, w, w.start + ci * Gm::CHUNK, lane);
+      load_k<CT, D, BS>(ks, p, w, w.start + ci * Gm::CHUNK, lane);
+      while (true) {
+        const int c0 = w.start + ci * Gm::CHUNK;
+        // The next chunk index is clamped so that every load is
+        // unconditional (a redundant last prefetch hits the cache).
+        const int cn = w.start + min(ci + kNW, nch - 1) * Gm::CHUNK;
+        store_v<CT, D>(vs, c0, w.end, s_v, lane);
+        load_v<CT, D, BS>(vs, p, w, cn, lane);
+        // Keep the scheduler from sinking the prefetch below the products:
+        // the loads must be in flight while this chunk is computed.
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t sc[kNT];
+        scores<CT, D>(ks, s_qf, sc, lane);
+        float fk[kNT], fv[kNT];
+#pragma unroll
+        for (int T = 0; T < kNT; ++T) {
+          fk[T] = p.scale_log2;
+          fv[T] = 1.f;
+          if constexpr (Gm::ELEM == 1) {
+            fk[T] *= ks.ksc[T];
+            fv[T] = ks.vsc[T];
+          }
+        }
+        load_k<CT, D, BS>(ks, p, w, cn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        softmax_pv<D>(sc, fk, fv, Gm::ELEM == 1, c0, w.end, s_v, acc, m, lsum, lane);
+        ci += kNW;
+        if (ci >= nch) break;
+      }
+      // The last prefetch is dead on the exit path; this use keeps the
+      // compiler from sinking the prefetch loads into the next iteration,
+      // which would serialise every load with its use.
+      keep_live(vs, ks);
+    }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+
+    // Merge the wave-level softmax states of this partition.
+    __syncthreads();  // every wave is done with its V tile (s_raw is reused)
+    float* s_acc = reinterpret_cast<float*>(s_raw);
+    if (q == 0) {
+      s_m[wave][r] = m;
+      s_l[wave][r] = lsum;
+    }
+#pragma unroll
+    for (int md = 0; md < Gm::NMD; ++md)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + r) * D + 16 * md + 4 * q + i] = acc[md][i];
+    __syncthreads();
+
+    const bool single = n <= p.P;
+    for (int idx = tid; idx < w.nh * D; idx += kNW * 64) {
+      const int g = idx / D;
+      const int d = idx - g * D;
+      float M = kNegInf;
+#pragma unroll
+      for (int k = 0; k < kNW; ++k) M = fmaxf(M, s_m[k][g]);
+      float L = 0.f, O = 0.f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int k = 0; k < kNW; ++k) {
+          const float wt = __builtin_amdgcn_exp2f(s_m[k][g] - M);
+          L = fmaf(s_l[k][g], wt, L);
+          O = fmaf(s_acc[(k * 16 + g) * D + d], wt, O);
         }
       }
-      load_k<CT, D, BS>(ks, p, cn, end, first_blk, s_tab, kvh, lane);
-      softmax_pv<D>(sc, fk, fv, Gm::ELEM == 1, c0, end, s_v, acc, m, lsum, lane);
-      ci += NW;
-      if (ci >= nch) break;
-    }
-    // The last prefetch is dead on the exit path; this use keeps the compiler
-    // from sinking the prefetch loads into the next iteration, which would
-    // serialise every load with its use.
-    keep_live(vs, ks);
-  }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-
-  // Merge the NW wave-level softmax states of this partition.
-  __syncthreads();  // every wave is done with its V tile (s_raw is reused)
-  float* s_acc = reinterpret_cast<float*>(s_raw);
-  if (q == 0) {
-    s_m[wave][r] = m;
-    s_l[wave][r] = lsum;
-  }
-#pragma unroll
-  for (int md = 0; md < Gm::NMD; ++md)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + r) * D + 16 * md + 4 * q + i] = acc[md][i];
-  __syncthreads();
-
-  const bool single = n <= p.P;
-  for (int idx = tid; idx < nh * D; idx += NW * 64) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
-    float L = 0.f, O = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float wt = __builtin_amdgcn_exp2f(s_m[w][g] - M);
-        L = fmaf(s_l[w][g], wt, L);
-        O = fmaf(s_acc[(w * 16 + g) * D + d], wt, O);
+      const int h = w.h0 + g;
+      if (single) {
+        const float o = L > 0.f ? O / L : 0.f;
+        reinterpret_cast<uint16_t*>(p.out)[((size_t)seq * p.H + h) * D + d] = f32_to_bf16(o);
+      } else {
+        const size_t pi = ((size_t)seq * p.H + h) * p.NP + part;
+        p.ws_acc[pi * D + d] = O;
+        if (d == 0) {
+          p.ws_m[pi] = M;
+          p.ws_l[pi] = L;
+        }
       }
     }
-    const int h = h0 + g;
-    if (single) {
-      const float o = L > 0.f ? O / L : 0.f;
-      reinterpret_cast<uint16_t*>(p.out)[((size_t)seq * p.H + h) * D + d] = f32_to_bf16(o);
-    } else {
-      const size_t pi = ((size_t)seq * p.H + h) * p.NP + part;
-      p.ws_acc[pi * D + d] = O;
-      if (d == 0) {
-        p.ws_m[pi] = M;
-        p.ws_l[pi] = L;
-      }
-    }
+    // s_m / s_l / s_raw are rewritten only after the next item's first barrier.
   }
+  // The last workgroup of this queue to finish returns its counters to zero.
+  if (tid == 0 && atomicAdd(&p.sched[8 + queue], 1) == queue_wgs - 1) {
+    atomicExch(&p.sched[queue], 0);
+    atomicExch(&p.sched[8 + queue], 0);
+  }
+}
+
+// Workgroups of a persistent launch: as many as are resident at once (CUs x
+// the kernel's occupancy, a multiple of the 8 XCDs), never more than items.
+// The occupancy query runs once per kernel variant and device.
+template <typename CT, int D, int BS, bool SCAN>
+unsigned persistent_grid(long long items) {
+  constexpr int kMaxDev = 64;
+  static int resident[kMaxDev];  // per device, for this kernel variant only
+  const void* kern = reinterpret_cast<const void*>(decode_mfma_kernel<CT, D, BS, SCAN>);
+  int dev = 0;
+  int per_dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDev) per_dev = resident[dev];
+  if (per_dev <= 0) {
+    int cus = 0, blocks = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kern, kNW * 64, 0) != hipSuccess ||
+        blocks <= 0)
+      blocks = 1;
+    per_dev = (cus * blocks + 7) / 8 * 8;
+    if (dev >= 0 && dev < kMaxDev) resident[dev] = per_dev;
+  }
+  return (unsigned)(per_dev < items ? per_dev : items);
 }
 
 template <typename CT, int D, int BS>
 hipError_t launch_bs(const DecodeArgs& a) {
-  constexpr int NW = 4;
   MfmaParams p;
   p.q = a.q; p.kc = a.key_cache; p.vc = a.value_cache; p.ks = a.key_scale; p.vs = a.value_scale;
   p.tables = a.tables; p.lens = a.lens; p.out = a.out;
-  p.ws_m = a.ws_m; p.ws_l = a.ws_l; p.ws_acc = a.ws_acc;
-  p.H = a.H; p.H_kv = a.H_kv; p.G = a.H / a.H_kv; p.chunks = (p.G + 15) / 16;
+  p.ws_m = a.ws_m; p.ws_l = a.ws_l; p.ws_acc = a.ws_acc; p.sched = a.sched;
+  p.S = a.S; p.H = a.H; p.H_kv = a.H_kv; p.G = a.H / a.H_kv; p.chunks = (p.G + 15) / 16;
   p.max_blocks = a.max_blocks; p.P = a.P; p.NP = a.NP;
   p.scale_log2 = a.scale * kLog2e;
-  dim3 grid(a.NP, a.H_kv * p.chunks, a.S);
-  hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, NW>), grid, dim3(NW * 64), 0, a.stream, p);
+  const long long items = (long long)a.H_kv * p.chunks * a.S * a.NP;
+  if (a.S <= kMaxScanSeqs) {
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, true>),
+                       dim3(persistent_grid<CT, D, BS, true>(items)), dim3(kNW * 64), 0, a.stream,
+                       p);
+  } else {
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, false>),
+                       dim3(persistent_grid<CT, D, BS, false>(items)), dim3(kNW * 64), 0,
+                       a.stream, p);
+  }
   return hipGetLastError();
 }
 

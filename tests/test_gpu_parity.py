@@ -139,3 +139,25 @@ def test_empty_batch_and_zero_lengths():
     torch.cuda.synchronize()
     o = out_f64(out)
     assert np.all(o[0] == 0) and np.all(o[2] == 0) and np.all(np.isfinite(o[1]))
+
+
+def test_workspace_reused_across_calls():
+    """One workspace serves consecutive calls of different shapes: the
+    work-queue counters in its first 256 bytes are zero after every call."""
+    import paged_kv_cache_370_amd as pkv
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    cases = [workloads.make_config(3, reduced=True), workloads.make_config(5, reduced=True),
+             workloads.make_config(4, reduced=True), workloads.make_config(3, reduced=True)]
+    for k, w in enumerate(cases):
+        _say(f"case reuse {k} {w.name}")
+        kc, vc, ks, vs = oracle_caches(w)
+        ref = oracle_decode(w, kc, vc, ks, vs)
+        dw = DeviceWorkload(w)
+        dw.write()
+        for ps in (0, 64):
+            pkv.paged_attention_decode(dw.out, dw.q, dw.kc, dw.vc, dw.tables, dw.lens,
+                                       w.max_context_len, w.scale, dw.ks, dw.vs,
+                                       partition_size=ps, workspace=ws)
+            torch.cuda.synchronize()
+            assert max_err(out_f64(dw.out), ref) <= TOL[w.cache_dtype], (k, ps)
+            assert int(ws[:256].count_nonzero()) == 0, (k, ps)
