@@ -640,11 +640,12 @@ hipError_t launch_c(const DecodeArgs& a) {
 
 }  // namespace
 
-// Grouped heads (G >= 2) with bf16 queries run here; one head per KV head
-// keeps the vector-ALU kernel, which needs fewer registers for the same bytes.
+// Every bf16-query decode runs here, one head per KV head included: the
+// score and P V products cost the same matrix-core issue for 1..16 heads and
+// the kernel stays HBM-bound.  fp32 queries keep the vector-ALU kernel.
 bool decode_mfma_supported(const DecodeArgs& a) {
   return a.q_dtype == PKV_BF16 && (a.cache_dtype == PKV_BF16 || a.cache_dtype == PKV_FP8_E4M3) &&
-         a.H / a.H_kv >= 2 && (a.P + a.bs - 1) / a.bs <= kMaxTable;
+         (a.P + a.bs - 1) / a.bs <= kMaxTable;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a) {
