@@ -119,3 +119,58 @@ def test_fp8_error_bound():
     # half an E4M3 ulp: 2^-4 relative in the normal range, 2^-10 absolute below 2^-6
     bound = np.where(y >= 2.0 ** -6, y * 2.0 ** -4, 2.0 ** -10) * (1 + 2.0 ** -20) * s
     assert np.all(np.abs(deq - x) <= bound)
+
+
+# ------------------------------------------------- planted mistakes are caught
+
+def _mutant_write(old, new):
+    """A copy of the oracle's write with one line of its source changed."""
+    import importlib.util
+    import types
+    import oracle.cache_write as cw
+    src = open(cw.__file__).read()
+    assert old in src, old
+    mod = types.ModuleType("mutant_cache_write")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new), cw.__file__, "exec"), mod.__dict__)
+    return mod.paged_kv_cache_write
+
+
+def _round_trip_pin(write):
+    w = workloads.make_config(2, reduced=True)
+    key, value, slots = w.writes[0]
+    nk, _ = write(key, value, w.key_cache, w.value_cache, slots, w.block_size)
+    for t, s in enumerate(slots):
+        if not np.array_equal(nk[s // w.block_size, :, s % w.block_size, :].view(np.uint8),
+                              key[t].view(np.uint8)):
+            return False
+    return True
+
+
+def _scale_pin(write):
+    rng, src, kc, ks = _fp8_setup()
+    slots = (4 * 16 + np.arange(16)).astype(np.int32)
+    _, _, nks, _ = write(src[:16], src[:16], kc, kc.copy(), slots, 16, ks, ks.copy())
+    amax = torch.from_numpy(_bf16_to_f32(src[:16])).abs().amax(dim=(0, 2))
+    scale = torch.clamp(amax / torch.tensor(448.0), min=torch.finfo(torch.float32).tiny)
+    return np.array_equal(nks[4], scale.numpy())
+
+
+def _append_pin(write):
+    rng, src, kc, ks = _fp8_setup(seed=1, T=20)
+    nk, _, nks, _ = write(src[:10], src[:10], kc, kc, (2 * 16 + np.arange(10)).astype(np.int32),
+                          16, ks, ks)
+    _, _, nks2, _ = write(src[10:12], src[10:12], nk, nk,
+                          (2 * 16 + np.array([10, 11])).astype(np.int32), 16, nks, nks)
+    return np.array_equal(nks2, nks, equal_nan=True)
+
+
+@pytest.mark.parametrize("old,new,pin", [
+    ("off = s % block_size", "off = (s + 1) % block_size", _round_trip_pin),
+    ("np.maximum(amax / np.float32(FP8_MAX), _FLT_MIN)",
+     "np.maximum(amax / np.float32(FP8_MAX - 1), _FLT_MIN)", _scale_pin),
+    ("fresh[blk[off == 0]] = True", "fresh[blk] = True", _append_pin),
+])
+def test_planted_mistakes_are_caught(old, new, pin):
+    assert pin(paged_kv_cache_write)
+    assert not pin(_mutant_write(old, new))
