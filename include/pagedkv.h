@@ -136,8 +136,8 @@ size_t paged_kv_cache_write_workspace_size(
  *   longer than one partition are split, each partition is attended on its
  *   own, and a second kernel merges the partial results.
  *   workspace: at least paged_attention_decode_workspace_size(...) bytes
- *   (always >= 256).  Its first 256 bytes are work-queue counters: they must
- *   be zero before the first call that uses the workspace (allocate it
+ *   (always >= 4096).  Its first 4096 bytes are work-queue counters: they
+ *   must be zero before the first call that uses the workspace (allocate it
  *   zero-filled) and every call leaves them zero again; the rest may hold
  *   anything.  Calls that may run at the same time must not share a
  *   workspace.

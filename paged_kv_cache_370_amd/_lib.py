@@ -161,7 +161,7 @@ def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
     _, H_kv, bs, _ = key_cache.shape
     qc, cc = dtype_code(query), dtype_code(key_cache)
     if workspace is None:
-        # zero-filled: the first 256 bytes are the library's work-queue counters
+        # zero-filled: the first 4 KiB are the library's work-queue counters
         need = decode_workspace_size(S, H, H_kv, D, bs, max_context_len, qc, cc, partition_size)
         workspace = torch.zeros(need, dtype=torch.uint8, device=query.device) if need else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

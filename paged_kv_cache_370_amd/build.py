@@ -33,6 +33,9 @@ FLAGS = [
     # MFMA accumulators in VGPRs: the online softmax rescales them with
     # vector ALU ops every chunk, and AGPRs would need copies both ways
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # single-lane atomics (work-queue claims) are not worth a wave-wide
+    # expansion, whose result read-back forces a wait on all pending loads
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

@@ -49,9 +49,10 @@ pkv_status_t check_decode_shape(int S, int H, int H_kv, int D, int bs, int max_c
   return PKV_OK;
 }
 
-// Workspace: a 256-byte header of work-queue counters, then the split
-// partials (m, l, acc) when a context can span more than one partition.
-constexpr size_t kSchedBytes = 256;
+// Workspace: a 4 KiB header of work-queue counters (16 counters, 256 bytes
+// apart), then the split partials (m, l, acc) when a context can span more
+// than one partition.
+constexpr size_t kSchedBytes = 4096;
 
 size_t decode_workspace(int S, int H, int D, int max_ctx, int P) {
   const int np = num_partitions(max_ctx, P);

@@ -19,7 +19,9 @@
 // as the fastest item index each XCD's L2 then serves a fixed set of KV
 // heads (blocks shared between sequences come from HBM once per XCD).  The
 // last workgroup of a queue to finish resets its counters to zero for the
-// next call.
+// next call.  Items are software-pipelined: while one item streams, the next
+// item's block ids and Q are fetched and the item after it is claimed, and
+// each wave issues the next item's first chunk before the merge.
 //
 // Why MFMA: the query heads that share a KV head turn both products into
 // small dense contractions, [16 tokens x D] . [D x 16 heads] for the scores
@@ -60,9 +62,13 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kMaxTable = 256;      // block-table entries one partition may span
-constexpr int kMaxScanSeqs = 1024;  // sequences whose offsets a workgroup keeps in LDS
+constexpr int kMaxScanSeqs = 512;  // sequences whose offsets a workgroup keeps in LDS
 constexpr int kNW = 4;              // waves per workgroup
 constexpr int kNT = 2;              // 16-token tiles per pipeline step
+constexpr int kWaitVmcnt0 = 0x0F70; // s_waitcnt vmcnt(0), other counters untouched (gfx9)
+// Work-queue counters sit 256 bytes apart: device-scope atomics are resolved
+// beyond the per-XCD L2s, and counters sharing a line would serialise there.
+constexpr int kCounterStride = 64;
 
 struct MfmaParams {
   const void* q;
@@ -76,7 +82,8 @@ struct MfmaParams {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
-  int* sched;  // [0..7] next item per queue, [8..15] finished workgroups per queue
+  int* sched;  // claim counter of queue x at [x * kCounterStride], finished-workgroup
+               // counter at [(8 + x) * kCounterStride]
   int S, H, H_kv, G, chunks, max_blocks, P, NP;
   float scale_log2;
 };
@@ -396,18 +403,98 @@ __device__ __forceinline__ int find_seq(const int* s_off, int S, int rest) {
   return lo;
 }
 
+// Decoded work item: its partition and whether it exists (without the
+// sequence scan, items past a sequence's end are placeholders).
+struct Item {
+  bool live;
+  int part, n;
+  Part w;
+};
+
+template <int BS, bool SCAN>
+__device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y, const int* s_off,
+                                            const int* s_len) {
+  Item it;
+  const int y = item % Y;
+  const int rest = item / Y;
+  int seq;
+  if constexpr (SCAN) {
+    seq = find_seq(s_off, p.S, rest);
+    it.part = rest - s_off[seq];
+    it.n = s_len[seq];
+    it.live = true;
+  } else {
+    seq = rest / p.NP;
+    it.part = rest - seq * p.NP;
+    it.n = p.lens[seq];
+    it.live = it.part == 0 || it.part * p.P < it.n;
+  }
+  it.w.seq = seq;
+  it.w.kvh = y / p.chunks;
+  const int hc = y - it.w.kvh * p.chunks;
+  it.w.h0 = it.w.kvh * p.G + hc * 16;
+  it.w.nh = min(16, p.G - hc * 16);
+  it.w.start = it.part * p.P;
+  it.w.end = min(it.n, it.w.start + p.P);
+  it.w.first_blk = it.w.start / BS;
+  return it;
+}
+
+// Block ids and Q operand fragments of an item, one of each per thread,
+// held in registers by fetch_meta and written to LDS by store_meta (thread
+// t owns table entry t and Q fragment element t).  Plain loads: the
+// compiler tracks them exactly, so they never force a wait on the chunk
+// pipeline.  Entries past the item's blocks repeat the table's last entry
+// and are never read; heads past the group are zeros.
+struct Meta {
+  int tab;
+  uint4 qf;
+  bool q_live;
+};
+
+template <typename CT, int D>
+__device__ __forceinline__ Meta fetch_meta(const MfmaParams& p, const Part& w, int tid) {
+  using Gm = Geometry<CT, D>;
+  Meta mt;
+  const int blk = min(w.first_blk + tid, p.max_blocks - 1);
+  mt.tab = p.tables[(size_t)w.seq * p.max_blocks + blk];
+  // fragment c = tid / 64 for lane l = (q, r) = tid % 64; threads past the
+  // fragments load a clamped one they never store (no branch, no early wait)
+  const int i = min(tid, Gm::NKC * 64 - 1);
+  const int c = i >> 6, l = i & 63;
+  const int hq = l & 15;
+  mt.qf = *reinterpret_cast<const uint4*>(
+      reinterpret_cast<const uint16_t*>(p.q) +
+      ((size_t)w.seq * p.H + w.h0 + min(hq, w.nh - 1)) * D + Gm::DQ * (l >> 4) + 8 * c);
+  mt.q_live = hq < w.nh;
+  return mt;
+}
+
+template <typename CT, int D>
+__device__ __forceinline__ void store_meta(const Meta& mt, int* tab, uint4* qf, int tid) {
+  tab[tid] = mt.tab;
+  if (tid < Geometry<CT, D>::NKC * 64) {
+    const uint4 v = mt.qf;
+    const bool z = mt.q_live;
+    qf[tid] = make_uint4(z ? v.x : 0u, z ? v.y : 0u, z ? v.z : 0u, z ? v.w : 0u);
+  }
+}
+
 template <typename CT, int D, int BS, bool SCAN>
 __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   using Gm = Geometry<CT, D>;
+  static_assert(kMaxTable == kNW * 64, "one table entry per thread");
+  static_assert(Gm::NKC <= kNW, "one Q fragment row per wave");
   constexpr int VTILE = Gm::CHUNK * Gm::VS;  // bf16 elements per wave
   constexpr int MERGE = kNW * 16 * D;   // fp32 partial outputs
   constexpr int UNION_BYTES = (VTILE * kNW * 2 > MERGE * 4) ? VTILE * kNW * 2 : MERGE * 4;
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[UNION_BYTES];
-  __shared__ int s_tab[kMaxTable];
+  __shared__ int s_tab[2][kMaxTable];
+  __shared__ uint4 s_qf[2][Gm::NKC * 64];
   __shared__ float s_m[kNW][16];
   __shared__ float s_l[kNW][16];
   __shared__ int s_red[kNW];
-  __shared__ uint4 s_qf[Gm::NKC * 64];
+  __shared__ int s_next[2];
   __shared__ int s_off[SCAN ? kMaxScanSeqs + 1 : 1];
   __shared__ int s_len[SCAN ? kMaxScanSeqs : 1];
 
@@ -417,65 +504,59 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   const int q = lane >> 4, r = lane & 15;
   const int Y = p.H_kv * p.chunks;
 
-  int total;
-  if constexpr (SCAN) total = Y * build_offsets(p, s_off, s_len, s_red);
-  else total = Y * p.S * p.NP;
-
-  __shared__ int s_item;
+  // Queue `queue` holds items k * nq + queue.  Its first 2 * queue_wgs items
+  // are taken statically (workgroup b starts with items b and
+  // (queue_wgs + b / nq) * nq + queue, so the launch makes no atomic traffic);
+  // claim c of the queue's counter is item (2 * queue_wgs + c) * nq + queue.
+  // Each claim is made two items ahead, so its latency is hidden.
   const int nq = min(8, (int)gridDim.x);
   const int queue = blockIdx.x % nq;
   const int queue_wgs = ((int)gridDim.x - queue + nq - 1) / nq;
-  while (true) {
-    if (tid == 0) s_item = atomicAdd(&p.sched[queue], 1) * nq + queue;
+  int* claim_ctr = p.sched + queue * kCounterStride;
+  int* done_ctr = p.sched + (8 + queue) * kCounterStride;
+  if (tid == 0) {
+    s_next[0] = blockIdx.x;
+    s_next[1] = (queue_wgs + (int)blockIdx.x / nq) * nq + queue;
+  }
+  int total;
+  if constexpr (SCAN) total = Y * build_offsets(p, s_off, s_len, s_red);  // has barriers
+  else {
+    total = Y * p.S * p.NP;
     __syncthreads();
-    const int item = s_item;  // read by every thread before the item's barriers
-    if (item >= total) break;
-    const int y = item % Y;
-    const int rest = item / Y;
-    int seq, part, n;
-    if constexpr (SCAN) {
-      seq = find_seq(s_off, p.S, rest);
-      part = rest - s_off[seq];
-      n = s_len[seq];
-    } else {
-      seq = rest / p.NP;
-      part = rest - seq * p.NP;
-      n = p.lens[seq];
-      if (part > 0 && part * p.P >= n) {  // uniform over the workgroup
-        __syncthreads();  // s_item is rewritten only after every thread read it
-        continue;
-      }
-    }
-    Part w;
-    w.seq = seq;
-    w.kvh = y / p.chunks;
-    const int hc = y - w.kvh * p.chunks;
-    w.h0 = w.kvh * p.G + hc * 16;
-    w.nh = min(16, p.G - hc * 16);
-    w.start = part * p.P;
-    w.end = min(n, w.start + p.P);
-    w.first_blk = w.start / BS;
-    w.s_tab = s_tab;
+  }
+  int cur = s_next[0];
+  int nxt = s_next[1];
+  int buf = 0;
+  Item it = decode_item<BS, SCAN>(p, min(cur, total - 1), Y, s_off, s_len);
+  if (cur < total) store_meta<CT, D>(fetch_meta<CT, D>(p, it.w, tid), s_tab[0], s_qf[0], tid);
+  __syncthreads();
 
-    // Block ids of this partition, fetched once (the previous item's readers
-    // of s_tab finished before its merge barrier).
-    const int nblk = w.end > w.start ? (w.end - 1) / BS - w.first_blk + 1 : 0;
-    const int32_t* trow = p.tables + (size_t)seq * p.max_blocks + w.first_blk;
-    for (int i = tid; i < nblk; i += kNW * 64) s_tab[i] = trow[i];
-
-    // Q operand fragments -> LDS: s_qf[c][l] for lane l = (q, r) holds head
-    // r, elements (D/4) q + 8 c .. + 8 (zeros for heads past the group).
-    for (int i = tid; i < Gm::NKC * 64; i += kNW * 64) {
-      const int c = i >> 6, l = i & 63;
-      const int hq = l & 15;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (hq < w.nh)
-        v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) +
-                                            ((size_t)seq * p.H + w.h0 + hq) * D +
-                                            Gm::DQ * (l >> 4) + 8 * c);
-      s_qf[i] = v;
+  KStage<CT, D> ks;
+  VStage<CT, D> vs;
+  // First chunk of the first item (a wave without a chunk loads a clamped
+  // one it never uses).
+  it.w.s_tab = s_tab[0];
+  if (cur < total && it.live) {
+    const int nch = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
+    const int c0 = it.w.start + min(wave, max(nch - 1, 0)) * Gm::CHUNK;
+    if (nch > 0) {
+      load_v<CT, D, BS>(vs, p, it.w, c0, lane);
+      load_k<CT, D, BS>(ks, p, it.w, c0, lane);
     }
-    __syncthreads();
+  }
+
+  while (cur < total) {
+    // Prefetch the next item's block ids and Q into the other buffers, and
+    // claim the item after it.  Nothing reads those buffers until the next
+    // item.
+    Item nx = decode_item<BS, SCAN>(p, min(nxt, total - 1), Y, s_off, s_len);
+    const Meta meta_next = fetch_meta<CT, D>(p, nx.w, tid);
+    // The claim's result is used only after barrier X, where nothing else is
+    // in flight, so waiting for it there costs nothing.
+    // (Only thread 0 sets and reads it: initialising it in the other lanes
+    // would make the compiler wait for every pending load first.)
+    int claim;
+    if (tid == 0) claim = atomicAdd(claim_ctr, 1);
 
     f32x4_t acc[Gm::NMD];
 #pragma unroll
@@ -483,25 +564,23 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     float m = kNegInf, lsum = 0.f;
 
     uint16_t* s_v = reinterpret_cast<uint16_t*>(s_raw) + wave * VTILE;
-    const int nch = (w.end - w.start + Gm::CHUNK - 1) / Gm::CHUNK;
+    const uint4* qf_cur = s_qf[buf];
+    const int nch = it.live ? (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK : 0;
     int ci = wave;
     if (ci < nch) {
-      KStage<CT, D> ks;
-      VStage<CT, D> vs;
-      load_v<CT, D, BS>(vs, p, w, w.start + ci * Gm::CHUNK, lane);
-      load_k<CT, D, BS>(ks, p, w, w.start + ci * Gm::CHUNK, lane);
+      // The first chunk's loads were issued before this item began.
       while (true) {
-        const int c0 = w.start + ci * Gm::CHUNK;
+        const int c0 = it.w.start + ci * Gm::CHUNK;
         // The next chunk index is clamped so that every load is
         // unconditional (a redundant last prefetch hits the cache).
-        const int cn = w.start + min(ci + kNW, nch - 1) * Gm::CHUNK;
-        store_v<CT, D>(vs, c0, w.end, s_v, lane);
-        load_v<CT, D, BS>(vs, p, w, cn, lane);
+        const int cn = it.w.start + min(ci + kNW, nch - 1) * Gm::CHUNK;
+        store_v<CT, D>(vs, c0, it.w.end, s_v, lane);
+        load_v<CT, D, BS>(vs, p, it.w, cn, lane);
         // Keep the scheduler from sinking the prefetch below the products:
         // the loads must be in flight while this chunk is computed.
         __builtin_amdgcn_sched_barrier(0);
         f32x4_t sc[kNT];
-        scores<CT, D>(ks, s_qf, sc, lane);
+        scores<CT, D>(ks, qf_cur, sc, lane);
         float fk[kNT], fv[kNT];
 #pragma unroll
         for (int T = 0; T < kNT; ++T) {
@@ -512,9 +591,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
             fv[T] = ks.vsc[T];
           }
         }
-        load_k<CT, D, BS>(ks, p, w, cn, lane);
+        load_k<CT, D, BS>(ks, p, it.w, cn, lane);
         __builtin_amdgcn_sched_barrier(0);
-        softmax_pv<D>(sc, fk, fv, Gm::ELEM == 1, c0, w.end, s_v, acc, m, lsum, lane);
+        softmax_pv<D>(sc, fk, fv, Gm::ELEM == 1, c0, it.w.end, s_v, acc, m, lsum, lane);
         ci += kNW;
         if (ci >= nch) break;
       }
@@ -526,8 +605,28 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
 
+    if (nxt < total) store_meta<CT, D>(meta_next, s_tab[buf ^ 1], s_qf[buf ^ 1], tid);
+    // Nothing useful is in flight here.  An explicit vmcnt(0) (which the
+    // compiler accounts for, unlike inline asm) clears its conservative view
+    // of pending loads, so the merge below does not wait for the next
+    // item's chunk loads issued after the barrier.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();  // X: V tiles, s_tab[buf], s_qf[buf] are free; s_*[buf^1] are complete
+    if (tid == 0) s_next[0] = (2 * queue_wgs + claim) * nq + queue;
+
+    // Issue the next item's first chunk now, so that its loads are in flight
+    // during the merge below.
+    nx.w.s_tab = s_tab[buf ^ 1];
+    if (nxt < total && nx.live) {
+      const int nch_n = (nx.w.end - nx.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
+      if (nch_n > 0) {
+        const int c0 = nx.w.start + min(wave, nch_n - 1) * Gm::CHUNK;
+        load_v<CT, D, BS>(vs, p, nx.w, c0, lane);
+        load_k<CT, D, BS>(ks, p, nx.w, c0, lane);
+      }
+    }
+
     // Merge the wave-level softmax states of this partition.
-    __syncthreads();  // every wave is done with its V tile (s_raw is reused)
     float* s_acc = reinterpret_cast<float*>(s_raw);
     if (q == 0) {
       s_m[wave][r] = m;
@@ -537,43 +636,52 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     for (int md = 0; md < Gm::NMD; ++md)
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + r) * D + 16 * md + 4 * q + i] = acc[md][i];
-    __syncthreads();
+    __syncthreads();  // Y
 
-    const bool single = n <= p.P;
-    for (int idx = tid; idx < w.nh * D; idx += kNW * 64) {
-      const int g = idx / D;
-      const int d = idx - g * D;
-      float M = kNegInf;
+    if (it.live) {
+      const bool single = it.n <= p.P;
+      for (int idx = tid; idx < it.w.nh * D; idx += kNW * 64) {
+        const int g = idx / D;
+        const int d = idx - g * D;
+        float M = kNegInf;
 #pragma unroll
-      for (int k = 0; k < kNW; ++k) M = fmaxf(M, s_m[k][g]);
-      float L = 0.f, O = 0.f;
-      if (M != kNegInf) {
+        for (int k = 0; k < kNW; ++k) M = fmaxf(M, s_m[k][g]);
+        float L = 0.f, O = 0.f;
+        if (M != kNegInf) {
 #pragma unroll
-        for (int k = 0; k < kNW; ++k) {
-          const float wt = __builtin_amdgcn_exp2f(s_m[k][g] - M);
-          L = fmaf(s_l[k][g], wt, L);
-          O = fmaf(s_acc[(k * 16 + g) * D + d], wt, O);
+          for (int k = 0; k < kNW; ++k) {
+            const float wt = __builtin_amdgcn_exp2f(s_m[k][g] - M);
+            L = fmaf(s_l[k][g], wt, L);
+            O = fmaf(s_acc[(k * 16 + g) * D + d], wt, O);
+          }
         }
-      }
-      const int h = w.h0 + g;
-      if (single) {
-        const float o = L > 0.f ? O / L : 0.f;
-        reinterpret_cast<uint16_t*>(p.out)[((size_t)seq * p.H + h) * D + d] = f32_to_bf16(o);
-      } else {
-        const size_t pi = ((size_t)seq * p.H + h) * p.NP + part;
-        p.ws_acc[pi * D + d] = O;
-        if (d == 0) {
-          p.ws_m[pi] = M;
-          p.ws_l[pi] = L;
+        const int h = it.w.h0 + g;
+        if (single) {
+          const float o = L > 0.f ? O / L : 0.f;
+          reinterpret_cast<uint16_t*>(p.out)[((size_t)it.w.seq * p.H + h) * D + d] =
+              f32_to_bf16(o);
+        } else {
+          const size_t pi = ((size_t)it.w.seq * p.H + h) * p.NP + it.part;
+          p.ws_acc[pi * D + d] = O;
+          if (d == 0) {
+            p.ws_m[pi] = M;
+            p.ws_l[pi] = L;
+          }
         }
       }
     }
-    // s_m / s_l / s_raw are rewritten only after the next item's first barrier.
+    const int nn = s_next[0];
+    __syncthreads();  // Z: merge reads of s_raw / s_m / s_l and s_next done
+
+    cur = nxt;
+    nxt = nn;
+    it = nx;
+    buf ^= 1;
   }
   // The last workgroup of this queue to finish returns its counters to zero.
-  if (tid == 0 && atomicAdd(&p.sched[8 + queue], 1) == queue_wgs - 1) {
-    atomicExch(&p.sched[queue], 0);
-    atomicExch(&p.sched[8 + queue], 0);
+  if (tid == 0 && atomicAdd(done_ctr, 1) == queue_wgs - 1) {
+    atomicExch(claim_ctr, 0);
+    atomicExch(done_ctr, 0);
   }
 }
 

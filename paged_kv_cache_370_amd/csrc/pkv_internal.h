@@ -37,8 +37,8 @@ struct DecodeArgs {
   int q_dtype, cache_dtype;
   int P;   // partition size in tokens (multiple of bs)
   int NP;  // partitions per sequence the grid covers: ceil(max_ctx / P)
-  int* sched;     // [16] work-queue counters (8 next-item, 8 finished-workgroup),
-                  // zero between calls
+  int* sched;     // work-queue counters (4 KiB header of the workspace), zero
+                  // between calls
   float* ws_m;    // [S][H][NP]  running max (base-2 units) per partition
   float* ws_l;    // [S][H][NP]  running sum per partition
   float* ws_acc;  // [S][H][NP][D]  unnormalised output per partition

@@ -45,13 +45,13 @@ def test_status_strings_and_version():
 
 
 def test_partition_and_workspace_queries():
-    # context fits one partition: only the 256-byte work-queue header
+    # context fits one partition: only the 4 KiB work-queue header
     assert pkv.decode_partition_size(4, 8, 8, 128, 16, 300, 1, 1, 0) == 304
-    assert pkv.decode_workspace_size(4, 8, 8, 128, 16, 300, 1, 1, 0) == 256
+    assert pkv.decode_workspace_size(4, 8, 8, 128, 16, 300, 1, 1, 0) == 4096
     # long contexts: 512-token partitions, partials for m, l and acc
     assert pkv.decode_partition_size(8, 64, 8, 128, 8, 32768, 1, 1, 512) == 512
     rows = 8 * 64 * 64
-    expect = 256 + 2 * ((rows * 4 + 255) // 256 * 256) + (rows * 128 * 4 + 255) // 256 * 256
+    expect = 4096 + 2 * ((rows * 4 + 255) // 256 * 256) + (rows * 128 * 4 + 255) // 256 * 256
     assert pkv.decode_workspace_size(8, 64, 8, 128, 8, 32768, 1, 1, 512) == expect
     # partition not a multiple of the block size, bad head size, bad dtype pair
     assert pkv.decode_partition_size(8, 64, 8, 128, 16, 32768, 1, 1, 40) < 0
@@ -89,7 +89,7 @@ def test_decode_argument_checks():
     assert _decode(max_ctx=128, max_blocks=8, ps=16) == 4   # needs workspace
     assert _decode(max_ctx=128, ps=16, ws=FAKE, wsb=10) == 4
     assert _decode(ws=None, wsb=0) == 4               # the counter header is always needed
-    assert _decode(ws=FAKE, wsb=255) == 4
+    assert _decode(ws=FAKE, wsb=4095) == 4
 
 
 def _write(**kw):
