@@ -349,55 +349,83 @@ __device__ __forceinline__ void softmax_pv(const f32x4_t (&s)[kNT], const float 
   }
 }
 
-// s_off[i] = number of items (partitions) of sequences 0..i-1 (a sequence of
-// length 0 still has one, which writes zeros); s_len[i] = its length.
-// Returns s_off[S].  Every thread of the workgroup calls it.
-__device__ int build_offsets(const MfmaParams& p, int* s_off, int* s_len, int* s_red) {
-  constexpr int NTH = kNW * 64;
-  const int tid = threadIdx.x;
-  const int per = (p.S + NTH - 1) / NTH;
-  const int base = tid * per;
-  int local = 0;
-  for (int k = 0; k < per; ++k) {
-    const int i = base + k;
-    if (i < p.S) {
-      const int n = p.lens[i];
-      s_len[i] = n;
-      local += max(1, (n + p.P - 1) / p.P);
-    }
-  }
-  int x = local;  // inclusive scan over the workgroup
-  const int lane = tid & 63, wave = tid >> 6;
+// Exclusive scan over the workgroup of one value per thread; returns the
+// thread's exclusive prefix, and the total in *total.  Every thread calls it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_red, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(x, off);
     if (lane >= off) x += y;
   }
+  __syncthreads();  // s_red may still be read by a previous scan
   if (lane == 63) s_red[wave] = x;
   __syncthreads();
-  for (int w = 0; w < wave; ++w) x += s_red[w];
-  int excl = x - local;
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) {
+    if (w < wave) x += s_red[w];
+    t += s_red[w];
+  }
+  *total = t;
+  return x - v;
+}
+
+// Item order of the sequence scan: first every full partition (P tokens) of
+// every sequence, then every sequence's last, shorter partition (a sequence
+// of length 0 has one empty item, which writes zeros).  Short items thus run
+// last, which keeps the end of the kernel balanced across workgroups.
+//   s_full[i]: full partitions of sequences 0..i-1   (s_full[S] = F)
+//   s_rag[i]:  short partitions of sequences 0..i-1  (s_rag[S] = R)
+//   s_len[i]:  context length of sequence i
+// Returns F (and R in *n_rag).  Every thread of the workgroup calls it.
+__device__ int build_offsets(const MfmaParams& p, int* s_full, uint16_t* s_rag, int* s_len,
+                             int* s_red, int* n_rag) {
+  constexpr int NTH = kNW * 64;
+  const int tid = threadIdx.x;
+  const int per = (p.S + NTH - 1) / NTH;
+  const int base = tid * per;
+  int nf = 0, nr = 0;
   for (int k = 0; k < per; ++k) {
     const int i = base + k;
     if (i < p.S) {
-      s_off[i] = excl;
-      excl += max(1, (s_len[i] + p.P - 1) / p.P);
+      const int n = p.lens[i];
+      s_len[i] = n;
+      nf += n / p.P;
+      nr += (n % p.P != 0 || n == 0) ? 1 : 0;
     }
   }
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < kNW; ++w) total += s_red[w];
-  if (tid == 0) s_off[p.S] = total;
+  int F, R;
+  int ef = block_exclusive_scan(nf, s_red, &F);
+  int er = block_exclusive_scan(nr, s_red, &R);
+  for (int k = 0; k < per; ++k) {
+    const int i = base + k;
+    if (i < p.S) {
+      const int n = s_len[i];
+      s_full[i] = ef;
+      s_rag[i] = (uint16_t)er;
+      ef += n / p.P;
+      er += (n % p.P != 0 || n == 0) ? 1 : 0;
+    }
+  }
+  if (tid == 0) {
+    s_full[p.S] = F;
+    s_rag[p.S] = (uint16_t)R;
+  }
   __syncthreads();
-  return total;
+  *n_rag = R;
+  return F;
 }
 
-// Largest i with s_off[i] <= rest (offsets strictly increase).
-__device__ __forceinline__ int find_seq(const int* s_off, int S, int rest) {
-  int lo = 0, hi = S;  // s_off[lo] <= rest < s_off[hi]
+// Largest i in [0, S) with off[i] <= rest, for non-decreasing off with
+// off[0] <= rest < off[S].
+template <typename T>
+__device__ __forceinline__ int find_seq(const T* off, int S, int rest) {
+  int lo = 0, hi = S;  // off[lo] <= rest < off[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (s_off[mid] <= rest) lo = mid;
+    if ((int)off[mid] <= rest) lo = mid;
     else hi = mid;
   }
   return lo;
@@ -412,16 +440,24 @@ struct Item {
 };
 
 template <int BS, bool SCAN>
-__device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y, const int* s_off,
+__device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y, int n_full,
+                                            const int* s_full, const uint16_t* s_rag,
                                             const int* s_len) {
   Item it;
   const int y = item % Y;
   const int rest = item / Y;
   int seq;
   if constexpr (SCAN) {
-    seq = find_seq(s_off, p.S, rest);
-    it.part = rest - s_off[seq];
-    it.n = s_len[seq];
+    // Values read from LDS are per-lane to the compiler; the item is uniform
+    // over the workgroup, so move them to scalar registers.
+    if (rest < n_full) {
+      seq = __builtin_amdgcn_readfirstlane(find_seq(s_full, p.S, rest));
+      it.part = rest - __builtin_amdgcn_readfirstlane(s_full[seq]);
+    } else {
+      seq = __builtin_amdgcn_readfirstlane(find_seq(s_rag, p.S, rest - n_full));
+      it.part = __builtin_amdgcn_readfirstlane(s_len[seq]) / p.P;
+    }
+    it.n = __builtin_amdgcn_readfirstlane(s_len[seq]);
     it.live = true;
   } else {
     seq = rest / p.NP;
@@ -495,7 +531,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   __shared__ float s_l[kNW][16];
   __shared__ int s_red[kNW];
   __shared__ int s_next[2];
-  __shared__ int s_off[SCAN ? kMaxScanSeqs + 1 : 1];
+  __shared__ int s_full[SCAN ? kMaxScanSeqs + 1 : 1];
+  __shared__ uint16_t s_rag[SCAN ? kMaxScanSeqs + 1 : 1];
   __shared__ int s_len[SCAN ? kMaxScanSeqs : 1];
 
   const int tid = threadIdx.x;
@@ -518,16 +555,19 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     s_next[0] = blockIdx.x;
     s_next[1] = (queue_wgs + (int)blockIdx.x / nq) * nq + queue;
   }
-  int total;
-  if constexpr (SCAN) total = Y * build_offsets(p, s_off, s_len, s_red);  // has barriers
-  else {
+  int total, n_full = 0;
+  if constexpr (SCAN) {
+    int n_rag;
+    n_full = build_offsets(p, s_full, s_rag, s_len, s_red, &n_rag);  // has barriers
+    total = Y * (n_full + n_rag);
+  } else {
     total = Y * p.S * p.NP;
     __syncthreads();
   }
   int cur = s_next[0];
   int nxt = s_next[1];
   int buf = 0;
-  Item it = decode_item<BS, SCAN>(p, min(cur, total - 1), Y, s_off, s_len);
+  Item it = decode_item<BS, SCAN>(p, min(cur, total - 1), Y, n_full, s_full, s_rag, s_len);
   if (cur < total) store_meta<CT, D>(fetch_meta<CT, D>(p, it.w, tid), s_tab[0], s_qf[0], tid);
   __syncthreads();
 
@@ -549,7 +589,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     // Prefetch the next item's block ids and Q into the other buffers, and
     // claim the item after it.  Nothing reads those buffers until the next
     // item.
-    Item nx = decode_item<BS, SCAN>(p, min(nxt, total - 1), Y, s_off, s_len);
+    Item nx = decode_item<BS, SCAN>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len);
     const Meta meta_next = fetch_meta<CT, D>(p, nx.w, tid);
     // The claim's result is used only after barrier X, where nothing else is
     // in flight, so waiting for it there costs nothing.
