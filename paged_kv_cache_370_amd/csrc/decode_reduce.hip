@@ -5,98 +5,87 @@
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p acc_p / sum_p w_p l_p.
 // (Whole-context softmax: dpshk.com PagedAttention article, section 2.2.)
 //
-// One workgroup of D threads per (sequence, query head): the threads first
-// reduce M and L over the partitions together (weights kept in LDS), then
-// thread d sums w_p acc_p[d] with several independent loads in flight.
+// One workgroup of D threads per (sequence, query head); thread d merges
+// acc_p[d] over the partitions in batches with an online maximum, all in
+// registers.  The first batch's loads do not wait for the context length:
+// they are clamped to the NP partition rows the workspace holds for every
+// sequence, so they are in flight together with the load of the length.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
 
-constexpr int kCachedWeights = 2048;  // partitions whose weight is kept in LDS
+constexpr int kFirst = 4;   // partitions loaded before the context length is known
+constexpr int kChunk = 16;  // partitions per later batch of independent loads
 
-template <int NWAVE>
-__device__ __forceinline__ float block_max(float x, float* s_red) {
-  x = wave_max(x);
-  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  float r = s_red[0];
+// Fold partitions [q0, q0 + U) (those below np) into the running (M, L, O).
+template <int U>
+__device__ __forceinline__ void merge_chunk(const float (&m)[U], const float (&l)[U],
+                                            const float (&a)[U], int q0, int np, float& M,
+                                            float& L, float& O) {
+  float mc = kNegInf;
 #pragma unroll
-  for (int w = 1; w < NWAVE; ++w) r = fmaxf(r, s_red[w]);
-  __syncthreads();
-  return r;
-}
-
-template <int NWAVE>
-__device__ __forceinline__ float block_sum(float x, float* s_red) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  float r = 0.f;
+  for (int u = 0; u < U; ++u)
+    if (q0 + u < np) mc = fmaxf(mc, m[u]);
+  const float mn = fmaxf(M, mc);  // finite: every partition below np holds tokens
+  const float r = __builtin_amdgcn_exp2f(M - mn);  // 0 while M is still -inf
+  L *= r;
+  O *= r;
 #pragma unroll
-  for (int w = 0; w < NWAVE; ++w) r += s_red[w];
-  __syncthreads();
-  return r;
+  for (int u = 0; u < U; ++u) {
+    if (q0 + u < np) {
+      const float w = __builtin_amdgcn_exp2f(m[u] - mn);
+      L = fmaf(l[u], w, L);
+      O = fmaf(a[u], w, O);
+    }
+  }
+  M = mn;
 }
 
 template <bool OUT_BF16, int D>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(
     void* __restrict__ out, const int32_t* __restrict__ lens, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const float* __restrict__ ws_acc, int H, int P, int NP) {
-  constexpr int NWAVE = D / 64;
-  __shared__ float s_w[kCachedWeights];
-  __shared__ float s_red[NWAVE];
+  constexpr int U0 = kFirst, U = kChunk;
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
-  const int n = lens[seq];
-  const int np = (n + P - 1) / P;
-  if (np <= 1) return;  // written directly by the partition kernel
   const int d = threadIdx.x;
   const size_t base = ((size_t)seq * H + h) * NP;
   const float* pm = ws_m + base;
   const float* pl = ws_l + base;
   const float* pa = ws_acc + base * D + d;
 
-  float M = kNegInf;
-  for (int q = d; q < np; q += D) M = fmaxf(M, pm[q]);
-  M = block_max<NWAVE>(M, s_red);
-  float L = 0.f;
-  for (int q = d; q < np; q += D) {
-    const float w = __builtin_amdgcn_exp2f(pm[q] - M);
-    if (q < kCachedWeights) s_w[q] = w;
-    L = fmaf(pl[q], w, L);
+  float m0[U0], l0[U0], a0[U0];
+#pragma unroll
+  for (int u = 0; u < U0; ++u) a0[u] = pa[(size_t)min(u, NP - 1) * D];
+  // Keep the scheduler from putting these vector loads behind the waits for
+  // the scalar loads below.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < U0; ++u) {
+    const int q = min(u, NP - 1);
+    m0[u] = pm[q];
+    l0[u] = pl[q];
   }
-  L = block_sum<NWAVE>(L, s_red);  // its barrier also publishes s_w
-
-  constexpr int U = 8;
-  float o[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) o[u] = 0.f;
-  int q = 0;
-  for (; q + U <= np; q += U) {
-    float a[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) a[u] = pa[(size_t)(q + u) * D];
+  const int n = lens[seq];
+  const int np = (n + P - 1) / P;  // one partition: written by the partition kernel
+  float M = kNegInf, L = 0.f, O = 0.f;
+  merge_chunk<U0>(m0, l0, a0, 0, np, M, L, O);
+  for (int q0 = U0; q0 < np; q0 += U) {
+    float m[U], l[U], a[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int qq = q + u;
-      const float w = qq < kCachedWeights ? s_w[qq] : __builtin_amdgcn_exp2f(pm[qq] - M);
-      o[u] = fmaf(a[u], w, o[u]);
+      const int q = min(q0 + u, np - 1);
+      m[u] = pm[q];
+      l[u] = pl[q];
+      a[u] = pa[(size_t)q * D];
     }
+    merge_chunk<U>(m, l, a, q0, np, M, L, O);
   }
-  for (; q < np; ++q) {
-    const float w = q < kCachedWeights ? s_w[q] : __builtin_amdgcn_exp2f(pm[q] - M);
-    o[0] = fmaf(pa[(size_t)q * D], w, o[0]);
-  }
-  float O = 0.f;
-#pragma unroll
-  for (int u = 0; u < U; ++u) O += o[u];
+  // No branch before this point, so the first chunk's loads are issued
+  // before the length arrives.
+  if (np <= 1) return;
   const float res = O / L;
   const size_t oi = ((size_t)seq * H + h) * D + d;
   if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16(res);

@@ -12,23 +12,27 @@
 namespace pkv {
 namespace {
 
-// One workgroup per token: both K and V rows of every KV head, 16 bytes per
-// lane.  Row bytes (D * elem) are 128..512, a multiple of 16.
+// One 16-byte vector per thread: a token's K and V rows (every KV head,
+// 2 * H_kv * row_vec vectors; row bytes D * elem are 128..512, a multiple of
+// 16) span wpt workgroups, so each thread makes one dependent load (its
+// token's slot, uniform over the workgroup) before its copy.  The grid
+// strides over (token, piece) pairs when there are more than it holds.
 __global__ __launch_bounds__(256) void kv_write_copy_kernel(
     const uint4* __restrict__ key, const uint4* __restrict__ value,
     uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
-    const int32_t* __restrict__ slots, int H_kv, int row_vec, int bs) {
-  const int t = blockIdx.x;
-  const int s = slots[t];
-  if (s < 0) return;
-  const int b = s / bs;
-  const int o = s - b * bs;
+    const int32_t* __restrict__ slots, int H_kv, int row_vec, int bs, int wpt, long long pieces) {
   const int per_token = H_kv * row_vec;  // 16-byte vectors per token per K or V
-  for (int i = threadIdx.x; i < 2 * per_token; i += blockDim.x) {
+  for (long long g = blockIdx.x; g < pieces; g += gridDim.x) {
+    const long long t = g / wpt;
+    const int i = (int)(g - t * wpt) * 256 + (int)threadIdx.x;
+    const int s = slots[t];
+    if (s < 0 || i >= 2 * per_token) continue;
     const bool is_v = i >= per_token;
     const int j = is_v ? i - per_token : i;
     const int h = j / row_vec;
     const int v = j - h * row_vec;
+    const int b = s / bs;
+    const int o = s - b * bs;
     const size_t src = (size_t)t * per_token + j;
     const size_t dst = (((size_t)b * H_kv + h) * bs + o) * row_vec + v;
     if (is_v) value_cache[dst] = value[src];
@@ -179,10 +183,13 @@ size_t kv_write_fp8_workspace(int num_blocks, int H_kv) {
 hipError_t launch_kv_write_copy(const WriteArgs& a) {
   const int elem = a.cache_dtype == PKV_F32 ? 4 : 2;
   const int row_vec = a.D * elem / 16;
-  hipLaunchKernelGGL(kv_write_copy_kernel, dim3(a.T), dim3(256), 0, a.stream,
+  const int wpt = (2 * a.H_kv * row_vec + 255) / 256;
+  const long long pieces = (long long)a.T * wpt;
+  const unsigned grid = (unsigned)(pieces < (1LL << 20) ? pieces : (1LL << 20));
+  hipLaunchKernelGGL(kv_write_copy_kernel, dim3(grid), dim3(256), 0, a.stream,
                      reinterpret_cast<const uint4*>(a.key), reinterpret_cast<const uint4*>(a.value),
                      reinterpret_cast<uint4*>(a.key_cache), reinterpret_cast<uint4*>(a.value_cache),
-                     a.slots, a.H_kv, row_vec, a.bs);
+                     a.slots, a.H_kv, row_vec, a.bs, wpt, pieces);
   return hipGetLastError();
 }
 
