@@ -65,10 +65,19 @@ constexpr int kMaxTable = 256;      // block-table entries one partition may spa
 constexpr int kMaxScanSeqs = 512;  // sequences whose offsets a workgroup keeps in LDS
 constexpr int kNW = 4;              // waves per workgroup
 constexpr int kNT = 2;              // 16-token tiles per pipeline step
-constexpr int kWaitVmcnt0 = 0x0F70; // s_waitcnt vmcnt(0), other counters untouched (gfx9)
 // Work-queue counters sit 256 bytes apart: device-scope atomics are resolved
 // beyond the per-XCD L2s, and counters sharing a line would serialise there.
 constexpr int kCounterStride = 64;
+// Initial running maximum: finite, so a step whose tokens are all masked
+// leaves (m, l, acc) unchanged instead of producing 2^(-inf - -inf).  Scores
+// are far above it for any finite input.
+constexpr float kRunMaxInit = -1e30f;
+
+// A step with nothing left to prefetch still issues its loads (branching
+// around them would cost registers and waits); they read row 0 of this
+// array, one cache line shared by every lane, and the values are never used.
+// 256 bytes hold one cache row of D = 128 bf16 elements and one scale.
+__device__ __attribute__((aligned(256))) unsigned char g_dummy_row[256];
 
 struct MfmaParams {
   const void* q;
@@ -145,68 +154,66 @@ struct VStage {
   uint4 v[kNT][Geometry<CT, D>::KV4];  // the chunk's V rows, kNT*KV4 wave loads
 };
 
+// Where a step's loads read from: the caches and FP8 scales, or the dummy row.
+struct Src {
+  const void* k;
+  const void* v;
+  const float* ks;
+  const float* vs;
+};
+
 // One work item's view of its partition.
 struct Part {
   int seq, kvh, h0, nh, start, end, first_blk;
-  const int* s_tab;
 };
 
+// Block ids of a chunk (tokens c0 .. c0 + CHUNK - 1) are CHUNK / BS
+// consecutive entries ctab[0 ..]; a chunk starts on a block boundary.
 template <typename CT, int D, int BS>
-__device__ __forceinline__ size_t token_row(const MfmaParams& p, const Part& w, int t, int lane) {
-  const int phys = w.s_tab[t / BS - w.first_blk];
+__device__ __forceinline__ size_t token_row(const MfmaParams& p, const Part& w, const int* ctab,
+                                            int c0, int t, int lane) {
+  const int phys = ctab[(t - c0) / BS];
   return (((size_t)phys * p.H_kv + w.kvh) * BS + (t % BS)) * D + Geometry<CT, D>::DQ * (lane >> 4);
-}
-
-template <typename CT, int D>
-__device__ __forceinline__ void keep_live(const VStage<CT, D>& vs, const KStage<CT, D>& ks) {
-#pragma unroll
-  for (int T = 0; T < kNT; ++T)
-#pragma unroll
-    for (int i = 0; i < Geometry<CT, D>::KV4; ++i) {
-      asm volatile("" ::"v"(vs.v[T][i].x), "v"(vs.v[T][i].y), "v"(vs.v[T][i].z),
-                   "v"(vs.v[T][i].w));
-      asm volatile("" ::"v"(ks.k[T][i].x), "v"(ks.k[T][i].y), "v"(ks.k[T][i].z),
-                   "v"(ks.k[T][i].w));
-    }
 }
 
 // V rows are fetched whole: wave load j covers rows j*RPI .. of the chunk,
 // lane l the 16-byte piece l % PR of row j*RPI + l / PR, so every load
 // instruction reads whole token rows (fully used cache lines).
 template <typename CT, int D, int BS>
-__device__ __forceinline__ void load_v(VStage<CT, D>& st, const MfmaParams& p, const Part& w,
-                                       int c0, int lane) {
+__device__ __forceinline__ void load_v(VStage<CT, D>& st, const MfmaParams& p, const Src& src,
+                                       const Part& w, const int* ctab, int c0, int lane) {
   using CS = typename CT::storage;
   using Gm = Geometry<CT, D>;
   constexpr int PR = Gm::PR, RPI = Gm::RPI;
-  const CS* vc = reinterpret_cast<const CS*>(p.vc);
+  const CS* vc = reinterpret_cast<const CS*>(src.v);
   uint4* flat = &st.v[0][0];
 #pragma unroll
   for (int j = 0; j < kNT * Gm::KV4; ++j) {
     const int t = min(c0 + j * RPI + lane / PR, w.end - 1);  // clamped: masked later
-    const int phys = w.s_tab[t / BS - w.first_blk];
+    const int phys = ctab[(t - c0) / BS];
     const size_t row = ((size_t)phys * p.H_kv + w.kvh) * BS + (t % BS);
     flat[j] = reinterpret_cast<const uint4*>(vc + row * D)[lane % PR];
   }
 }
 
 template <typename CT, int D, int BS>
-__device__ __forceinline__ void load_k(KStage<CT, D>& st, const MfmaParams& p, const Part& w,
-                                       int c0, int lane) {
+__device__ __forceinline__ void load_k(KStage<CT, D>& st, const MfmaParams& p, const Src& src,
+                                       const Part& w, const int* ctab, int c0, int lane) {
   using CS = typename CT::storage;
-  const CS* kc = reinterpret_cast<const CS*>(p.kc);
+  const CS* kc = reinterpret_cast<const CS*>(src.k);
 #pragma unroll
   for (int T = 0; T < kNT; ++T) {
     const int t = min(c0 + 16 * T + (lane & 15), w.end - 1);  // clamped: masked later
-    const uint4* src = reinterpret_cast<const uint4*>(kc + token_row<CT, D, BS>(p, w, t, lane));
+    const uint4* krow =
+        reinterpret_cast<const uint4*>(kc + token_row<CT, D, BS>(p, w, ctab, c0, t, lane));
 #pragma unroll
-    for (int i = 0; i < Geometry<CT, D>::KV4; ++i) st.k[T][i] = src[i];
+    for (int i = 0; i < Geometry<CT, D>::KV4; ++i) st.k[T][i] = krow[i];
     if constexpr (Geometry<CT, D>::ELEM == 1) {
       // the lane's scores are tokens 16T + 4q + i: one block for every bs >= 4
       const int ts = min(c0 + 16 * T + 4 * (lane >> 4), w.end - 1);
-      const size_t si = (size_t)w.s_tab[ts / BS - w.first_blk] * p.H_kv + w.kvh;
-      st.ksc[T] = p.ks[si];
-      st.vsc[T] = p.vs[si];
+      const size_t si = (size_t)ctab[(ts - c0) / BS] * p.H_kv + w.kvh;
+      st.ksc[T] = src.ks[si];
+      st.vsc[T] = src.vs[si];
     }
   }
 }
@@ -476,42 +483,45 @@ __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y
   return it;
 }
 
-// Block ids and Q operand fragments of an item, one of each per thread,
-// held in registers by fetch_meta and written to LDS by store_meta (thread
-// t owns table entry t and Q fragment element t).  Plain loads: the
-// compiler tracks them exactly, so they never force a wait on the chunk
-// pipeline.  Entries past the item's blocks repeat the table's last entry
-// and are never read; heads past the group are zeros.
-struct Meta {
-  int tab;
-  uint4 qf;
-  bool q_live;
-};
+// Block ids of an item, one slice per wave: wave w processes chunks
+// w, w + NW, w + 2 NW, .. of the item, and lane l of the wave holds the id of
+// block l % EPC of its chunk number l / EPC (EPC = CHUNK / BS blocks per
+// chunk; 64 entries cover the kMaxTable blocks an item may span).  Each wave
+// writes and reads only its own slice in LDS, so no workgroup barrier guards
+// it.  Entries past the item's blocks repeat the table's last entry and are
+// never read.  Plain loads: the compiler tracks them exactly, so they never
+// force a wait on the chunk pipeline.
+template <typename CT, int D, int BS>
+__device__ __forceinline__ int fetch_tab(const MfmaParams& p, const Part& w, int wave, int lane) {
+  constexpr int EPC = Geometry<CT, D>::CHUNK / BS;
+  const int blk = w.first_blk + (wave + kNW * (lane / EPC)) * EPC + lane % EPC;
+  return p.tables[(size_t)w.seq * p.max_blocks + min(blk, p.max_blocks - 1)];
+}
 
+__device__ __forceinline__ void store_tab(int tab, int* wtab, int lane) {
+  wtab[lane] = tab;
+  wave_lds_sync();  // the slice is visible to every lane of the wave
+}
+
+// Q operand fragments of an item, one element per thread (thread t owns
+// element t), shared by the waves; heads past the group are zeros.
 template <typename CT, int D>
-__device__ __forceinline__ Meta fetch_meta(const MfmaParams& p, const Part& w, int tid) {
+__device__ __forceinline__ uint4 fetch_q(const MfmaParams& p, const Part& w, int tid) {
   using Gm = Geometry<CT, D>;
-  Meta mt;
-  const int blk = min(w.first_blk + tid, p.max_blocks - 1);
-  mt.tab = p.tables[(size_t)w.seq * p.max_blocks + blk];
   // fragment c = tid / 64 for lane l = (q, r) = tid % 64; threads past the
   // fragments load a clamped one they never store (no branch, no early wait)
   const int i = min(tid, Gm::NKC * 64 - 1);
   const int c = i >> 6, l = i & 63;
   const int hq = l & 15;
-  mt.qf = *reinterpret_cast<const uint4*>(
+  return *reinterpret_cast<const uint4*>(
       reinterpret_cast<const uint16_t*>(p.q) +
       ((size_t)w.seq * p.H + w.h0 + min(hq, w.nh - 1)) * D + Gm::DQ * (l >> 4) + 8 * c);
-  mt.q_live = hq < w.nh;
-  return mt;
 }
 
 template <typename CT, int D>
-__device__ __forceinline__ void store_meta(const Meta& mt, int* tab, uint4* qf, int tid) {
-  tab[tid] = mt.tab;
+__device__ __forceinline__ void store_q(uint4 v, const Part& w, uint4* qf, int tid) {
   if (tid < Geometry<CT, D>::NKC * 64) {
-    const uint4 v = mt.qf;
-    const bool z = mt.q_live;
+    const bool z = (tid & 15) < w.nh;  // head (tid % 64) % 16 of fragment tid / 64
     qf[tid] = make_uint4(z ? v.x : 0u, z ? v.y : 0u, z ? v.z : 0u, z ? v.w : 0u);
   }
 }
@@ -525,18 +535,19 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   constexpr int MERGE = kNW * 16 * D;   // fp32 partial outputs
   constexpr int UNION_BYTES = (VTILE * kNW * 2 > MERGE * 4) ? VTILE * kNW * 2 : MERGE * 4;
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[UNION_BYTES];
-  __shared__ int s_tab[2][kMaxTable];
+  __shared__ int s_wtab[2][kNW][kMaxTable / kNW];
   __shared__ uint4 s_qf[2][Gm::NKC * 64];
   __shared__ float s_m[kNW][16];
   __shared__ float s_l[kNW][16];
   __shared__ int s_red[kNW];
   __shared__ int s_next[2];
+  __shared__ int s_zero[4];  // block id 0 for the dummy row
   __shared__ int s_full[SCAN ? kMaxScanSeqs + 1 : 1];
   __shared__ uint16_t s_rag[SCAN ? kMaxScanSeqs + 1 : 1];
   __shared__ int s_len[SCAN ? kMaxScanSeqs : 1];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps selects scalar
   const int lane = tid & 63;
   const int q = lane >> 4, r = lane & 15;
   const int Y = p.H_kv * p.chunks;
@@ -555,6 +566,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     s_next[0] = blockIdx.x;
     s_next[1] = (queue_wgs + (int)blockIdx.x / nq) * nq + queue;
   }
+  if (tid < 4) s_zero[tid] = 0;
   int total, n_full = 0;
   if constexpr (SCAN) {
     int n_rag;
@@ -567,104 +579,114 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   int cur = s_next[0];
   int nxt = s_next[1];
   int buf = 0;
+  constexpr int EPC = Gm::CHUNK / BS;  // block ids per chunk
   Item it = decode_item<BS, SCAN>(p, min(cur, total - 1), Y, n_full, s_full, s_rag, s_len);
-  if (cur < total) store_meta<CT, D>(fetch_meta<CT, D>(p, it.w, tid), s_tab[0], s_qf[0], tid);
+  if (cur < total) {
+    store_tab(fetch_tab<CT, D, BS>(p, it.w, wave, lane), s_wtab[0][wave], lane);
+    store_q<CT, D>(fetch_q<CT, D>(p, it.w, tid), it.w, s_qf[0], tid);
+  }
+  // The second item's block ids travel in a register until the first
+  // item's last chunk (each item's are fetched one item ahead).
+  int tab_next = fetch_tab<CT, D, BS>(
+      p, decode_item<BS, SCAN>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len).w, wave,
+      lane);
   __syncthreads();
+
+  const Src cache{p.kc, p.vc, p.ks, p.vs};
+  const Src dummy{g_dummy_row, g_dummy_row, reinterpret_cast<const float*>(g_dummy_row),
+                  reinterpret_cast<const float*>(g_dummy_row)};
+  Part dummy_part{};  // token 0 of block 0, KV head 0: row 0 of the dummy
+  dummy_part.end = 1;
 
   KStage<CT, D> ks;
   VStage<CT, D> vs;
-  // First chunk of the first item (a wave without a chunk loads a clamped
-  // one it never uses).
-  it.w.s_tab = s_tab[0];
+  // First chunk of the first item (a wave without one computes a masked
+  // step on whatever its registers hold).
   if (cur < total && it.live) {
-    const int nch = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
-    const int c0 = it.w.start + min(wave, max(nch - 1, 0)) * Gm::CHUNK;
-    if (nch > 0) {
-      load_v<CT, D, BS>(vs, p, it.w, c0, lane);
-      load_k<CT, D, BS>(ks, p, it.w, c0, lane);
+    const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
+    if (nvalid > wave) {
+      const int c0 = it.w.start + wave * Gm::CHUNK;
+      load_v<CT, D, BS>(vs, p, cache, it.w, s_wtab[0][wave], c0, lane);
+      load_k<CT, D, BS>(ks, p, cache, it.w, s_wtab[0][wave], c0, lane);
     }
   }
 
   while (cur < total) {
-    // Prefetch the next item's block ids and Q into the other buffers, and
-    // claim the item after it.  Nothing reads those buffers until the next
-    // item.
-    Item nx = decode_item<BS, SCAN>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len);
-    const Meta meta_next = fetch_meta<CT, D>(p, nx.w, tid);
-    // The claim's result is used only after barrier X, where nothing else is
-    // in flight, so waiting for it there costs nothing.
-    // (Only thread 0 sets and reads it: initialising it in the other lanes
-    // would make the compiler wait for every pending load first.)
+    // The next item's block ids go to the slice buffer the previous item
+    // used.  Stored first: waiting for them also waits for this item's
+    // first chunk, which the first step needs next, and for nothing issued
+    // later (inside the loop the wait would be placed on every step).
+    int* wt_nxt = s_wtab[buf ^ 1][wave];
+    store_tab(tab_next, wt_nxt, lane);
+    // Prefetch the next item's Q and claim the item after it.  Nothing reads
+    // the other buffers until the next item.
+    const Item nx = decode_item<BS, SCAN>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len);
+    const uint4 q_next = fetch_q<CT, D>(p, nx.w, tid);
+    // The claim's result is used only after barrier X.  (Only thread 0 sets
+    // and reads it: initialising it in the other lanes would make the
+    // compiler wait for every pending load first.)
     int claim;
     if (tid == 0) claim = atomicAdd(claim_ctr, 1);
 
     f32x4_t acc[Gm::NMD];
 #pragma unroll
     for (int md = 0; md < Gm::NMD; ++md) acc[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m = kNegInf, lsum = 0.f;
+    float m = kRunMaxInit, lsum = 0.f;
 
     uint16_t* s_v = reinterpret_cast<uint16_t*>(s_raw) + wave * VTILE;
     const uint4* qf_cur = s_qf[buf];
-    const int nch = it.live ? (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK : 0;
+    const bool more = nxt < total;
+    const int nvalid = it.live ? (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK : 0;
+    const int nvalid_n = more && nx.live ? (nx.w.end - nx.w.start + Gm::CHUNK - 1) / Gm::CHUNK : 0;
+    // After its last chunk of this item a wave streams its first chunk of
+    // the next item, so the next item's data arrives during the merge.  A
+    // wave with no chunk of this item runs one fully masked step, which
+    // leaves its state at (kRunMaxInit, 0, 0), so that every wave reaches
+    // the loads below.
+    const bool next_mine = nvalid_n > wave;
+    const int* ctab = s_wtab[buf][wave];  // this chunk's block ids
     int ci = wave;
-    if (ci < nch) {
-      // The first chunk's loads were issued before this item began.
-      while (true) {
-        const int c0 = it.w.start + ci * Gm::CHUNK;
-        // The next chunk index is clamped so that every load is
-        // unconditional (a redundant last prefetch hits the cache).
-        const int cn = it.w.start + min(ci + kNW, nch - 1) * Gm::CHUNK;
-        store_v<CT, D>(vs, c0, it.w.end, s_v, lane);
-        load_v<CT, D, BS>(vs, p, it.w, cn, lane);
-        // Keep the scheduler from sinking the prefetch below the products:
-        // the loads must be in flight while this chunk is computed.
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4_t sc[kNT];
-        scores<CT, D>(ks, qf_cur, sc, lane);
-        float fk[kNT], fv[kNT];
+    do {
+      const int c0 = it.w.start + ci * Gm::CHUNK;
+      const bool last = ci + kNW >= nvalid;
+      // Where the prefetch goes: this wave's next chunk of the item, else
+      // its first chunk of the next item, else the dummy row (scalar
+      // selects, no branch).
+      const bool to_next = last && next_mine;
+      const bool idle = last && !next_mine;
+      const Src src = idle ? dummy : cache;
+      const Part lw = to_next ? nx.w : (idle ? dummy_part : it.w);
+      const int* ntab = to_next ? wt_nxt : (idle ? s_zero : ctab + EPC);
+      const int cn = to_next ? nx.w.start + wave * Gm::CHUNK : (idle ? 0 : c0 + kNW * Gm::CHUNK);
+      store_v<CT, D>(vs, c0, it.w.end, s_v, lane);
+      load_v<CT, D, BS>(vs, p, src, lw, ntab, cn, lane);
+      // Keep the scheduler from sinking the prefetch below the products:
+      // the loads must be in flight while this chunk is computed.
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4_t sc[kNT];
+      scores<CT, D>(ks, qf_cur, sc, lane);
+      float fk[kNT], fv[kNT];
 #pragma unroll
-        for (int T = 0; T < kNT; ++T) {
-          fk[T] = p.scale_log2;
-          fv[T] = 1.f;
-          if constexpr (Gm::ELEM == 1) {
-            fk[T] *= ks.ksc[T];
-            fv[T] = ks.vsc[T];
-          }
+      for (int T = 0; T < kNT; ++T) {
+        fk[T] = p.scale_log2;
+        fv[T] = 1.f;
+        if constexpr (Gm::ELEM == 1) {
+          fk[T] *= ks.ksc[T];
+          fv[T] = ks.vsc[T];
         }
-        load_k<CT, D, BS>(ks, p, it.w, cn, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        softmax_pv<D>(sc, fk, fv, Gm::ELEM == 1, c0, it.w.end, s_v, acc, m, lsum, lane);
-        ci += kNW;
-        if (ci >= nch) break;
       }
-      // The last prefetch is dead on the exit path; this use keeps the
-      // compiler from sinking the prefetch loads into the next iteration,
-      // which would serialise every load with its use.
-      keep_live(vs, ks);
-    }
+      load_k<CT, D, BS>(ks, p, src, lw, ntab, cn, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_pv<D>(sc, fk, fv, Gm::ELEM == 1, c0, it.w.end, s_v, acc, m, lsum, lane);
+      ci += kNW;
+      ctab += EPC;
+    } while (ci < nvalid);
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
 
-    if (nxt < total) store_meta<CT, D>(meta_next, s_tab[buf ^ 1], s_qf[buf ^ 1], tid);
-    // Nothing useful is in flight here.  An explicit vmcnt(0) (which the
-    // compiler accounts for, unlike inline asm) clears its conservative view
-    // of pending loads, so the merge below does not wait for the next
-    // item's chunk loads issued after the barrier.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();  // X: V tiles, s_tab[buf], s_qf[buf] are free; s_*[buf^1] are complete
+    if (more) store_q<CT, D>(q_next, nx.w, s_qf[buf ^ 1], tid);
+    __syncthreads();  // X: V tiles and s_qf[buf] are free; s_qf[buf^1] is complete
     if (tid == 0) s_next[0] = (2 * queue_wgs + claim) * nq + queue;
-
-    // Issue the next item's first chunk now, so that its loads are in flight
-    // during the merge below.
-    nx.w.s_tab = s_tab[buf ^ 1];
-    if (nxt < total && nx.live) {
-      const int nch_n = (nx.w.end - nx.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
-      if (nch_n > 0) {
-        const int c0 = nx.w.start + min(wave, nch_n - 1) * Gm::CHUNK;
-        load_v<CT, D, BS>(vs, p, nx.w, c0, lane);
-        load_k<CT, D, BS>(ks, p, nx.w, c0, lane);
-      }
-    }
 
     // Merge the wave-level softmax states of this partition.
     float* s_acc = reinterpret_cast<float*>(s_raw);
@@ -678,22 +700,29 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + r) * D + 16 * md + 4 * q + i] = acc[md][i];
     __syncthreads();  // Y
 
+    // The item after the next one is known now: fetch its block ids, which
+    // are stored during the next item's last chunk.
+    const int nn = __builtin_amdgcn_readfirstlane(s_next[0]);
+    tab_next = fetch_tab<CT, D, BS>(
+        p, decode_item<BS, SCAN>(p, min(nn, total - 1), Y, n_full, s_full, s_rag, s_len).w, wave,
+        lane);
+
     if (it.live) {
       const bool single = it.n <= p.P;
       for (int idx = tid; idx < it.w.nh * D; idx += kNW * 64) {
         const int g = idx / D;
         const int d = idx - g * D;
-        float M = kNegInf;
+        // Every wave's m is finite (at least kRunMaxInit); waves without
+        // tokens carry l = 0 and acc = 0 and get weight 0 or add nothing.
+        float M = kRunMaxInit;
 #pragma unroll
         for (int k = 0; k < kNW; ++k) M = fmaxf(M, s_m[k][g]);
         float L = 0.f, O = 0.f;
-        if (M != kNegInf) {
 #pragma unroll
-          for (int k = 0; k < kNW; ++k) {
-            const float wt = __builtin_amdgcn_exp2f(s_m[k][g] - M);
-            L = fmaf(s_l[k][g], wt, L);
-            O = fmaf(s_acc[(k * 16 + g) * D + d], wt, O);
-          }
+        for (int k = 0; k < kNW; ++k) {
+          const float wt = __builtin_amdgcn_exp2f(s_m[k][g] - M);
+          L = fmaf(s_l[k][g], wt, L);
+          O = fmaf(s_acc[(k * 16 + g) * D + d], wt, O);
         }
         const int h = it.w.h0 + g;
         if (single) {
@@ -710,7 +739,6 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
         }
       }
     }
-    const int nn = s_next[0];
     __syncthreads();  // Z: merge reads of s_raw / s_m / s_l and s_next done
 
     cur = nxt;
