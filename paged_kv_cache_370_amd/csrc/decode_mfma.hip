@@ -707,9 +707,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
         p, decode_item<BS, SCAN>(p, min(nn, total - 1), Y, n_full, s_full, s_rag, s_len).w, wave,
         lane);
 
+    // Thread t merges 4 consecutive d of one head: one 16-byte LDS read per
+    // wave state and one 16-byte (8-byte for bf16) store, so few stores
+    // are left for the next item's first wait to drain.
     if (it.live) {
       const bool single = it.n <= p.P;
-      for (int idx = tid; idx < it.w.nh * D; idx += kNW * 64) {
+      for (int idx = tid * 4; idx < it.w.nh * D; idx += kNW * 64 * 4) {
         const int g = idx / D;
         const int d = idx - g * D;
         // Every wave's m is finite (at least kRunMaxInit); waves without
@@ -717,21 +720,30 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
         float M = kRunMaxInit;
 #pragma unroll
         for (int k = 0; k < kNW; ++k) M = fmaxf(M, s_m[k][g]);
-        float L = 0.f, O = 0.f;
+        float L = 0.f;
+        float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int k = 0; k < kNW; ++k) {
           const float wt = __builtin_amdgcn_exp2f(s_m[k][g] - M);
           L = fmaf(s_l[k][g], wt, L);
-          O = fmaf(s_acc[(k * 16 + g) * D + d], wt, O);
+          const float4 a = *reinterpret_cast<const float4*>(&s_acc[(k * 16 + g) * D + d]);
+          O.x = fmaf(a.x, wt, O.x);
+          O.y = fmaf(a.y, wt, O.y);
+          O.z = fmaf(a.z, wt, O.z);
+          O.w = fmaf(a.w, wt, O.w);
         }
-        const int h = it.w.h0 + g;
+        const size_t row = (size_t)it.w.seq * p.H + it.w.h0 + g;
         if (single) {
-          const float o = L > 0.f ? O / L : 0.f;
-          reinterpret_cast<uint16_t*>(p.out)[((size_t)it.w.seq * p.H + h) * D + d] =
-              f32_to_bf16(o);
+          const bool ok = L > 0.f;
+          const float ox = ok ? O.x / L : 0.f, oy = ok ? O.y / L : 0.f;
+          const float oz = ok ? O.z / L : 0.f, ow = ok ? O.w / L : 0.f;
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * D + d) =
+              make_uint2(pack_bf16x2(ox, oy), pack_bf16x2(oz, ow));
         } else {
-          const size_t pi = ((size_t)it.w.seq * p.H + h) * p.NP + it.part;
-          p.ws_acc[pi * D + d] = O;
+          const size_t pi = row * p.NP + it.part;
+          // Streaming store: the reduce kernel reads the partial once.
+          const f32x4_t o4 = {O.x, O.y, O.z, O.w};
+          __builtin_nontemporal_store(o4, reinterpret_cast<f32x4_t*>(p.ws_acc + pi * D + d));
           if (d == 0) {
             p.ws_m[pi] = M;
             p.ws_l[pi] = L;
