@@ -600,8 +600,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
 
   KStage<CT, D> ks;
   VStage<CT, D> vs;
-  // First chunk of the first item (a wave without one computes a masked
-  // step on whatever its registers hold).
+  // A wave without a chunk of its first item runs a masked step on
+  // whatever its registers hold: selects turn those scores into -inf and V
+  // rows into zeros, but the FP8 V scale multiplies p = 0, so it must not be
+  // left uninitialised (0 * NaN = NaN).
+#pragma unroll
+  for (int T = 0; T < kNT; ++T) ks.ksc[T] = ks.vsc[T] = 0.f;
+  // First chunk of the first item.
   if (cur < total && it.live) {
     const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
     if (nvalid > wave) {
