@@ -201,6 +201,45 @@ pkv_status_t paged_attention_decode_reduce(
     void* workspace, size_t workspace_bytes,
     void* stream);
 
+/*
+ * paged_kv_block_copy -- copy whole blocks from one pool to another: the
+ * copy-on-write of a shared block before a sequence writes into it (page
+ * "vLLM的诞生背景：大模型推理的痛点与PagedAttention的破局", the limitations
+ * paragraph: shared blocks need reference counts and copy-on-write), and
+ * swapping blocks out to host memory and back in (page "PagedAttention 与连续
+ * 批处理：LLM Serving 的底层架构拆解", section "PagedAttention：把显存做成虚拟内存":
+ * inactive sequences' pages move to CPU memory and return when needed;
+ * dpshk.com article, section 3.2: host-device copies run on a stream).
+ *
+ * For pair i, block block_pairs[2i] of the source pool is copied to block
+ * block_pairs[2i+1] of the destination pool: the K and V tiles of every KV
+ * head and, for FP8 pools, the block's K and V scales.  Both pools have the
+ * layout above ([num_blocks][H_kv][bs][D], scales [num_blocks][H_kv]) and
+ * the same dtype; they may be one pool (copy-on-write) or two (swap).
+ *
+ *   Pool pointers may be device memory or pinned host memory the device can
+ *   address (hipHostMalloc, torch pin_memory): device -> host is a swap-out,
+ *   host -> device a swap-in.  block_pairs is int32 [num_pairs][2] in memory
+ *   the device can read.
+ *   Destination blocks must be distinct, and when the pools are the same no
+ *   destination may also be a source; then the result does not depend on
+ *   the order of the copies.  Block ids must lie inside their pools (the
+ *   caller's contract, not checked on the device).
+ *   key_scale / value_scale pointers are used only for FP8 pools (may be
+ *   NULL otherwise).
+ *   num_pairs == 0 returns PKV_OK after the size and dtype checks without
+ *   inspecting any pointer.
+ */
+pkv_status_t paged_kv_block_copy(
+    const void* src_key_cache, const void* src_value_cache,
+    const float* src_key_scale, const float* src_value_scale,
+    void* dst_key_cache, void* dst_value_cache,
+    float* dst_key_scale, float* dst_value_scale,
+    const int32_t* block_pairs, int32_t num_pairs,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t cache_dtype,
+    void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* pkv_status_string(int32_t status);
 

@@ -17,7 +17,9 @@ computes, written from the three web pages on PagedAttention:
   a block table);
 * page "PagedAttention 与连续批处理：LLM Serving 的底层架构拆解", section
   "PagedAttention：把显存做成虚拟内存" (attention finds each page through the
-  page table).
+  page table; pages swapped to CPU memory and back);
+* copy-on-write of shared blocks: page "vLLM的诞生背景…", limitations
+  paragraph (``block_copy``).
 
 Floating point is evaluated in float64, except where a reading fixes float32
 (the FP8 scale and the division before encoding; see ``cache_write``).
@@ -34,6 +36,7 @@ Every function here has an independent pin in ``tests/test_oracle_*.py``
 
 from .fp8_e4m3 import fp8_decode, fp8_encode, FP8_MAX, fp8_finite_values
 from .cache_write import paged_kv_cache_write
+from .block_copy import paged_kv_block_copy
 from .attention import (
     paged_attention_decode,
     paged_attention_decode_one,
@@ -47,6 +50,7 @@ __all__ = [
     "FP8_MAX",
     "fp8_finite_values",
     "paged_kv_cache_write",
+    "paged_kv_block_copy",
     "paged_attention_decode",
     "paged_attention_decode_one",
     "gather_sequence",

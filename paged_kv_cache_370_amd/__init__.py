@@ -18,6 +18,7 @@ from ._lib import (
     paged_attention_decode,
     paged_attention_decode_partitions,
     paged_attention_decode_reduce,
+    paged_kv_block_copy,
     paged_kv_cache_write,
     status_string,
     write_workspace_size,
@@ -28,6 +29,7 @@ __all__ = [
     "PKV_BF16", "PKV_F32", "PKV_FP8_E4M3", "PagedKVError", "BlockManager", "OutOfBlocks",
     "decode_partition_size", "decode_workspace_size", "dtype_code", "load",
     "paged_attention_decode", "paged_attention_decode_partitions",
-    "paged_attention_decode_reduce", "paged_kv_cache_write", "status_string",
+    "paged_attention_decode_reduce", "paged_kv_block_copy", "paged_kv_cache_write",
+    "status_string",
     "write_workspace_size",
 ]

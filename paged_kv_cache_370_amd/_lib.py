@@ -25,6 +25,7 @@ EXPORTS = (
     "paged_attention_decode_workspace_size",
     "paged_attention_decode_partitions",
     "paged_attention_decode_reduce",
+    "paged_kv_block_copy",
     "pkv_status_string",
     "pkv_version",
 )
@@ -68,6 +69,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode_partition_size.argtypes = geo
     lib.paged_attention_decode_workspace_size.restype = sz
     lib.paged_attention_decode_workspace_size.argtypes = geo
+    lib.paged_kv_block_copy.restype = i32
+    lib.paged_kv_block_copy.argtypes = [vp] * 9 + [i32] * 5 + [vp]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [i32]
     lib.pkv_version.restype = i32
@@ -202,3 +205,31 @@ def paged_attention_decode_reduce(out, context_lens, num_kv_heads, block_size, m
                                               int(partition_size), _ptr(workspace), wbytes,
                                               _stream(stream))
     _check(st, "paged_attention_decode_reduce")
+
+
+# -------------------------------------------------------------- block copy
+
+def paged_kv_block_copy(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache,
+                        block_pairs, src_key_scale=None, src_value_scale=None,
+                        dst_key_scale=None, dst_value_scale=None, stream=None):
+    """Copy block block_pairs[i, 0] of the source pool to block block_pairs[i, 1]
+    of the destination pool (K, V and, for FP8 pools, their scales).
+
+    Pools are [num_blocks][H_kv][bs][D] tensors of one dtype, on the device or
+    in pinned host memory (torch pin_memory=True); block_pairs is int32
+    [n][2] on the device (or pinned).  Copy-on-write passes one pool twice;
+    swapping out / in passes a device and a pinned host pool.
+    """
+    _contig(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache, block_pairs,
+            src_key_scale, src_value_scale, dst_key_scale, dst_value_scale)
+    if src_key_cache.dtype != dst_key_cache.dtype or src_key_cache.shape[1:] != dst_key_cache.shape[1:]:
+        raise ValueError("source and destination pools differ in dtype or block shape")
+    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be int32 [n][2]")
+    _, H_kv, bs, D = src_key_cache.shape
+    st = load().paged_kv_block_copy(
+        _ptr(src_key_cache), _ptr(src_value_cache), _ptr(src_key_scale), _ptr(src_value_scale),
+        _ptr(dst_key_cache), _ptr(dst_value_cache), _ptr(dst_key_scale), _ptr(dst_value_scale),
+        _ptr(block_pairs), block_pairs.shape[0], H_kv, D, bs, dtype_code(src_key_cache),
+        _stream(stream))
+    _check(st, "paged_kv_block_copy")

@@ -12,11 +12,19 @@ What it follows:
   做成虚拟内存");
 * sharing a block bumps its reference count and puts the same physical block
   in the other table (section 2.3); a block returns to the free list when its
-  count drops to zero.  Only whole blocks are shared, so a shared prefix must
-  end on a block boundary (page "PagedAttention 与连续批处理…", advice section).
+  count drops to zero.  Only whole blocks are shared between requests, so a
+  shared prefix must end on a block boundary (page "PagedAttention 与连续批处
+  理…", advice section); a forked sequence (beam search, section 2.3) shares
+  its parent's last, partial block too;
+* writing into a shared block first copies it to a private block (copy-on-
+  write; page "vLLM的诞生背景…", limitations paragraph), and a sequence's
+  blocks can be swapped out to a host pool and back (page "PagedAttention 与
+  连续批处理…", section "PagedAttention：把显存做成虚拟内存").  The manager only
+  records these copies as (source block, destination block) pairs;
+  paged_kv_block_copy moves the bytes.
 """
 
-from typing import Dict, List
+from typing import Dict, List, Tuple
 
 import numpy as np
 
@@ -35,6 +43,8 @@ class BlockManager:
         self._free: List[int] = list(range(num_blocks - 1, -1, -1))
         self._tables: Dict[int, List[int]] = {}
         self._lens: Dict[int, int] = {}
+        self._copies: List[Tuple[int, int]] = []
+        self._swapped: set = set()  # sequences whose table holds host blocks
 
     # --------------------------------------------------------------- blocks
     @property
@@ -75,11 +85,70 @@ class BlockManager:
         table = self._tables[seq]
         if n % self.block_size == 0:
             table.append(self.allocate())
-        b = table[n // self.block_size]
+        j = n // self.block_size
+        b = table[j]
         if self.ref_count[b] > 1:
-            raise ValueError("appending into a shared block needs copy-on-write")
+            # copy-on-write: the sequence gets a private copy of the block
+            nb = self.allocate()
+            self._copies.append((b, nb))
+            self.ref_count[b] -= 1
+            table[j] = nb
+            b = nb
         self._lens[seq] = n + 1
         return b * self.block_size + n % self.block_size
+
+    def fork(self, src: int, dst: int) -> None:
+        """dst becomes a copy of src sharing every block, the partial last one
+        included; the first write into a shared block copies it."""
+        if dst in self._tables:
+            raise ValueError(f"sequence {dst} exists")
+        self._tables[dst] = []
+        for b in self._tables[src]:
+            self.ref_count[b] += 1
+            self._tables[dst].append(b)
+        self._lens[dst] = self._lens[src]
+
+    def take_copies(self) -> np.ndarray:
+        """Pending copy-on-write pairs as int32 [n][2] (source, destination),
+        to run through paged_kv_block_copy before the write; clears them."""
+        out = np.array(self._copies, dtype=np.int32).reshape(-1, 2)
+        self._copies = []
+        return out
+
+    def swap_out(self, seq: int, host: "BlockManager") -> np.ndarray:
+        """Move seq's blocks to host blocks of the host pool's manager; returns
+        the (device block, host block) pairs to copy before the device blocks
+        are reused.  Only sequences with no shared block can be swapped."""
+        table = self._tables[seq]
+        if any(self.ref_count[b] > 1 for b in table):
+            raise ValueError("a sequence with shared blocks cannot be swapped out")
+        if host.num_free < len(table):
+            raise OutOfBlocks("host pool exhausted")
+        pairs = []
+        for j, b in enumerate(table):
+            hb = host.allocate()
+            pairs.append((b, hb))
+            self.free(b)
+            table[j] = hb
+        self._swapped.add(seq)
+        return np.array(pairs, dtype=np.int32).reshape(-1, 2)
+
+    def swap_in(self, seq: int, host: "BlockManager") -> np.ndarray:
+        """Bring a swapped-out sequence back into device blocks; returns the
+        (host block, device block) pairs to copy."""
+        if seq not in self._swapped:
+            raise ValueError(f"sequence {seq} is not swapped out")
+        table = self._tables[seq]
+        if self.num_free < len(table):
+            raise OutOfBlocks("block pool exhausted")
+        pairs = []
+        for j, hb in enumerate(table):
+            b = self.allocate()
+            pairs.append((hb, b))
+            host.free(hb)
+            table[j] = b
+        self._swapped.discard(seq)
+        return np.array(pairs, dtype=np.int32).reshape(-1, 2)
 
     def share_prefix(self, src: int, dst: int, num_blocks: int) -> None:
         """Give dst the first num_blocks blocks of src (whole, full blocks)."""

@@ -187,6 +187,33 @@ pkv_status_t paged_kv_cache_write(const void* key, const void* value, void* key_
   return hip_status(copy ? launch_kv_write_copy(a) : launch_kv_write_fp8(a));
 }
 
+pkv_status_t paged_kv_block_copy(const void* src_key_cache, const void* src_value_cache,
+                                 const float* src_key_scale, const float* src_value_scale,
+                                 void* dst_key_cache, void* dst_value_cache, float* dst_key_scale,
+                                 float* dst_value_scale, const int32_t* block_pairs,
+                                 int32_t num_pairs, int32_t num_kv_heads, int32_t head_size,
+                                 int32_t block_size, int32_t cache_dtype, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0) return PKV_ERR_SHAPE;
+  if (!valid_d(head_size) || !valid_bs(block_size)) return PKV_ERR_SHAPE;
+  if (cache_dtype != PKV_F32 && cache_dtype != PKV_BF16 && cache_dtype != PKV_FP8_E4M3)
+    return PKV_ERR_DTYPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!src_key_cache || !src_value_cache || !dst_key_cache || !dst_value_cache || !block_pairs)
+    return PKV_ERR_NULL;
+  if (cache_dtype == PKV_FP8_E4M3 &&
+      (!src_key_scale || !src_value_scale || !dst_key_scale || !dst_value_scale))
+    return PKV_ERR_NULL;
+  BlockCopyArgs a;
+  a.src_k = src_key_cache; a.src_v = src_value_cache;
+  a.dst_k = dst_key_cache; a.dst_v = dst_value_cache;
+  a.src_ks = src_key_scale; a.src_vs = src_value_scale;
+  a.dst_ks = dst_key_scale; a.dst_vs = dst_value_scale;
+  a.pairs = block_pairs; a.n = num_pairs; a.H_kv = num_kv_heads; a.D = head_size;
+  a.bs = block_size; a.cache_dtype = cache_dtype;
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(launch_kv_block_copy(a));
+}
+
 int32_t paged_attention_decode_partition_size(int32_t num_seqs, int32_t num_heads,
                                               int32_t num_kv_heads, int32_t head_size,
                                               int32_t block_size, int32_t max_context_len,

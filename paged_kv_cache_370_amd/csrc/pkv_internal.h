@@ -45,6 +45,21 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
+struct BlockCopyArgs {
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const float* src_ks;
+  const float* src_vs;
+  float* dst_ks;
+  float* dst_vs;
+  const int32_t* pairs;  // [n][2] (source block, destination block)
+  int n, H_kv, D, bs, cache_dtype;
+  hipStream_t stream;
+};
+
+hipError_t launch_kv_block_copy(const BlockCopyArgs& a);
 hipError_t launch_kv_write_copy(const WriteArgs& a);
 hipError_t launch_kv_write_fp8(const WriteArgs& a);
 size_t kv_write_fp8_workspace(int num_blocks, int H_kv);

@@ -116,6 +116,28 @@ def test_write_argument_checks():
     assert _write(T=0, D=80) == 2                     # sizes are still checked
 
 
+def _copy(**kw):
+    a = dict(sk=FAKE, sv=FAKE, sks=None, svs=None, dk=FAKE, dv=FAKE, dks=None, dvs=None,
+             pairs=FAKE, n=4, H_kv=2, D=128, bs=16, cd=1)
+    a.update(kw)
+    return pkv.load().paged_kv_block_copy(
+        a["sk"], a["sv"], a["sks"], a["svs"], a["dk"], a["dv"], a["dks"], a["dvs"], a["pairs"],
+        a["n"], a["H_kv"], a["D"], a["bs"], a["cd"], None)
+
+
+def test_block_copy_argument_checks():
+    assert _copy(sk=None) == 1
+    assert _copy(pairs=None) == 1
+    assert _copy(cd=2) == 1                       # FP8 pools need all four scale arrays
+    assert _copy(cd=2, sks=FAKE, svs=FAKE, dks=FAKE) == 1
+    assert _copy(D=96) == 2
+    assert _copy(bs=4) == 2
+    assert _copy(H_kv=0) == 2
+    assert _copy(n=-1) == 2
+    assert _copy(cd=7) == 3
+    assert _copy(n=0, sk=None, sv=None, dk=None, dv=None, pairs=None) == 0
+
+
 def test_empty_decode_batch_needs_no_pointers():
     assert _decode(S=0, out=None, q=None, kc=None, vc=None, tables=None, lens=None) == 0
     assert _decode(S=0, D=96) == 2

@@ -51,8 +51,57 @@ def test_sharing_needs_whole_blocks_and_cow():
     bm.share_prefix(0, 2, 1)
     bm.finish(0)
     bm._lens[1] = 15                            # a partly filled shared block
+    shared = bm.table(1)[0]
+    slot = bm.append_slot(1)                    # copy-on-write, not a write into it
+    (src, dst), = bm.take_copies().tolist()
+    assert src == shared and dst != shared and bm.table(1) == [dst]
+    assert slot == dst * 16 + 15
+    assert bm.ref_count[shared] == 1 and bm.ref_count[dst] == 1
+    assert bm.take_copies().shape == (0, 2)     # taken once
+
+
+def test_fork_shares_every_block_until_written():
+    bm = BlockManager(8, 4)
+    bm.add_sequence(0)
+    for _ in range(6):
+        bm.append_slot(0)
+    bm.fork(0, 1)
+    assert bm.table(1) == bm.table(0) and bm.length(1) == 6
+    assert all(bm.ref_count[b] == 2 for b in bm.table(0))
+    bm.append_slot(0)                            # last block is shared: copied
+    (src, dst), = bm.take_copies().tolist()
+    assert src == bm.table(1)[1] and dst == bm.table(0)[1]
+    bm.append_slot(1)                            # now private to sequence 1: no copy
+    assert bm.take_copies().shape == (0, 2)
+    assert bm.table(0)[0] == bm.table(1)[0]      # the full first block stays shared
+    bm.finish(0)
+    bm.finish(1)
+    assert bm.num_free == 8 and np.all(bm.ref_count == 0)
+
+
+def test_swap_out_and_in():
+    dev, host = BlockManager(6, 4), BlockManager(3, 4)
+    dev.add_sequence(0)
+    for _ in range(9):
+        dev.append_slot(0)
+    before = dev.table(0)
+    out = dev.swap_out(0, host)
+    assert out[:, 0].tolist() == before and dev.num_free == 6 and host.num_free == 0
+    assert dev.table(0) == out[:, 1].tolist()
+    with pytest.raises(OutOfBlocks):
+        host_full = BlockManager(6, 4)
+        host_full.add_sequence(1)
+        for _ in range(9):
+            host_full.append_slot(1)
+        host_full.swap_out(1, host)              # no host blocks left
+    back = dev.swap_in(0, host)
+    assert back[:, 0].tolist() == out[:, 1].tolist() and host.num_free == 3
+    assert dev.table(0) == back[:, 1].tolist() and dev.length(0) == 9
     with pytest.raises(ValueError):
-        bm.append_slot(1)
+        dev.swap_in(0, host)                     # not swapped out
+    dev.fork(0, 1)
+    with pytest.raises(ValueError):
+        dev.swap_out(0, host)                    # shared blocks stay on the device
 
 
 def test_pool_exhaustion_raises():
