@@ -10,7 +10,9 @@ algorithmic KV bytes the decode reads per step divided by the step time
 (GB/s); `roofline` is the partition kernel's algorithmic bytes over its own
 event-timed duration against the 8 TB/s HBM peak; `cpu_baseline` times the
 CPU oracle (float64 numpy, one BLAS thread) on a bounded sample of the same
-workload.
+workload.  `block_copy` times whole-block copies on the same pool: a
+device-to-device copy (copy-on-write) and swapping blocks out to pinned host
+memory and back in.
 """
 
 import argparse
@@ -43,6 +45,8 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="tokens per partition; -1 = the workload's own, 0 = library choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block-copy", action="store_true",
+                    help="skip the block copy / swap measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget for the oracle sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -291,9 +295,64 @@ def main():
         result["setup_write"] = {"ms": round(setup_ms, 3),
                                  "source_bytes": setup_bytes,
                                  "GB_per_s_source_read": round(setup_bytes / setup_ms / 1e6, 1)}
+    if not args.no_block_copy:
+        result["block_copy"] = block_copy_bench(pkv, torch, kc, vc, ks, vs, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_for(w, writes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def block_copy_bench(pkv, torch, kc, vc, ks, vs, reps, copy_pairs=1024, swap_pairs=256):
+    """Times paged_kv_block_copy on the workload's pool: copy_pairs random
+    blocks into a second device pool (the copy-on-write shape: HBM read and
+    write), and swap_pairs blocks out to a pinned host pool and back in
+    (PCIe).  Bytes count the K and V tiles (and FP8 scales) moved once."""
+    rng = np.random.default_rng(7)
+    nb = kc.shape[0]
+    dev = kc.device
+    block_bytes = 2 * kc[0].numel() * kc.element_size() + (
+        2 * ks[0].numel() * 4 if ks is not None else 0)
+
+    def pool(blocks, pinned=False):
+        mk = (lambda t: torch.empty((blocks,) + tuple(t.shape[1:]), dtype=t.dtype,
+                                    pin_memory=True)) if pinned else (
+            lambda t: torch.empty((blocks,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev))
+        return (mk(kc), mk(vc), mk(ks) if ks is not None else None,
+                mk(vs) if vs is not None else None)
+
+    def timed(src, dst, pairs):
+        pkv.paged_kv_block_copy(src[0], src[1], dst[0], dst[1], pairs, src[2], src[3], dst[2],
+                                dst[3])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            pkv.paged_kv_block_copy(src[0], src[1], dst[0], dst[1], pairs, src[2], src[3],
+                                    dst[2], dst[3])
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        n = pairs.shape[0]
+        return {"pairs": n, "us": round(us, 2), "bytes_moved": n * block_bytes,
+                "GB_per_s": round(n * block_bytes / (us * 1e-6) / 1e9, 1)}
+
+    src = (kc, vc, ks, vs)
+    n = min(copy_pairs, nb)
+    pairs = torch.from_numpy(np.stack([rng.choice(nb, n, replace=False), rng.permutation(n)],
+                                      axis=1).astype(np.int32)).to(dev)
+    out = {"block_bytes": block_bytes,
+           "device_copy": timed(src, pool(n), pairs)}
+    m = min(swap_pairs, nb)
+    host = pool(m, pinned=True)
+    out_pairs = torch.from_numpy(np.stack([rng.choice(nb, m, replace=False), rng.permutation(m)],
+                                          axis=1).astype(np.int32)).to(dev)
+    out["swap_out"] = timed(src, host, out_pairs)
+    in_pairs = torch.from_numpy(np.stack([rng.permutation(m), rng.permutation(m)],
+                                         axis=1).astype(np.int32)).to(dev)
+    out["swap_in"] = timed(host, pool(m), in_pairs)
+    out["note"] = ("device_copy moves each byte HBM to HBM (it is read and written: 2x the "
+                   "bytes in HBM traffic); swaps cross PCIe once")
+    return out
 
 
 def cpu_baseline_for(w, writes, budget):
