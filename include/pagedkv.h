@@ -202,6 +202,45 @@ pkv_status_t paged_attention_decode_reduce(
     void* stream);
 
 /*
+ * paged_attention_prefill -- attention of several new query tokens per
+ * sequence over the paged cache, causal: the prefill (or one chunk of a
+ * chunked prefill) on the same block tables as decode.  Sequence i holds
+ * context_lens[i] = n tokens in the cache, its num_query_tokens = M newest
+ * included (written first); query token t sits at position n - M + t and
+ *   out[i][t][h][:] = softmax(q[i][t][h] . K[0 .. n-M+t][h/G]^T * scale)
+ *                     . V[0 .. n-M+t][h/G]
+ * (the decode formula of dpshk.com article section 2.2 applied to each
+ * token over the positions before it; page "PagedAttention 与连续批处理…",
+ * section "连续批处理：让 GPU 永远有活干": new requests join the running
+ * batch, so their prompts are processed against the same paged cache).
+ *   query, out: [S][M][H][D], bf16 only (PKV_ERR_DTYPE otherwise); the
+ *   caches may be bf16 or FP8.  n >= M for every sequence (the caller's
+ *   contract; a token left with no position to see gets zeros).  M = 1 is
+ *   decode.  Indices are 32-bit: num_kv_heads * ceil(M * G / 16) * S *
+ *   ceil(max_context_len / P) must stay below 2^30 and S * M * H * D below
+ *   2^31 (PKV_ERR_SHAPE otherwise).  Other arguments, partitions and the
+ *   workspace (paged_attention_prefill_workspace_size bytes, its first 4096
+ *   zero) are as for paged_attention_decode.
+ */
+pkv_status_t paged_attention_prefill(
+    void* out, const void* query,
+    const void* key_cache, const void* value_cache,
+    const float* key_scale, const float* value_scale,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_query_tokens, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float scale,
+    int32_t q_dtype, int32_t cache_dtype, int32_t partition_size,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/* Workspace bytes paged_attention_prefill needs (0 for invalid arguments). */
+size_t paged_attention_prefill_workspace_size(
+    int32_t num_seqs, int32_t num_query_tokens, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_context_len,
+    int32_t q_dtype, int32_t cache_dtype, int32_t partition_size);
+
+/*
  * paged_kv_block_copy -- copy whole blocks from one pool to another: the
  * copy-on-write of a shared block before a sequence writes into it (page
  * "vLLM的诞生背景：大模型推理的痛点与PagedAttention的破局", the limitations

@@ -40,6 +40,7 @@ from .block_copy import paged_kv_block_copy
 from .attention import (
     paged_attention_decode,
     paged_attention_decode_one,
+    paged_attention_prefill,
     gather_sequence,
     element_values,
 )
@@ -53,6 +54,7 @@ __all__ = [
     "paged_kv_block_copy",
     "paged_attention_decode",
     "paged_attention_decode_one",
+    "paged_attention_prefill",
     "gather_sequence",
     "element_values",
 ]

@@ -123,3 +123,24 @@ def paged_attention_decode_one(q, key_cache, value_cache, block_tables, context_
     K = gather_sequence(key_cache, key_scale, block_tables[seq], n, block_size, [g])[:, 0, :]
     V = gather_sequence(value_cache, value_scale, block_tables[seq], n, block_size, [g])[:, 0, :]
     return _attend(qv, K, V, float(np.float32(scale)))
+
+
+def paged_attention_prefill(q, key_cache, value_cache, block_tables, context_lens, scale,
+                            block_size, key_scale=None, value_scale=None):
+    """float64 [S][M][H][D]: the decode formula for each of M new query tokens.
+
+    Sequence i holds n = context_lens[i] tokens, its M newest being the query
+    tokens; token t sits at position n - M + t and attends to positions
+    0 .. n - M + t (causal), i.e. it is a decode step whose context ends at
+    its own position (dpshk.com article, section 2.2, applied per token).
+    """
+    q = np.asarray(q)
+    M = q.shape[1]
+    lens = np.asarray(context_lens, dtype=np.int64)
+    assert np.all(lens >= M), "every sequence holds its query tokens"
+    out = np.zeros(q.shape, dtype=np.float64)
+    for t in range(M):
+        out[:, t] = paged_attention_decode(q[:, t], key_cache, value_cache, block_tables,
+                                           lens - M + t + 1, scale, block_size, key_scale,
+                                           value_scale)
+    return out

@@ -18,7 +18,9 @@ from ._lib import (
     paged_attention_decode,
     paged_attention_decode_partitions,
     paged_attention_decode_reduce,
+    paged_attention_prefill,
     paged_kv_block_copy,
+    prefill_workspace_size,
     paged_kv_cache_write,
     status_string,
     write_workspace_size,
@@ -29,7 +31,8 @@ __all__ = [
     "PKV_BF16", "PKV_F32", "PKV_FP8_E4M3", "PagedKVError", "BlockManager", "OutOfBlocks",
     "decode_partition_size", "decode_workspace_size", "dtype_code", "load",
     "paged_attention_decode", "paged_attention_decode_partitions",
-    "paged_attention_decode_reduce", "paged_kv_block_copy", "paged_kv_cache_write",
+    "paged_attention_decode_reduce", "paged_attention_prefill", "paged_kv_block_copy",
+    "paged_kv_cache_write", "prefill_workspace_size",
     "status_string",
     "write_workspace_size",
 ]

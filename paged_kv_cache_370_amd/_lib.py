@@ -26,6 +26,8 @@ EXPORTS = (
     "paged_attention_decode_partitions",
     "paged_attention_decode_reduce",
     "paged_kv_block_copy",
+    "paged_attention_prefill",
+    "paged_attention_prefill_workspace_size",
     "pkv_status_string",
     "pkv_version",
 )
@@ -69,6 +71,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode_partition_size.argtypes = geo
     lib.paged_attention_decode_workspace_size.restype = sz
     lib.paged_attention_decode_workspace_size.argtypes = geo
+    lib.paged_attention_prefill.restype = i32
+    lib.paged_attention_prefill.argtypes = ([vp] * 8 + [i32] * 8 + [fp] + [i32] * 3
+                                            + [vp, sz, vp])
+    lib.paged_attention_prefill_workspace_size.restype = sz
+    lib.paged_attention_prefill_workspace_size.argtypes = [i32] * 10
     lib.paged_kv_block_copy.restype = i32
     lib.paged_kv_block_copy.argtypes = [vp] * 9 + [i32] * 5 + [vp]
     lib.pkv_status_string.restype = ctypes.c_char_p
@@ -233,3 +240,39 @@ def paged_kv_block_copy(src_key_cache, src_value_cache, dst_key_cache, dst_value
         _ptr(block_pairs), block_pairs.shape[0], H_kv, D, bs, dtype_code(src_key_cache),
         _stream(stream))
     _check(st, "paged_kv_block_copy")
+
+
+# ----------------------------------------------------------------- prefill
+
+def prefill_workspace_size(num_seqs, num_query_tokens, num_heads, num_kv_heads, head_size,
+                           block_size, max_context_len, q_code, c_code, partition_size=0) -> int:
+    return int(load().paged_attention_prefill_workspace_size(
+        num_seqs, num_query_tokens, num_heads, num_kv_heads, head_size, block_size,
+        max_context_len, q_code, c_code, partition_size))
+
+
+def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, context_lens,
+                            max_context_len, scale, key_scale=None, value_scale=None,
+                            partition_size=0, workspace=None, stream=None):
+    """out/query [S][M][H][D] bf16: M new tokens per sequence, already in the
+    cache as the newest M of context_lens[i]; token t attends causally to the
+    positions up to n - M + t."""
+    _contig(out, query, key_cache, value_cache, block_tables, context_lens, key_scale,
+            value_scale)
+    if query.dim() != 4 or out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("query and out must both be [S][M][H][D] of one dtype")
+    S, M, H, D = query.shape
+    _, H_kv, bs, _ = key_cache.shape
+    qc, cc = dtype_code(query), dtype_code(key_cache)
+    if workspace is None:
+        # zero-filled: the first 4 KiB are the library's work-queue counters
+        need = prefill_workspace_size(S, M, H, H_kv, D, bs, max_context_len, qc, cc,
+                                      partition_size)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=query.device) if need else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().paged_attention_prefill(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
+        _ptr(value_scale), _ptr(block_tables), _ptr(context_lens), S, M, H, H_kv, D, bs,
+        block_tables.shape[1], int(max_context_len), float(scale), qc, cc, int(partition_size),
+        _ptr(workspace), wbytes, _stream(stream))
+    _check(st, "paged_attention_prefill")

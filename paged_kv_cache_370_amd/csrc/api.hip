@@ -54,10 +54,11 @@ pkv_status_t check_decode_shape(int S, int H, int H_kv, int D, int bs, int max_c
 // than one partition.
 constexpr size_t kSchedBytes = 4096;
 
-size_t decode_workspace(int S, int H, int D, int max_ctx, int P) {
+// rows of partials: S sequences x M query tokens x H heads x partitions
+size_t decode_workspace(int S, int H, int D, int max_ctx, int P, int M = 1) {
   const int np = num_partitions(max_ctx, P);
   if (np <= 1) return kSchedBytes;
-  const size_t rows = (size_t)S * H * np;
+  const size_t rows = (size_t)S * M * H * np;
   return kSchedBytes + 2 * align256(rows * sizeof(float)) + align256(rows * D * sizeof(float));
 }
 
@@ -73,7 +74,7 @@ DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
                          const int32_t* context_lens, int S, int H, int H_kv, int D, int bs,
                          int max_blocks, int max_ctx, float scale, int q, int c, int partition,
                          void* workspace, size_t workspace_bytes, void* stream,
-                         bool need_inputs) {
+                         bool need_inputs, int M = 1) {
   DecodeSetup r{};
   r.status = check_decode_shape(S, H, H_kv, D, bs, max_ctx, q, c);
   if (r.status != PKV_OK) return r;
@@ -83,6 +84,14 @@ DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
   }
   const int P = resolve_partition(bs, max_ctx, partition);
   if (P <= 0) {
+    r.status = PKV_ERR_SHAPE;
+    return r;
+  }
+  // Work items (KV head x 16-row chunk x sequence x partition) and reduce
+  // rows index with 32-bit integers.
+  const long long chunks = ((long long)M * (H / H_kv) + 15) / 16;
+  if ((long long)H_kv * chunks * S * num_partitions(max_ctx, P) >= (1LL << 30) ||
+      (long long)S * M * H * D >= (1LL << 31)) {
     r.status = PKV_ERR_SHAPE;
     return r;
   }
@@ -104,7 +113,7 @@ DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
       return r;
     }
   }
-  const size_t need = decode_workspace(S, H, D, max_ctx, P);
+  const size_t need = decode_workspace(S, H, D, max_ctx, P, M);
   if (!workspace || workspace_bytes < need) {
     r.status = PKV_ERR_WORKSPACE;
     return r;
@@ -115,12 +124,12 @@ DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
   a.tables = block_tables; a.lens = context_lens;
   a.S = S; a.H = H; a.H_kv = H_kv; a.D = D; a.bs = bs; a.max_blocks = max_blocks;
   a.max_ctx = max_ctx; a.scale = scale; a.q_dtype = q; a.cache_dtype = c;
-  a.P = P; a.NP = num_partitions(max_ctx, P);
+  a.P = P; a.NP = num_partitions(max_ctx, P); a.M = M;
   {
     char* ws = reinterpret_cast<char*>(workspace);
     a.sched = reinterpret_cast<int*>(ws);
     if (a.NP > 1) {
-      const size_t rows = (size_t)S * H * a.NP;
+      const size_t rows = (size_t)S * M * H * a.NP;
       char* part = ws + kSchedBytes;
       a.ws_m = reinterpret_cast<float*>(part);
       a.ws_l = reinterpret_cast<float*>(part + align256(rows * sizeof(float)));
@@ -288,6 +297,46 @@ pkv_status_t paged_attention_decode(void* out, const void* query, const void* ke
                                        head_size, block_size, max_context_len, q_dtype,
                                        cache_dtype, partition_size, workspace, workspace_bytes,
                                        stream);
+}
+
+pkv_status_t paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                                     const void* value_cache, const float* key_scale,
+                                     const float* value_scale, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_query_tokens, int32_t num_heads,
+                                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     float scale, int32_t q_dtype, int32_t cache_dtype,
+                                     int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (num_query_tokens <= 0) return PKV_ERR_SHAPE;
+  if (check_decode_shape(num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                         max_context_len, q_dtype, cache_dtype) == PKV_OK &&
+      q_dtype != PKV_BF16)
+    return PKV_ERR_DTYPE;  // the matrix-core kernel serves several query tokens
+  DecodeSetup s = setup_decode(out, query, key_cache, value_cache, key_scale, value_scale,
+                               block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                               head_size, block_size, max_blocks_per_seq, max_context_len, scale,
+                               q_dtype, cache_dtype, partition_size, workspace, workspace_bytes,
+                               stream, true, num_query_tokens);
+  if (s.status != PKV_OK || s.empty) return s.status;
+  if (!decode_mfma_supported(s.a)) return PKV_ERR_SHAPE;
+  const pkv_status_t st = hip_status(launch_decode_mfma(s.a));
+  if (st != PKV_OK || s.a.NP <= 1) return st;
+  return hip_status(launch_decode_reduce(s.a));
+}
+
+size_t paged_attention_prefill_workspace_size(int32_t num_seqs, int32_t num_query_tokens,
+                                              int32_t num_heads, int32_t num_kv_heads,
+                                              int32_t head_size, int32_t block_size,
+                                              int32_t max_context_len, int32_t q_dtype,
+                                              int32_t cache_dtype, int32_t partition_size) {
+  if (num_query_tokens <= 0) return 0;
+  const int P = paged_attention_decode_partition_size(num_seqs, num_heads, num_kv_heads,
+                                                      head_size, block_size, max_context_len,
+                                                      q_dtype, cache_dtype, partition_size);
+  if (P <= 0) return 0;
+  return decode_workspace(num_seqs, num_heads, head_size, max_context_len, P, num_query_tokens);
 }
 
 }  // extern "C"

@@ -94,6 +94,7 @@ struct MfmaParams {
   int* sched;  // claim counter of queue x at [x * kCounterStride], finished-workgroup
                // counter at [(8 + x) * kCounterStride]
   int S, H, H_kv, G, chunks, max_blocks, P, NP;
+  int M;  // query tokens per sequence (1 for decode)
   float scale_log2;
 };
 
@@ -163,9 +164,23 @@ struct Src {
 };
 
 // One work item's view of its partition.
+// Rows: the (query token, head) pairs of one KV head, row m * G + g for
+// token m and head kvh * G + g (with one token per sequence, row = head).
+// An item covers nh <= 16 consecutive rows from r0.
 struct Part {
-  int seq, kvh, h0, nh, start, end, first_blk;
+  int seq, kvh, r0, nh, start, end, first_blk;
 };
+
+// Index of a row's [D] vector in q / out ([S][M][H][D]) and of its partial.
+template <bool MQ>
+__device__ __forceinline__ size_t row_of(const MfmaParams& p, const Part& w, int rho) {
+  if constexpr (MQ) {
+    const int m = rho / p.G;
+    return ((size_t)w.seq * p.M + m) * p.H + (size_t)w.kvh * p.G + (rho - m * p.G);
+  } else {
+    return (size_t)w.seq * p.H + (size_t)w.kvh * p.G + rho;
+  }
+}
 
 // Block ids of a chunk (tokens c0 .. c0 + CHUNK - 1) are CHUNK / BS
 // consecutive entries ctab[0 ..]; a chunk starts on a block boundary.
@@ -285,12 +300,15 @@ __device__ __forceinline__ void scores(const KStage<CT, D>& st, const uint4* s_q
 // Online softmax update with this chunk's scores, then O^T += V^T . P^T.
 template <int D>
 __device__ __forceinline__ void softmax_pv(const f32x4_t (&s)[kNT], const float (&fk)[kNT],
-                                           const float (&fv)[kNT], bool scaled_v, int c0, int end,
-                                           const uint16_t* s_v, f32x4_t (&acc)[D / 16], float& m,
-                                           float& lsum, int lane) {
+                                           const float (&fv)[kNT], bool scaled_v, int c0,
+                                           int full_end, int end, const uint16_t* s_v,
+                                           f32x4_t (&acc)[D / 16], float& m, float& lsum,
+                                           int lane) {
+  // end: this lane's row sees tokens below it; full_end (uniform, <= every
+  // row's end): a chunk below it needs no mask.
   constexpr int VS = D + 16;
   const int q = lane >> 4, r = lane & 15;
-  const bool full = c0 + 16 * kNT <= end;
+  const bool full = c0 + 16 * kNT <= full_end;
   float x[kNT][4];
   float mc = kNegInf;
 #pragma unroll
@@ -475,8 +493,8 @@ __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y
   it.w.seq = seq;
   it.w.kvh = y / p.chunks;
   const int hc = y - it.w.kvh * p.chunks;
-  it.w.h0 = it.w.kvh * p.G + hc * 16;
-  it.w.nh = min(16, p.G - hc * 16);
+  it.w.r0 = hc * 16;
+  it.w.nh = min(16, p.M * p.G - hc * 16);
   it.w.start = it.part * p.P;
   it.w.end = min(it.n, it.w.start + p.P);
   it.w.first_blk = it.w.start / BS;
@@ -505,7 +523,7 @@ __device__ __forceinline__ void store_tab(int tab, int* wtab, int lane) {
 
 // Q operand fragments of an item, one element per thread (thread t owns
 // element t), shared by the waves; heads past the group are zeros.
-template <typename CT, int D>
+template <typename CT, int D, bool MQ>
 __device__ __forceinline__ uint4 fetch_q(const MfmaParams& p, const Part& w, int tid) {
   using Gm = Geometry<CT, D>;
   // fragment c = tid / 64 for lane l = (q, r) = tid % 64; threads past the
@@ -515,7 +533,7 @@ __device__ __forceinline__ uint4 fetch_q(const MfmaParams& p, const Part& w, int
   const int hq = l & 15;
   return *reinterpret_cast<const uint4*>(
       reinterpret_cast<const uint16_t*>(p.q) +
-      ((size_t)w.seq * p.H + w.h0 + min(hq, w.nh - 1)) * D + Gm::DQ * (l >> 4) + 8 * c);
+      row_of<MQ>(p, w, w.r0 + min(hq, w.nh - 1)) * D + Gm::DQ * (l >> 4) + 8 * c);
 }
 
 template <typename CT, int D>
@@ -526,7 +544,7 @@ __device__ __forceinline__ void store_q(uint4 v, const Part& w, uint4* qf, int t
   }
 }
 
-template <typename CT, int D, int BS, bool SCAN>
+template <typename CT, int D, int BS, bool SCAN, bool MQ>
 __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   using Gm = Geometry<CT, D>;
   static_assert(kMaxTable == kNW * 64, "one table entry per thread");
@@ -583,7 +601,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   Item it = decode_item<BS, SCAN>(p, min(cur, total - 1), Y, n_full, s_full, s_rag, s_len);
   if (cur < total) {
     store_tab(fetch_tab<CT, D, BS>(p, it.w, wave, lane), s_wtab[0][wave], lane);
-    store_q<CT, D>(fetch_q<CT, D>(p, it.w, tid), it.w, s_qf[0], tid);
+    store_q<CT, D>(fetch_q<CT, D, MQ>(p, it.w, tid), it.w, s_qf[0], tid);
   }
   // The second item's block ids travel in a register until the first
   // item's last chunk (each item's are fetched one item ahead).
@@ -626,7 +644,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     // Prefetch the next item's Q and claim the item after it.  Nothing reads
     // the other buffers until the next item.
     const Item nx = decode_item<BS, SCAN>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len);
-    const uint4 q_next = fetch_q<CT, D>(p, nx.w, tid);
+    const uint4 q_next = fetch_q<CT, D, MQ>(p, nx.w, tid);
     // The claim's result is used only after barrier X.  (Only thread 0 sets
     // and reads it: initialising it in the other lanes would make the
     // compiler wait for every pending load first.)
@@ -650,6 +668,16 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     // the loads below.
     const bool next_mine = nvalid_n > wave;
     const int* ctab = s_wtab[buf][wave];  // this chunk's block ids
+    // Causal rows (several query tokens per sequence): token m of a
+    // sequence of n cached tokens sits at position n - M + m and sees
+    // positions up to it.  With one token per sequence every row sees the
+    // whole partition.
+    int full_end = it.w.end, row_end = it.w.end;
+    if constexpr (MQ) {
+      const int base = it.n - p.M + 1;  // end of token 0's row
+      row_end = min(it.w.end, base + (it.w.r0 + r) / p.G);
+      full_end = min(it.w.end, base + it.w.r0 / p.G);
+    }
     int ci = wave;
     do {
       const int c0 = it.w.start + ci * Gm::CHUNK;
@@ -682,7 +710,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       }
       load_k<CT, D, BS>(ks, p, src, lw, ntab, cn, lane);
       __builtin_amdgcn_sched_barrier(0);
-      softmax_pv<D>(sc, fk, fv, Gm::ELEM == 1, c0, it.w.end, s_v, acc, m, lsum, lane);
+      softmax_pv<D>(sc, fk, fv, Gm::ELEM == 1, c0, full_end, row_end, s_v, acc, m, lsum, lane);
       ci += kNW;
       ctab += EPC;
     } while (ci < nvalid);
@@ -737,7 +765,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
           O.z = fmaf(a.z, wt, O.z);
           O.w = fmaf(a.w, wt, O.w);
         }
-        const size_t row = (size_t)it.w.seq * p.H + it.w.h0 + g;
+        const size_t row = row_of<MQ>(p, it.w, it.w.r0 + g);
         if (single) {
           const bool ok = L > 0.f;
           const float ox = ok ? O.x / L : 0.f, oy = ok ? O.y / L : 0.f;
@@ -773,11 +801,11 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
 // Workgroups of a persistent launch: as many as are resident at once (CUs x
 // the kernel's occupancy, a multiple of the 8 XCDs), never more than items.
 // The occupancy query runs once per kernel variant and device.
-template <typename CT, int D, int BS, bool SCAN>
+template <typename CT, int D, int BS, bool SCAN, bool MQ>
 unsigned persistent_grid(long long items) {
   constexpr int kMaxDev = 64;
   static int resident[kMaxDev];  // per device, for this kernel variant only
-  const void* kern = reinterpret_cast<const void*>(decode_mfma_kernel<CT, D, BS, SCAN>);
+  const void* kern = reinterpret_cast<const void*>(decode_mfma_kernel<CT, D, BS, SCAN, MQ>);
   int dev = 0;
   int per_dev = 0;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDev) per_dev = resident[dev];
@@ -795,26 +823,33 @@ unsigned persistent_grid(long long items) {
   return (unsigned)(per_dev < items ? per_dev : items);
 }
 
+template <typename CT, int D, int BS, bool MQ>
+hipError_t launch_mode(const DecodeArgs& a, const MfmaParams& p, long long items) {
+  if (a.S <= kMaxScanSeqs) {
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, true, MQ>),
+                       dim3(persistent_grid<CT, D, BS, true, MQ>(items)), dim3(kNW * 64), 0,
+                       a.stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, false, MQ>),
+                       dim3(persistent_grid<CT, D, BS, false, MQ>(items)), dim3(kNW * 64), 0,
+                       a.stream, p);
+  }
+  return hipGetLastError();
+}
+
 template <typename CT, int D, int BS>
 hipError_t launch_bs(const DecodeArgs& a) {
   MfmaParams p;
   p.q = a.q; p.kc = a.key_cache; p.vc = a.value_cache; p.ks = a.key_scale; p.vs = a.value_scale;
   p.tables = a.tables; p.lens = a.lens; p.out = a.out;
   p.ws_m = a.ws_m; p.ws_l = a.ws_l; p.ws_acc = a.ws_acc; p.sched = a.sched;
-  p.S = a.S; p.H = a.H; p.H_kv = a.H_kv; p.G = a.H / a.H_kv; p.chunks = (p.G + 15) / 16;
+  p.S = a.S; p.H = a.H; p.H_kv = a.H_kv; p.G = a.H / a.H_kv; p.M = a.M;
+  p.chunks = (a.M * p.G + 15) / 16;
   p.max_blocks = a.max_blocks; p.P = a.P; p.NP = a.NP;
   p.scale_log2 = a.scale * kLog2e;
   const long long items = (long long)a.H_kv * p.chunks * a.S * a.NP;
-  if (a.S <= kMaxScanSeqs) {
-    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, true>),
-                       dim3(persistent_grid<CT, D, BS, true>(items)), dim3(kNW * 64), 0, a.stream,
-                       p);
-  } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, false>),
-                       dim3(persistent_grid<CT, D, BS, false>(items)), dim3(kNW * 64), 0,
-                       a.stream, p);
-  }
-  return hipGetLastError();
+  return a.M > 1 ? launch_mode<CT, D, BS, true>(a, p, items)
+                 : launch_mode<CT, D, BS, false>(a, p, items);
 }
 
 template <typename CT, int D>

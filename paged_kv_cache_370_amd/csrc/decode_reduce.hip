@@ -5,7 +5,7 @@
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p acc_p / sum_p w_p l_p.
 // (Whole-context softmax: dpshk.com PagedAttention article, section 2.2.)
 //
-// One workgroup of D threads per (sequence, query head); thread d merges
+// One workgroup of D threads per (sequence, query token, query head); thread d merges
 // acc_p[d] over the partitions in batches with an online maximum, all in
 // registers.  The first batch's loads do not wait for the context length:
 // they are clamped to the NP partition rows the workspace holds for every
@@ -46,12 +46,17 @@ __device__ __forceinline__ void merge_chunk(const float (&m)[U], const float (&l
 template <bool OUT_BF16, int D>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(
     void* __restrict__ out, const int32_t* __restrict__ lens, const float* __restrict__ ws_m,
-    const float* __restrict__ ws_l, const float* __restrict__ ws_acc, int H, int P, int NP) {
+    const float* __restrict__ ws_l, const float* __restrict__ ws_acc, int H, int P, int NP,
+    int M) {
   constexpr int U0 = kFirst, U = kChunk;
-  const int h = blockIdx.x;
-  const int seq = blockIdx.y;
+  // One workgroup per row (seq * M + t) * H + h: query token t of sequence
+  // seq, query head h (M = 1 for decode).
+  const size_t row = blockIdx.x;
+  const int st = (int)(row / H);
+  const int seq = st / M;
+  const int t = st - seq * M;
   const int d = threadIdx.x;
-  const size_t base = ((size_t)seq * H + h) * NP;
+  const size_t base = row * NP;
   const float* pm = ws_m + base;
   const float* pl = ws_l + base;
   const float* pa = ws_acc + base * D + d;
@@ -69,38 +74,42 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
     l0[u] = pl[q];
   }
   const int n = lens[seq];
-  const int np = (n + P - 1) / P;  // one partition: written by the partition kernel
-  float M = kNegInf, L = 0.f, O = 0.f;
-  merge_chunk<U0>(m0, l0, a0, 0, np, M, L, O);
+  // Token t sits at position n - M + t and sees the positions up to it: its
+  // partitions are the first ceil(end / P) of the sequence's.
+  const int end = n - M + t + 1;
+  const int np = (end + P - 1) / P;
+  float Mx = kNegInf, L = 0.f, O = 0.f;
+  merge_chunk<U0>(m0, l0, a0, 0, np, Mx, L, O);
   for (int q0 = U0; q0 < np; q0 += U) {
-    float m[U], l[U], a[U];
+    float mm[U], l[U], a[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int q = min(q0 + u, np - 1);
-      m[u] = pm[q];
+      mm[u] = pm[q];
       l[u] = pl[q];
       a[u] = pa[(size_t)q * D];
     }
-    merge_chunk<U>(m, l, a, q0, np, M, L, O);
+    merge_chunk<U>(mm, l, a, q0, np, Mx, L, O);
   }
   // No branch before this point, so the first chunk's loads are issued
-  // before the length arrives.
-  if (np <= 1) return;
-  const float res = O / L;
-  const size_t oi = ((size_t)seq * H + h) * D + d;
+  // before the length arrives.  A sequence of at most P tokens was written
+  // directly by the partition kernel.
+  if (n <= P) return;
+  const float res = L > 0.f ? O / L : 0.f;
+  const size_t oi = row * D + d;
   if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16(res);
   else reinterpret_cast<float*>(out)[oi] = res;
 }
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a) {
-  dim3 grid(a.H, a.S);
+  const unsigned grid = (unsigned)((size_t)a.S * a.M * a.H);
   if (a.q_dtype == PKV_BF16) {
     hipLaunchKernelGGL((decode_reduce_kernel<true, D>), grid, dim3(D), 0, a.stream, a.out, a.lens,
-                       a.ws_m, a.ws_l, a.ws_acc, a.H, a.P, a.NP);
+                       a.ws_m, a.ws_l, a.ws_acc, a.H, a.P, a.NP, a.M);
   } else {
     hipLaunchKernelGGL((decode_reduce_kernel<false, D>), grid, dim3(D), 0, a.stream, a.out,
-                       a.lens, a.ws_m, a.ws_l, a.ws_acc, a.H, a.P, a.NP);
+                       a.lens, a.ws_m, a.ws_l, a.ws_acc, a.H, a.P, a.NP, a.M);
   }
   return hipGetLastError();
 }

@@ -33,6 +33,8 @@ struct DecodeArgs {
   const int32_t* tables;
   const int32_t* lens;
   int S, H, H_kv, D, bs, max_blocks, max_ctx;
+  int M = 1;  // query tokens per sequence: 1 for decode, the chunk for prefill;
+              // q and out are [S][M][H][D]
   float scale;
   int q_dtype, cache_dtype;
   int P;   // partition size in tokens (multiple of bs)

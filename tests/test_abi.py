@@ -151,3 +151,39 @@ def test_product_never_imports_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", src, re.M), f
                 assert "workloads" not in src, f
+
+
+def _prefill(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None, tables=FAKE, lens=FAKE, S=2,
+             M=4, H=8, H_kv=2, D=128, bs=16, max_blocks=8, max_ctx=100, scale=0.1, qd=1, cd=1,
+             ps=0, ws=None, wsb=0)
+    a.update(kw)
+    return pkv.load().paged_attention_prefill(
+        a["out"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["tables"], a["lens"], a["S"],
+        a["M"], a["H"], a["H_kv"], a["D"], a["bs"], a["max_blocks"], a["max_ctx"], a["scale"],
+        a["qd"], a["cd"], a["ps"], a["ws"], a["wsb"], None)
+
+
+def test_prefill_argument_checks():
+    assert _prefill(M=0) == 2
+    assert _prefill(out=None) == 1
+    assert _prefill(q=None) == 1
+    assert _prefill(cd=2) == 1                        # FP8 without scales
+    assert _prefill(qd=0, cd=0) == 3                  # fp32 queries: decode only
+    assert _prefill(qd=0, cd=2) == 3
+    assert _prefill(D=96) == 2
+    assert _prefill(H=7) == 2
+    assert _prefill(max_ctx=1000) == 2
+    assert _prefill(ws=None, wsb=0) == 4
+    assert _prefill(S=0, out=None, q=None, kc=None, vc=None, tables=None, lens=None) == 0
+    # 32-bit index range: items and reduce rows
+    assert _prefill(S=1 << 20, M=4096, H=64, H_kv=8, max_ctx=100) == 2
+
+
+def test_prefill_workspace_grows_with_tokens():
+    one = pkv.decode_workspace_size(4, 8, 2, 128, 16, 3000, 1, 1, 512)
+    assert pkv.prefill_workspace_size(4, 1, 8, 2, 128, 16, 3000, 1, 1, 512) == one
+    rows = 4 * 16 * 8 * 6
+    expect = 4096 + 2 * ((rows * 4 + 255) // 256 * 256) + (rows * 128 * 4 + 255) // 256 * 256
+    assert pkv.prefill_workspace_size(4, 16, 8, 2, 128, 16, 3000, 1, 1, 512) == expect
+    assert pkv.prefill_workspace_size(4, 0, 8, 2, 128, 16, 3000, 1, 1, 512) == 0

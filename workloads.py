@@ -86,6 +86,7 @@ class Workload:
     scale: float = 0.0
     partition_size: int = 0
     shared_blocks: int = 0
+    query_tokens: int = 1
 
     @property
     def max_blocks(self) -> int:
@@ -99,8 +100,12 @@ class Workload:
 def build_workload(name, S, H, H_kv, D, block_size, q_dtype, cache_dtype, lens,
                    seed, free_frac=0.1, prefix_tokens=0, fill="random",
                    layout_seed=None, partition_size=0, src_dtype=None,
-                   max_blocks=None, num_blocks=None):
+                   max_blocks=None, num_blocks=None, query_tokens=1):
     """Build one seeded workload.
+
+    query_tokens = M > 1 (a prefill chunk): q is [S][M][H][D] and the step
+    write supplies the M newest positions n-M .. n-1 of every sequence
+    (every n >= M); with M = 1, q is [S][H][D] and the step is position n-1.
 
     fill="random": the pool already holds N(0,1) K/V for positions < n-1 of
         every sequence; the step write supplies position n-1.
@@ -148,7 +153,9 @@ def build_workload(name, S, H, H_kv, D, block_size, q_dtype, cache_dtype, lens,
         cursor += k
 
     pool_shape = (num_blocks, H_kv, bs, D)
-    q = _normal(rng_val, (S, H, D), q_dtype)
+    M = int(query_tokens)
+    assert M >= 1 and (M == 1 or np.all(lens >= M))
+    q = _normal(rng_val, (S, H, D) if M == 1 else (S, M, H, D), q_dtype)
 
     if fill == "random":
         kc = _normal(rng_val, pool_shape, cache_dtype)
@@ -160,11 +167,10 @@ def build_workload(name, S, H, H_kv, D, block_size, q_dtype, cache_dtype, lens,
         for i in range(S):
             if lens[i] == 0:
                 continue
-            last = tables[i, nb[i] - 1]
-            start = int(lens[i] - 1 - (nb[i] - 1) * bs)   # row of position n-1
-            kc[last, :, start:, :] = poison
-            vc[last, :, start:, :] = poison
-        positions = [np.arange(n - 1, n) if n > 0 else np.zeros(0, np.int64) for n in lens]
+            for pos in range(int(lens[i]) - M, int(nb[i]) * bs):   # the step's rows and after
+                kc[tables[i, pos // bs], :, pos % bs, :] = poison
+                vc[tables[i, pos // bs], :, pos % bs, :] = poison
+        positions = [np.arange(n - M, n) if n > 0 else np.zeros(0, np.int64) for n in lens]
         writes = [_step_write(rng_val, tables, positions, H_kv, D, bs, src_dtype)]
     else:
         kc = np.full(pool_shape, _poison(cache_dtype), dtype=_np_dtype(cache_dtype))
@@ -172,8 +178,8 @@ def build_workload(name, S, H, H_kv, D, block_size, q_dtype, cache_dtype, lens,
         if fill == "write-all":
             groups = [[np.arange(n) for n in lens]]
         else:
-            groups = [[np.arange(max(n - 1, 0)) for n in lens],
-                      [np.arange(n - 1, n) if n > 0 else np.zeros(0, np.int64) for n in lens]]
+            groups = [[np.arange(max(n - M, 0)) for n in lens],
+                      [np.arange(n - M, n) if n > 0 else np.zeros(0, np.int64) for n in lens]]
         writes = []
         for g_idx, positions in enumerate(groups):
             if pb and g_idx == 0:
@@ -192,7 +198,7 @@ def build_workload(name, S, H, H_kv, D, block_size, q_dtype, cache_dtype, lens,
                     block_tables=tables, context_lens=lens.astype(np.int32),
                     writes=writes, key_scale=ks, value_scale=vs,
                     scale=float(np.float32(1.0 / np.sqrt(D))),
-                    partition_size=partition_size, shared_blocks=pb)
+                    partition_size=partition_size, shared_blocks=pb, query_tokens=M)
 
 
 def _step_write(rng, tables, positions, H_kv, D, bs, src_dtype):
