@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged-decode attention: KV bytes read GB/s (% of HBM peak); seq-heads/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOADS = {"tiny-fp32": 1, "7b-decode-bf16": 2, "32k-gqa-bf16": 3,
              "shared-prefix-bf16": 4, "fp8-kv": 5}
 DEFAULT_WORKLOAD = "7b-decode-bf16"
@@ -45,6 +46,8 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="tokens per partition; -1 = the workload's own, 0 = library choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", default="prefill-chunk-gqa-bf16",
+                    help="chunked-prefill workload timed beside the decode step ('none': skip)")
     ap.add_argument("--no-block-copy", action="store_true",
                     help="skip the block copy / swap measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -297,6 +300,8 @@ def main():
                                  "GB_per_s_source_read": round(setup_bytes / setup_ms / 1e6, 1)}
     if not args.no_block_copy:
         result["block_copy"] = block_copy_bench(pkv, torch, kc, vc, ks, vs, args.steps)
+    if args.prefill != "none":
+        result["prefill"] = prefill_bench(pkv, torch, args.prefill, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_for(w, writes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -353,6 +358,73 @@ def block_copy_bench(pkv, torch, kc, vc, ks, vs, reps, copy_pairs=1024, swap_pai
     out["note"] = ("device_copy moves each byte HBM to HBM (it is read and written: 2x the "
                    "bytes in HBM traffic); swaps cross PCIe once")
     return out
+
+
+def prefill_flops(lens, M, H, D):
+    """Algorithmic flops of causal multi-token attention: token t of a
+    sequence of n tokens sees e = n - M + t + 1 positions; per query head
+    QK^T and PV take 2 * D * e multiply-adds each (4 * D * e flops)."""
+    e = np.concatenate([np.asarray(n) - M + np.arange(M) + 1 for n in lens])
+    return int(4 * D * H * e.sum())
+
+
+def prefill_bench(pkv, torch, name, reps):
+    """Times one chunked-prefill step (paged_kv_cache_write of the chunk's
+    K/V, then paged_attention_prefill) on a synthetic workload, and the
+    attention launch alone back to back, against the bf16 MFMA peak."""
+    import workloads
+    w = workloads.make_prefill(name)
+    dev = torch.device("cuda:0")
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, kc, vc = t(w.q), t(w.key_cache), t(w.value_cache)
+    tables, lens = t(w.block_tables), t(w.context_lens)
+    key, value, slots = (t(x) for x in w.writes[-1])
+    out = torch.empty_like(q)
+    M = w.query_tokens
+    P = pkv.decode_partition_size(w.S, w.H, w.H_kv, w.D, w.block_size, w.max_context_len, 1, 1,
+                                  0)
+    need = pkv.prefill_workspace_size(w.S, M, w.H, w.H_kv, w.D, w.block_size, w.max_context_len,
+                                      1, 1, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+
+    def attn():
+        pkv.paged_attention_prefill(out, q, kc, vc, tables, lens, w.max_context_len, w.scale,
+                                    workspace=ws)
+
+    def step():
+        pkv.paged_kv_cache_write(key, value, kc, vc, slots)
+        attn()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    step_ms, attn_ms = timed(step), timed(attn)
+    flops = prefill_flops(w.context_lens, M, w.H, w.D)
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    return {"workload": w.name, "seqs": w.S, "chunk_tokens": M, "q_heads": w.H,
+            "kv_heads": w.H_kv, "head_size": w.D, "block_size": w.block_size,
+            "context": int(w.max_context_len), "partition_size": P,
+            "flops_per_step": flops, "ms_per_step": round(step_ms, 5),
+            "tokens_per_s": round(w.S * M / (step_ms * 1e-3), 1),
+            "attention_ms": round(attn_ms, 5),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
 def cpu_baseline_for(w, writes, budget):

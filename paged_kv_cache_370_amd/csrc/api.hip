@@ -3,6 +3,8 @@
 // check happens before the first launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "pkv_internal.h"
 
 using namespace pkv;
@@ -299,6 +301,52 @@ pkv_status_t paged_attention_decode(void* out, const void* query, const void* ke
                                        stream);
 }
 
+// Which kernel serves a multi-token call, and its partition size.  Long
+// chunks (at least kTileMinRows (token, head) rows per KV head) over a bf16
+// cache run on the tiled prefill kernel; short ones (and FP8 caches) on the
+// decode kernel's multi-token mode, whose 16-row tiles suit the HBM-bound
+// case.  The tiled kernel's own partition choice keeps whole contexts in one
+// partition unless the grid would leave CUs idle (two workgroups per CU on
+// 256 CUs), in partitions of at least 512 keys.
+constexpr int kTileMinRows = 64;
+constexpr long long kTileFillWorkgroups = 512;
+
+struct PrefillPlan {
+  bool tiled;
+  int P;  // partition size, or <= 0 for invalid arguments
+};
+
+PrefillPlan prefill_plan(int S, int M, int H, int H_kv, int D, int bs, int max_ctx, int q,
+                         int c, int requested) {
+  PrefillPlan pl{false, -1};
+  if (M <= 0 || check_decode_shape(S, H, H_kv, D, bs, max_ctx, q, c) != PKV_OK ||
+      q != PKV_BF16)
+    return pl;
+  const long long rows = (long long)M * (H / H_kv);
+  pl.tiled = c == PKV_BF16 && rows >= kTileMinRows;
+  if (!pl.tiled) {
+    pl.P = resolve_partition(bs, max_ctx, requested);
+    return pl;
+  }
+  if (requested != 0) {
+    pl.P = requested > 0 && requested % bs == 0 && requested / bs + 1 <= kPrefillMaxTable
+               ? requested
+               : -1;
+    return pl;
+  }
+  const int tile = prefill_tile_rows();
+  const long long tiles = (long long)S * H_kv * ((rows + tile - 1) / tile);
+  const int cap = (kPrefillMaxTable - 1) * bs / 64 * 64;  // keys one table slice holds
+  long long np = (max_ctx + cap - 1) / cap;
+  const long long fill = tiles > 0 ? (kTileFillWorkgroups + tiles - 1) / tiles : 1;
+  const long long by_len = max_ctx / 512 > 1 ? max_ctx / 512 : 1;
+  np = std::max(np, std::min(fill, by_len));
+  if (np < 1) np = 1;
+  const long long per = (max_ctx + np - 1) / np;
+  pl.P = (int)std::max<long long>(64, (per + 63) / 64 * 64);
+  return pl;
+}
+
 pkv_status_t paged_attention_prefill(void* out, const void* query, const void* key_cache,
                                      const void* value_cache, const float* key_scale,
                                      const float* value_scale, const int32_t* block_tables,
@@ -310,18 +358,28 @@ pkv_status_t paged_attention_prefill(void* out, const void* query, const void* k
                                      int32_t partition_size, void* workspace,
                                      size_t workspace_bytes, void* stream) {
   if (num_query_tokens <= 0) return PKV_ERR_SHAPE;
-  if (check_decode_shape(num_seqs, num_heads, num_kv_heads, head_size, block_size,
-                         max_context_len, q_dtype, cache_dtype) == PKV_OK &&
-      q_dtype != PKV_BF16)
-    return PKV_ERR_DTYPE;  // the matrix-core kernel serves several query tokens
+  const pkv_status_t shape = check_decode_shape(num_seqs, num_heads, num_kv_heads, head_size,
+                                                block_size, max_context_len, q_dtype, cache_dtype);
+  if (shape != PKV_OK) return shape;
+  if (q_dtype != PKV_BF16) return PKV_ERR_DTYPE;  // the matrix-core kernels take bf16 queries
+  const PrefillPlan plan = prefill_plan(num_seqs, num_query_tokens, num_heads, num_kv_heads,
+                                        head_size, block_size, max_context_len, q_dtype,
+                                        cache_dtype, partition_size);
+  if (plan.P <= 0) return PKV_ERR_SHAPE;
   DecodeSetup s = setup_decode(out, query, key_cache, value_cache, key_scale, value_scale,
                                block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
                                head_size, block_size, max_blocks_per_seq, max_context_len, scale,
-                               q_dtype, cache_dtype, partition_size, workspace, workspace_bytes,
-                               stream, true, num_query_tokens);
+                               q_dtype, cache_dtype, plan.P, workspace, workspace_bytes, stream,
+                               true, num_query_tokens);
   if (s.status != PKV_OK || s.empty) return s.status;
-  if (!decode_mfma_supported(s.a)) return PKV_ERR_SHAPE;
-  const pkv_status_t st = hip_status(launch_decode_mfma(s.a));
+  pkv_status_t st;
+  if (plan.tiled) {
+    if (!prefill_mfma_supported(s.a)) return PKV_ERR_SHAPE;
+    st = hip_status(launch_prefill_mfma(s.a));
+  } else {
+    if (!decode_mfma_supported(s.a)) return PKV_ERR_SHAPE;
+    st = hip_status(launch_decode_mfma(s.a));
+  }
   if (st != PKV_OK || s.a.NP <= 1) return st;
   return hip_status(launch_decode_reduce(s.a));
 }
@@ -331,12 +389,12 @@ size_t paged_attention_prefill_workspace_size(int32_t num_seqs, int32_t num_quer
                                               int32_t head_size, int32_t block_size,
                                               int32_t max_context_len, int32_t q_dtype,
                                               int32_t cache_dtype, int32_t partition_size) {
-  if (num_query_tokens <= 0) return 0;
-  const int P = paged_attention_decode_partition_size(num_seqs, num_heads, num_kv_heads,
-                                                      head_size, block_size, max_context_len,
-                                                      q_dtype, cache_dtype, partition_size);
-  if (P <= 0) return 0;
-  return decode_workspace(num_seqs, num_heads, head_size, max_context_len, P, num_query_tokens);
+  const PrefillPlan plan = prefill_plan(num_seqs, num_query_tokens, num_heads, num_kv_heads,
+                                        head_size, block_size, max_context_len, q_dtype,
+                                        cache_dtype, partition_size);
+  if (plan.P <= 0) return 0;
+  return decode_workspace(num_seqs, num_heads, head_size, max_context_len, plan.P,
+                          num_query_tokens);
 }
 
 }  // extern "C"

@@ -71,4 +71,12 @@ bool decode_mfma_supported(const DecodeArgs& a);
 hipError_t launch_decode_mfma(const DecodeArgs& a);
 hipError_t launch_decode_reduce(const DecodeArgs& a);
 
+// Tiled multi-token kernel (long prefill chunks, bf16 cache): a workgroup
+// owns prefill_tile_rows() rows of one KV head and stages one partition's
+// block ids in LDS, at most kPrefillMaxTable of them.
+constexpr int kPrefillMaxTable = 1024;
+int prefill_tile_rows();
+bool prefill_mfma_supported(const DecodeArgs& a);
+hipError_t launch_prefill_mfma(const DecodeArgs& a);
+
 }  // namespace pkv

@@ -1,0 +1,499 @@
+// Multi-token paged attention for long prefill chunks on gfx950 matrix cores.
+//
+// Each query token of a chunk is a decode step over the positions up to its
+// own (PagedAttention article on dpshk.com, section 2.2, applied per token;
+// new requests join the running batch and their prompts attend over the same
+// paged cache: page "PagedAttention 与连续批处理…", continuous-batching
+// section).  With many tokens per sequence the work is a dense contraction,
+// so this kernel is built for the matrix cores rather than for HBM:
+//
+//   * rows of a KV head are the (token, head) pairs m * G + g of its G query
+//     heads; a workgroup owns a tile of 128 rows, each of its 4 waves 32 rows
+//     (two 16-row MFMA groups that share every K and V fragment read);
+//   * the workgroup walks its keys in chunks of 64: K and V rows are gathered
+//     through the block table straight into LDS by global_load_lds (no
+//     register staging), double-buffered so chunk c+1 streams in while chunk
+//     c is multiplied;
+//   * S^T = K . Q^T and O^T += V^T . P^T on v_mfma_f32_16x16x32_bf16, with
+//     the online softmax between them in registers (the decode kernel's
+//     formulation: a lane holds one row, so row reductions are two swizzles);
+//   * LDS rows are XOR-swizzled in 16-byte pieces so the K fragment reads
+//     (ds_read_b128) and the V transposed reads (ds_read_b64_tr_b16) are free
+//     of bank conflicts without padding, which the DMA cannot insert.
+//
+// A tile needs only the keys below its last row's position; rows of earlier
+// tokens mask the newest keys of the last chunks.  Long contexts may be split
+// into partitions whose partials (running max in base-2 units, sum, and
+// unnormalised output) the split reduce merges per (token, head); a
+// sequence that fits one partition is finished here.
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_v;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_v;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_v;
+typedef __attribute__((address_space(3))) i16x4_v lds_i16x4_v;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kBM = 128;        // rows per workgroup tile
+constexpr int kWaves = 4;       // 32 rows per wave
+constexpr int kKC = 64;         // keys per LDS chunk
+constexpr float kMaxInit = -1e30f;  // running max before any key (finite: no inf - inf)
+
+struct PrefillParams {
+  const uint16_t* q;   // [S][M][H][D] bf16
+  uint16_t* out;       // [S][M][H][D] bf16
+  const uint16_t* kc;  // [num_blocks][H_kv][BS][D] bf16
+  const uint16_t* vc;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* ws_m;  // [S][M][H][NP] when NP > 1
+  float* ws_l;
+  float* ws_acc;  // [S][M][H][NP][D]
+  int M, H, H_kv, G, max_blocks, P, NP;
+  int RT;       // row tiles per KV head: ceil(M * G / kBM)
+  int total;    // workgroups with work: S * H_kv * NP * RT
+  int per_xcd;  // ceil(total / 8)
+  float scale_log2;
+};
+
+__device__ __forceinline__ bf16x8_v to_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_v, v); }
+
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// s_waitcnt with vmcnt(N) and lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8), then a workgroup barrier.  The compiler
+// barriers keep memory operations on their side; no fence is used, because a
+// workgroup release fence waits for every LDS DMA in flight, the next
+// chunk's included.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 32-bit LDS address of a shared-memory object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
+}
+
+// Inside the chunk loop every LDS read is inline assembly that ends with its
+// own wait.  The compiler cannot tell which LDS bytes a DMA in flight will
+// write, so before any LDS read it can see it would wait for all of them,
+// the next chunk's included, and the copy would no longer overlap the
+// products.  The chunk data itself is ordered by the explicit waits and
+// barriers of wait_vm_barrier.
+
+// NKC 16-byte K fragment reads at the lane's addresses + OFF.
+template <int OFF>
+__device__ __forceinline__ void lds_read_k(uint4 (&a)[4], const uint32_t (&ad)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n"
+      "ds_read_b128 %1, %5 offset:%8\n"
+      "ds_read_b128 %2, %6 offset:%8\n"
+      "ds_read_b128 %3, %7 offset:%8\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_read_k(uint4 (&a)[2], const uint32_t (&ad)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %2 offset:%4\n"
+      "ds_read_b128 %1, %3 offset:%4\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1])
+      : "v"(ad[0]), "v"(ad[1]), "i"(OFF));
+}
+
+// Four transposing reads (ds_read_b64_tr_b16) at the lane's address + OFF
+// + {0, 1, 2, 3} * STEP: both 16-key halves of both 32-key halves of a chunk
+// for one 16-wide d tile.
+template <int OFF, int STEP>
+__device__ __forceinline__ void lds_read_v(uint2 (&v)[4], uint32_t ad) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%5\n"
+      "ds_read_b64_tr_b16 %1, %4 offset:%6\n"
+      "ds_read_b64_tr_b16 %2, %4 offset:%7\n"
+      "ds_read_b64_tr_b16 %3, %4 offset:%8\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(ad), "i"(OFF), "i"(OFF + STEP), "i"(OFF + 2 * STEP), "i"(OFF + 3 * STEP));
+}
+
+// Block ids of a chunk's DMA rounds from the LDS table slice.
+__device__ __forceinline__ void lds_read_tab(int (&v)[4], const uint32_t (&ad)[4]) {
+  asm volatile(
+      "ds_read_b32 %0, %4\n"
+      "ds_read_b32 %1, %5\n"
+      "ds_read_b32 %2, %6\n"
+      "ds_read_b32 %3, %7\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]));
+}
+__device__ __forceinline__ void lds_read_tab(int (&v)[2], const uint32_t (&ad)[2]) {
+  asm volatile(
+      "ds_read_b32 %0, %2\n"
+      "ds_read_b32 %1, %3\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1])
+      : "v"(ad[0]), "v"(ad[1]));
+}
+
+template <int D>
+struct Layout {
+  static constexpr int PR = D / 8;                  // 16-byte pieces per row
+  static constexpr int RB = 256 / (2 * D);          // rows per 256 bytes
+  static constexpr int ROW = 2 * D;                 // bytes per row
+  static constexpr int TILE = kKC * ROW;            // bytes of a K or V chunk
+  static constexpr int CHUNK = 2 * TILE;            // K tile then V tile
+  static constexpr int ROUNDS = kKC * PR / 256;     // DMA rounds per chunk (4 or 2)
+  static constexpr int RPI = 64 / PR;               // rows per wave DMA instruction
+  static constexpr int NKC = D / 32;                // k-steps of the score products
+  static constexpr int NMD = D / 16;                // 16-wide d tiles of O^T
+  // Physical 16-byte piece of logical piece p in row k: XOR with bits of the
+  // row's 256-byte line, so 16 consecutive rows (K reads) and the 16 rows of
+  // a transposed read spread over all banks.  Rows k, k + 16 and k + 32
+  // share the pattern.
+  __device__ static __forceinline__ int swz(int k) { return (k / RB) & (PR - 1); }
+  __device__ static __forceinline__ int phys(int k, int p) { return p ^ swz(k); }
+};
+
+// Gathers keys c0 .. c0 + kKC - 1 of KV head kvh into buffer `buf` (K and V
+// tiles).  Wave w, round i fills bytes [(4 i + w) KiB, +1 KiB) of each tile,
+// lane l the physical piece 64 (4 i + w) + l, and fetches the logical piece
+// that the swizzle stores there.  One round covers RPI <= 8 rows of one
+// cache block, so its block id is one table entry.  Keys at or past kend
+// are read as key kend - 1 (a real row of the same block; masked later).
+template <int D, int BS>
+__device__ __forceinline__ void issue_chunk(char* buf, const PrefillParams& p, uint32_t tab,
+                                            int elast, int kvh, int start, int c0, int kend,
+                                            int wave, int lane) {
+  using L = Layout<D>;
+  int blk[L::ROUNDS];
+  uint32_t ta[L::ROUNDS];
+  const int cidx = (c0 - start) / BS;
+#pragma unroll
+  for (int i = 0; i < L::ROUNDS; ++i)
+    ta[i] = tab + 4 * min(cidx + (L::RPI * (i * kWaves + wave)) / BS, elast);
+  lds_read_tab(blk, ta);
+#pragma unroll
+  for (int i = 0; i < L::ROUNDS; ++i) {
+    const int k = L::RPI * (i * kWaves + wave) + lane / L::PR;
+    const int piece = L::phys(k, lane % L::PR);  // XOR is its own inverse
+    const int t = min(c0 + k, kend - 1);
+    const size_t row = ((size_t)blk[i] * p.H_kv + kvh) * BS + (t % BS);
+    const size_t off = row * D + 8 * piece;
+    const int lds = (i * kWaves + wave) * 1024;
+    __builtin_amdgcn_global_load_lds(p.kc + off, (lds_void*)(buf + lds), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(p.vc + off, (lds_void*)(buf + L::TILE + lds), 16, 0, 0);
+  }
+}
+
+// One chunk from buffer SEL: scores of both row groups, online softmax,
+// O^T update.  kad: the lane's K fragment addresses in buffer 0 (key r,
+// logical pieces (D/32) q4 + c); vad: the lane's V address in buffer 0 for
+// d tile 0, XORed with 32 md for tile md.  e[j]: keys below it are visible
+// to this lane's row of group j; full[j] (uniform): no mask for group j.
+template <int D, int SEL>
+__device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uint32_t vad,
+                                              const uint4 (&qf)[2][D / 32],
+                                              f32x4_v (&acc)[2][D / 16], float (&m)[2],
+                                              float (&l)[2], const int (&e)[2],
+                                              const bool (&full)[2], int c0, float sl,
+                                              int lane) {
+  using L = Layout<D>;
+  constexpr int KOFF = SEL * L::CHUNK;
+  const int q4 = lane >> 4;
+  f32x4_v s[2][4];
+  // S^T = K . Q^T, 16 keys per tile T: lane (q4, r) holds key 16 T + r,
+  // contraction elements (D/4) q4 + 8 c .. + 7 (the Q fragments use the same
+  // order).  The swizzle of row 16 T + r does not depend on T.
+#define PKV_SCORE_TILE(T)                                                                     \
+  {                                                                                           \
+    uint4 a[L::NKC];                                                                          \
+    lds_read_k<KOFF + (T) * 16 * L::ROW>(a, kad);                                             \
+    s[0][T] = f32x4_v{0.f, 0.f, 0.f, 0.f};                                                    \
+    s[1][T] = f32x4_v{0.f, 0.f, 0.f, 0.f};                                                    \
+    _Pragma("unroll") for (int c = 0; c < L::NKC; ++c) {                                      \
+      s[0][T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(a[c]), to_bf16x8(qf[0][c]), \
+                                                         s[0][T], 0, 0, 0);                   \
+      s[1][T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(a[c]), to_bf16x8(qf[1][c]), \
+                                                         s[1][T], 0, 0, 0);                   \
+    }                                                                                         \
+  }
+  PKV_SCORE_TILE(0)
+  PKV_SCORE_TILE(1)
+  PKV_SCORE_TILE(2)
+  PKV_SCORE_TILE(3)
+#undef PKV_SCORE_TILE
+  // Online softmax per group: lane (q4, r) holds row r, keys 16 T + 4 q4 + i.
+  uint4 pb[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float x[4][4];
+    float mc = kNegInf;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = full[j] || (c0 + 16 * T + 4 * q4 + i < e[j]);
+        x[T][i] = ok ? s[j][T][i] * sl : kNegInf;
+        mc = fmaxf(mc, x[T][i]);
+      }
+    }
+    mc = fmaxf(mc, __shfl_xor(mc, 16));
+    mc = fmaxf(mc, __shfl_xor(mc, 32));
+    const float m_new = fmaxf(m[j], mc);
+    const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
+    m[j] = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[T][i] = __builtin_amdgcn_exp2f(x[T][i] - m_new);
+        ps += x[T][i];
+      }
+    }
+    l[j] = fmaf(l[j], alpha, ps);
+#pragma unroll
+    for (int md = 0; md < L::NMD; ++md) acc[j][md] *= alpha;
+    // P^T operand of keys 32 u + {4 q4 .. 4 q4 + 3, 16 + 4 q4 .. 16 + 4 q4 + 3}
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      pb[j][u] = make_uint4(bf16x2_rne(x[2 * u][0], x[2 * u][1]),
+                            bf16x2_rne(x[2 * u][2], x[2 * u][3]),
+                            bf16x2_rne(x[2 * u + 1][0], x[2 * u + 1][1]),
+                            bf16x2_rne(x[2 * u + 1][2], x[2 * u + 1][3]));
+    }
+  }
+  // O^T += V^T . P^T.  Transposed reads: lane (q4, r) addresses key
+  // 32 u + 4 q4 + r / 4 (and + 16) at d = 16 md + 4 (r % 4) and receives
+  // V[those 4 keys][16 md + r]; v[2u] / v[2u+1] are the two 16-key halves.
+  constexpr int VOFF = SEL * L::CHUNK + L::TILE;
+#pragma unroll
+  for (int md = 0; md < L::NMD; ++md) {
+    uint2 v[4];
+    lds_read_v<VOFF, 16 * L::ROW>(v, vad ^ (32u * md));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8_v va = to_bf16x8(make_uint4(v[2 * u].x, v[2 * u].y, v[2 * u + 1].x,
+                                               v[2 * u + 1].y));
+      acc[0][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, to_bf16x8(pb[0][u]), acc[0][md],
+                                                            0, 0, 0);
+      acc[1][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, to_bf16x8(pb[1][u]), acc[1][md],
+                                                            0, 0, 0);
+    }
+  }
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillParams p) {
+  using L = Layout<D>;
+  __shared__ int s_tab[kPrefillMaxTable];
+  __shared__ __attribute__((aligned(1024))) char s_buf[2 * L::CHUNK];
+
+  // Workgroup b runs on XCD b % 8; each XCD takes a contiguous range of
+  // tiles, so the row tiles of one (sequence, KV head, partition) share that
+  // XCD's L2.  Within it the tiles of later tokens (more keys) go first.
+  const int b = blockIdx.x;
+  const int lin = (b & 7) * p.per_xcd + (b >> 3);
+  if (lin >= p.total) return;
+  const int unit = lin / p.RT;
+  const int rt = p.RT - 1 - (lin - unit * p.RT);
+  const int part = unit % p.NP;
+  const int sk = unit / p.NP;
+  const int seq = sk / p.H_kv;
+  const int kvh = sk - seq * p.H_kv;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q4 = lane >> 4, r = lane & 15;
+  const int n = p.lens[seq];
+  const int MG = p.M * p.G;
+  const int r0 = rt * kBM;
+  const int rlast = min(r0 + kBM, MG) - 1;
+  const int base = n - p.M + 1;  // keys below base + m: visible to token m
+  const int start = part * p.P;
+  const int pend = min(n, start + p.P);
+  const int kend = min(pend, base + rlast / p.G);
+  const bool single = n <= p.P;
+  const int nch = kend > start ? (kend - start + kKC - 1) / kKC : 0;
+  if (nch == 0 && !single) return;  // no row of the tile sees this partition
+
+  const int t0 = start / BS;
+  const int elast = nch > 0 ? (kend - 1) / BS - t0 : 0;  // last table entry used
+  if (nch > 0) {
+    const int32_t* trow = p.tables + (size_t)seq * p.max_blocks + t0;
+    for (int i = tid; i <= elast; i += kWaves * 64) s_tab[i] = trow[i];
+  }
+
+  // This lane's rows (one per group) and their query fragments.
+  uint4 qf[2][L::NKC];
+  int e[2];
+  size_t orow[2];
+  bool live[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rho = r0 + 32 * wave + 16 * j + r;
+    live[j] = rho <= rlast;
+    const int rc = min(rho, rlast);
+    const int m = rc / p.G;
+    orow[j] = ((size_t)seq * p.M + m) * p.H + (size_t)kvh * p.G + (rc - m * p.G);
+    const uint16_t* qrow = p.q + orow[j] * D + (D / 4) * q4;
+#pragma unroll
+    for (int c = 0; c < L::NKC; ++c) qf[j][c] = *reinterpret_cast<const uint4*>(qrow + 8 * c);
+    e[j] = min(pend, base + rc / p.G);
+  }
+  // Uniform per group: a group's first row has the smallest end.
+  const int gfull0 = min(pend, base + min(r0 + 32 * wave, rlast) / p.G);
+  const int gfull1 = min(pend, base + min(r0 + 32 * wave + 16, rlast) / p.G);
+
+  // LDS addresses (buffer 0; buffer 1 and the V tile are immediate offsets).
+  const uint32_t buf0 = lds_addr(s_buf);
+  const uint32_t tab = lds_addr(s_tab);
+  uint32_t kad[L::NKC];
+#pragma unroll
+  for (int c = 0; c < L::NKC; ++c)
+    kad[c] = buf0 + r * L::ROW + 16 * L::phys(r, (D / 32) * q4 + c);
+  uint32_t vad;
+  {
+    const int k0 = 4 * q4 + (r >> 2);
+    const int sw = L::swz(k0);
+    const int bb = ((r & 3) >> 1) ^ (sw & 1);  // low bit of the physical piece
+    // piece (2 md + (r&3)/2) ^ sw = 2 (md ^ (sw/2)) + bb: bits 5.. of the
+    // address hold md ^ (sw / 2), which the loop XORs with md
+    vad = (buf0 + k0 * L::ROW + 8 * (r & 1) + 16 * bb) | (32u * (sw >> 1));
+  }
+
+  f32x4_v acc[2][L::NMD];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int md = 0; md < L::NMD; ++md) acc[j][md] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {kMaxInit, kMaxInit}, l[2] = {0.f, 0.f};
+
+  __syncthreads();  // the table slice is in LDS
+  if (nch > 0)
+    issue_chunk<D, BS>(s_buf, p, tab, elast, kvh, start, start, kend, wave, lane);
+  for (int ch = 0; ch < nch; ch += 2) {
+    {  // even chunk, buffer 0
+      const int c0 = start + ch * kKC;
+      if (ch + 1 < nch) {
+        issue_chunk<D, BS>(s_buf + L::CHUNK, p, tab, elast, kvh, start, c0 + kKC, kend, wave,
+                           lane);
+        wait_vm_barrier<2 * L::ROUNDS>();
+      } else {
+        wait_vm_barrier<0>();
+      }
+      const bool full[2] = {c0 + kKC <= gfull0, c0 + kKC <= gfull1};
+      compute_chunk<D, 0>(kad, vad, qf, acc, m, l, e, full, c0, p.scale_log2, lane);
+      wait_vm_barrier<63>();  // every wave is done with buffer 0
+    }
+    if (ch + 1 < nch) {  // odd chunk, buffer 1
+      const int c0 = start + (ch + 1) * kKC;
+      if (ch + 2 < nch) {
+        issue_chunk<D, BS>(s_buf, p, tab, elast, kvh, start, c0 + kKC, kend, wave, lane);
+        wait_vm_barrier<2 * L::ROUNDS>();
+      } else {
+        wait_vm_barrier<0>();
+      }
+      const bool full[2] = {c0 + kKC <= gfull0, c0 + kKC <= gfull1};
+      compute_chunk<D, 1>(kad, vad, qf, acc, m, l, e, full, c0, p.scale_log2, lane);
+      wait_vm_barrier<63>();  // every wave is done with buffer 1
+    }
+  }
+
+  // Each lane summed its own keys of the row: add the four lanes of a row.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    l[j] += __shfl_xor(l[j], 16);
+    l[j] += __shfl_xor(l[j], 32);
+  }
+  // Lane (q4, r) of group j holds O^T[16 md + 4 q4 + i][row r].
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (!live[j]) continue;
+    if (single) {
+      const float inv = l[j] > 0.f ? 1.f / l[j] : 0.f;
+      uint16_t* o = p.out + orow[j] * D + 4 * q4;
+#pragma unroll
+      for (int md = 0; md < L::NMD; ++md) {
+        const f32x4_v a = acc[j][md];
+        *reinterpret_cast<uint2*>(o + 16 * md) =
+            make_uint2(bf16x2_rne(a[0] * inv, a[1] * inv), bf16x2_rne(a[2] * inv, a[3] * inv));
+      }
+    } else {
+      const size_t pi = orow[j] * p.NP + part;
+      float* o = p.ws_acc + pi * D + 4 * q4;
+#pragma unroll
+      for (int md = 0; md < L::NMD; ++md)
+        __builtin_nontemporal_store(acc[j][md], reinterpret_cast<f32x4_v*>(o + 16 * md));
+      if (q4 == 0) {
+        p.ws_m[pi] = m[j];
+        p.ws_l[pi] = l[j];
+      }
+    }
+  }
+}
+
+template <int D, int BS>
+hipError_t launch_db(const DecodeArgs& a) {
+  PrefillParams p;
+  p.q = reinterpret_cast<const uint16_t*>(a.q);
+  p.out = reinterpret_cast<uint16_t*>(a.out);
+  p.kc = reinterpret_cast<const uint16_t*>(a.key_cache);
+  p.vc = reinterpret_cast<const uint16_t*>(a.value_cache);
+  p.tables = a.tables;
+  p.lens = a.lens;
+  p.ws_m = a.ws_m; p.ws_l = a.ws_l; p.ws_acc = a.ws_acc;
+  p.M = a.M; p.H = a.H; p.H_kv = a.H_kv; p.G = a.H / a.H_kv;
+  p.max_blocks = a.max_blocks; p.P = a.P; p.NP = a.NP;
+  p.RT = (a.M * p.G + kBM - 1) / kBM;
+  const long long total = (long long)a.S * a.H_kv * a.NP * p.RT;
+  p.total = (int)total;
+  p.per_xcd = (int)((total + 7) / 8);
+  p.scale_log2 = a.scale * kLog2e;
+  const unsigned grid = (unsigned)(8LL * p.per_xcd);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, BS>), dim3(grid), dim3(kWaves * 64), 0, a.stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a) {
+  switch (a.bs) {
+    case 8: return launch_db<D, 8>(a);
+    case 16: return launch_db<D, 16>(a);
+    case 32: return launch_db<D, 32>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int prefill_tile_rows() { return kBM; }
+
+bool prefill_mfma_supported(const DecodeArgs& a) {
+  return a.q_dtype == PKV_BF16 && a.cache_dtype == PKV_BF16 && (a.D == 64 || a.D == 128) &&
+         (a.P + a.bs - 1) / a.bs + 1 <= kPrefillMaxTable;
+}
+
+hipError_t launch_prefill_mfma(const DecodeArgs& a) {
+  if (a.S == 0) return hipSuccess;
+  return a.D == 128 ? launch_d<128>(a) : launch_d<64>(a);
+}
+
+}  // namespace pkv

@@ -69,6 +69,38 @@ def test_random_shapes(seed):
     assert err <= TOL[cache], err
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_tiled_shapes(seed):
+    """bf16 caches with at least 64 (token, head) rows per KV head: the tiled
+    kernel, over whole contexts and over explicit partitions (split reduce),
+    several row tiles with a ragged last one, and chunks that are the whole
+    sequence (the causal triangle)."""
+    rng = np.random.default_rng(900 + seed)
+    D = [128, 64][seed % 2]
+    bs = [16, 8, 32][seed % 3]
+    H_kv = int(rng.integers(1, 3))
+    G = int(rng.choice([1, 2, 4, 8]))
+    M = int(rng.choice([64, 100, 200])) if G == 1 else int(rng.choice([16, 33, 70, 130]))
+    S = int(rng.integers(1, 4))
+    lens = rng.integers(M, M + 900, size=S)
+    if seed % 4 == 1:
+        lens[:] = M                        # prompt processed from scratch
+    ps = [0, 0, 64, 256, 4 * bs, 192][seed % 6]
+    ps = ps - ps % bs
+    w = workloads.build_workload(f"tiled{seed}", S, H_kv * G, H_kv, D, bs, "bf16", "bf16", lens,
+                                 seed, query_tokens=M)
+    _say(f"case tiled{seed} D={D} bs={bs} H_kv={H_kv} G={G} M={M} lens={list(lens)} ps={ps}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle.paged_attention_prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                         bs, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    out = _prefill(dw, ps)
+    err = max_err(out_f64(out), ref)
+    _say(f"  max_err={err:.3e}")
+    assert err <= TOL["bf16"], err
+
+
 def test_one_query_token_is_decode():
     w = workloads.make_config(2, reduced=True)
     _say(f"case prefill M=1 vs decode {w.name}")

@@ -269,6 +269,26 @@ def make_config(cfg: int, reduced: bool = False, seed: Optional[int] = None,
     raise ValueError(cfg)
 
 
+PREFILL_CONFIGS = {
+    # name: (S, M, H, H_kv, D, bs, cache, context length per sequence)
+    "prefill-chunk-gqa-bf16": (4, 512, 32, 8, 128, 16, "bf16", 4096),
+    "prefill-chunk-mha-bf16": (4, 512, 32, 32, 128, 16, "bf16", 4096),
+}
+
+
+def make_prefill(name: str, reduced: bool = False, seed: int = 31) -> Workload:
+    """A chunked-prefill step: each sequence's newest M tokens are the chunk
+    (written by the step, then attending causally to all positions before
+    them).  reduced=True shrinks the context and chunk for the oracle."""
+    S, M, H, H_kv, D, bs, cache, n = PREFILL_CONFIGS[name]
+    if reduced:
+        S, M, n = 2, 40, 300
+    lens = np.full(S, n)
+    return build_workload(name + ("-reduced" if reduced else ""), S, H, H_kv, D, bs, "bf16",
+                          cache, lens, seed, free_frac=0.05,
+                          fill="write" if cache == "fp8" else "random", query_tokens=M)
+
+
 def duplicate_shared_blocks(w: Workload) -> Workload:
     """Twin of a shared-prefix workload: each sequence gets private copies of
     the shared blocks (same bytes), appended to the pool."""
