@@ -17,9 +17,13 @@
 //   * S^T = K . Q^T and O^T += V^T . P^T on v_mfma_f32_16x16x32_bf16, with
 //     the online softmax between them in registers (the decode kernel's
 //     formulation: a lane holds one row, so row reductions are two swizzles);
-//   * LDS rows are XOR-swizzled in 16-byte pieces so the K fragment reads
-//     (ds_read_b128) and the V transposed reads (ds_read_b64_tr_b16) are free
-//     of bank conflicts without padding, which the DMA cannot insert.
+//   * LDS rows are XOR-swizzled (K in 16-byte pieces, V in 32-byte halves of
+//     them) so the K fragment reads (ds_read_b128) and the V transposed reads
+//     (ds_read_b64_tr_b16) are free of bank conflicts without padding, which
+//     the DMA cannot insert;
+//   * row maxima and sums cross lanes with the gfx950 permlane swaps, and
+//     the accumulators are rescaled only when a row maximum grows by more
+//     than 2^8.
 //
 // A tile needs only the keys below its last row's position; rows of earlier
 // tokens mask the newest keys of the last chunks.  Long contexts may be split
@@ -118,21 +122,6 @@ __device__ __forceinline__ void lds_read_k(uint4 (&a)[2], const uint32_t (&ad)[2
       : "v"(ad[0]), "v"(ad[1]), "i"(OFF));
 }
 
-// Four transposing reads (ds_read_b64_tr_b16) at the lane's address + OFF
-// + {0, 1, 2, 3} * STEP: both 16-key halves of both 32-key halves of a chunk
-// for one 16-wide d tile.
-template <int OFF, int STEP>
-__device__ __forceinline__ void lds_read_v(uint2 (&v)[4], uint32_t ad) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4 offset:%5\n"
-      "ds_read_b64_tr_b16 %1, %4 offset:%6\n"
-      "ds_read_b64_tr_b16 %2, %4 offset:%7\n"
-      "ds_read_b64_tr_b16 %3, %4 offset:%8\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-      : "v"(ad), "i"(OFF), "i"(OFF + STEP), "i"(OFF + 2 * STEP), "i"(OFF + 3 * STEP));
-}
-
 // Block ids of a chunk's DMA rounds from the LDS table slice.
 __device__ __forceinline__ void lds_read_tab(int (&v)[4], const uint32_t (&ad)[4]) {
   asm volatile(
@@ -153,6 +142,47 @@ __device__ __forceinline__ void lds_read_tab(int (&v)[2], const uint32_t (&ad)[2
       : "v"(ad[0]), "v"(ad[1]));
 }
 
+// Eight transposing reads (ds_read_b64_tr_b16) for two 16-wide d tiles: at
+// each of the lane's two addresses + OFF + {0, 1, 2, 3} * STEP, the 16-key
+// quarters of a 64-key chunk.
+template <int OFF, int STEP>
+__device__ __forceinline__ void lds_read_v(uint2 (&v)[8], uint32_t ad0, uint32_t ad1) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%10\n"
+      "ds_read_b64_tr_b16 %1, %8 offset:%11\n"
+      "ds_read_b64_tr_b16 %2, %8 offset:%12\n"
+      "ds_read_b64_tr_b16 %3, %8 offset:%13\n"
+      "ds_read_b64_tr_b16 %4, %9 offset:%10\n"
+      "ds_read_b64_tr_b16 %5, %9 offset:%11\n"
+      "ds_read_b64_tr_b16 %6, %9 offset:%12\n"
+      "ds_read_b64_tr_b16 %7, %9 offset:%13\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7])
+      : "v"(ad0), "v"(ad1), "i"(OFF), "i"(OFF + STEP), "i"(OFF + 2 * STEP), "i"(OFF + 3 * STEP));
+}
+
+// Maximum / sum over the four lanes of a row (l, l^16, l^32, l^48) with the
+// gfx950 lane swaps (no LDS round trip).
+__device__ __forceinline__ float max4_rows(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4_rows(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// v_max3_f32 (the compiler does not form it from fmaxf).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 template <int D>
 struct Layout {
   static constexpr int PR = D / 8;                  // 16-byte pieces per row
@@ -170,6 +200,9 @@ struct Layout {
   // share the pattern.
   __device__ static __forceinline__ int swz(int k) { return (k / RB) & (PR - 1); }
   __device__ static __forceinline__ int phys(int k, int p) { return p ^ swz(k); }
+  // V tile: XOR of the 32-byte half-piece index, so the 4 rows of a
+  // transposed read group (and 8 consecutive rows) sit in distinct banks.
+  __device__ static __forceinline__ int vswz(int k) { return 2 * ((k / RB) & (PR / 2 - 1)); }
 };
 
 // Gathers keys c0 .. c0 + kKC - 1 of KV head kvh into buffer `buf` (K and V
@@ -193,13 +226,14 @@ __device__ __forceinline__ void issue_chunk(char* buf, const PrefillParams& p, u
 #pragma unroll
   for (int i = 0; i < L::ROUNDS; ++i) {
     const int k = L::RPI * (i * kWaves + wave) + lane / L::PR;
-    const int piece = L::phys(k, lane % L::PR);  // XOR is its own inverse
+    const int pp = lane % L::PR;
     const int t = min(c0 + k, kend - 1);
     const size_t row = ((size_t)blk[i] * p.H_kv + kvh) * BS + (t % BS);
-    const size_t off = row * D + 8 * piece;
+    const size_t offk = row * D + 8 * (pp ^ L::swz(k));  // XOR is its own inverse
+    const size_t offv = row * D + 8 * (pp ^ L::vswz(k));
     const int lds = (i * kWaves + wave) * 1024;
-    __builtin_amdgcn_global_load_lds(p.kc + off, (lds_void*)(buf + lds), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(p.vc + off, (lds_void*)(buf + L::TILE + lds), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(p.kc + offk, (lds_void*)(buf + lds), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(p.vc + offv, (lds_void*)(buf + L::TILE + lds), 16, 0, 0);
   }
 }
 
@@ -240,39 +274,53 @@ __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uin
   PKV_SCORE_TILE(2)
   PKV_SCORE_TILE(3)
 #undef PKV_SCORE_TILE
-  // Online softmax per group: lane (q4, r) holds row r, keys 16 T + 4 q4 + i.
+  // Online softmax per group: lane (q4, r) holds row r, keys 16 T + 4 q4 + i
+  // (scores in raw units; sl > 0 turns them into base-2 logits).  The
+  // running maximum m moves only when a row's chunk maximum exceeds it by
+  // more than 8 (wave-uniform test), so most chunks skip the rescale of the
+  // accumulators; the exponents stay below 2^8, and acc and l always share
+  // one reference, so the normalised result is unchanged.
   uint4 pb[2][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    float x[4][4];
     float mc = kNegInf;
+    if (!full[j]) {
 #pragma unroll
-    for (int T = 0; T < 4; ++T) {
+      for (int T = 0; T < 4; ++T)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = full[j] || (c0 + 16 * T + 4 * q4 + i < e[j]);
-        x[T][i] = ok ? s[j][T][i] * sl : kNegInf;
-        mc = fmaxf(mc, x[T][i]);
-      }
+        for (int i = 0; i < 4; ++i)
+          if (!(c0 + 16 * T + 4 * q4 + i < e[j])) s[j][T][i] = kNegInf;
     }
-    mc = fmaxf(mc, __shfl_xor(mc, 16));
-    mc = fmaxf(mc, __shfl_xor(mc, 32));
-    const float m_new = fmaxf(m[j], mc);
-    const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
-    m[j] = m_new;
+    {
+      float t0 = max3f(s[j][0][0], s[j][0][1], s[j][0][2]);
+      float t1 = max3f(s[j][0][3], s[j][1][0], s[j][1][1]);
+      float t2 = max3f(s[j][1][2], s[j][1][3], s[j][2][0]);
+      float t3 = max3f(s[j][2][1], s[j][2][2], s[j][2][3]);
+      float t4 = max3f(s[j][3][0], s[j][3][1], s[j][3][2]);
+      t0 = max3f(t0, t1, t2);
+      t3 = max3f(t3, t4, s[j][3][3]);
+      mc = max4_rows(__builtin_fmaxf(t0, t3));
+    }
+    const float mcs = mc * sl;
+    if (__any(mcs > m[j] + 8.f)) {
+      const float m_new = fmaxf(m[j], mcs);
+      const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
+      m[j] = m_new;
+      l[j] *= alpha;
+#pragma unroll
+      for (int md = 0; md < L::NMD; ++md) acc[j][md] *= alpha;
+    }
     float ps = 0.f;
+    float x[4][4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[T][i] = __builtin_amdgcn_exp2f(x[T][i] - m_new);
+        x[T][i] = __builtin_amdgcn_exp2f(fmaf(s[j][T][i], sl, -m[j]));
         ps += x[T][i];
       }
     }
-    l[j] = fmaf(l[j], alpha, ps);
-#pragma unroll
-    for (int md = 0; md < L::NMD; ++md) acc[j][md] *= alpha;
-    // P^T operand of keys 32 u + {4 q4 .. 4 q4 + 3, 16 + 4 q4 .. 16 + 4 q4 + 3}
+    l[j] += ps;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       pb[j][u] = make_uint4(bf16x2_rne(x[2 * u][0], x[2 * u][1]),
@@ -283,20 +331,24 @@ __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uin
   }
   // O^T += V^T . P^T.  Transposed reads: lane (q4, r) addresses key
   // 32 u + 4 q4 + r / 4 (and + 16) at d = 16 md + 4 (r % 4) and receives
-  // V[those 4 keys][16 md + r]; v[2u] / v[2u+1] are the two 16-key halves.
+  // V[those 4 keys][16 md + r]; v[4h + 2u] / v[4h + 2u + 1] are the two
+  // 16-key halves of 32-key half u for d tile md + h.
   constexpr int VOFF = SEL * L::CHUNK + L::TILE;
 #pragma unroll
-  for (int md = 0; md < L::NMD; ++md) {
-    uint2 v[4];
-    lds_read_v<VOFF, 16 * L::ROW>(v, vad ^ (32u * md));
+  for (int md = 0; md < L::NMD; md += 2) {
+    uint2 v[8];
+    lds_read_v<VOFF, 16 * L::ROW>(v, vad ^ (32u * md), vad ^ (32u * (md + 1)));
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const bf16x8_v va = to_bf16x8(make_uint4(v[2 * u].x, v[2 * u].y, v[2 * u + 1].x,
-                                               v[2 * u + 1].y));
-      acc[0][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, to_bf16x8(pb[0][u]), acc[0][md],
-                                                            0, 0, 0);
-      acc[1][md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, to_bf16x8(pb[1][u]), acc[1][md],
-                                                            0, 0, 0);
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint2 lo = v[4 * h + 2 * u], hi = v[4 * h + 2 * u + 1];
+        const bf16x8_v va = to_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        acc[0][md + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, to_bf16x8(pb[0][u]),
+                                                                  acc[0][md + h], 0, 0, 0);
+        acc[1][md + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, to_bf16x8(pb[1][u]),
+                                                                  acc[1][md + h], 0, 0, 0);
+      }
     }
   }
 }
@@ -355,9 +407,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
     orow[j] = ((size_t)seq * p.M + m) * p.H + (size_t)kvh * p.G + (rc - m * p.G);
     const uint16_t* qrow = p.q + orow[j] * D + (D / 4) * q4;
 #pragma unroll
-    for (int c = 0; c < L::NKC; ++c) qf[j][c] = *reinterpret_cast<const uint4*>(qrow + 8 * c);
+    for (int c = 0; c < L::NKC; ++c) {
+      qf[j][c] = *reinterpret_cast<const uint4*>(qrow + 8 * c);
+      if (p.scale_log2 < 0.f) {  // fold the scale's sign into Q (exact)
+        qf[j][c].x ^= 0x80008000u; qf[j][c].y ^= 0x80008000u;
+        qf[j][c].z ^= 0x80008000u; qf[j][c].w ^= 0x80008000u;
+      }
+    }
     e[j] = min(pend, base + rc / p.G);
   }
+  // Positive factor from raw scores to base-2 logits (a zero scale becomes a
+  // tiny positive one: every weight is then 1 up to rounding, as it should).
+  const float sl = fmaxf(fabsf(p.scale_log2), 1e-30f);
   // Uniform per group: a group's first row has the smallest end.
   const int gfull0 = min(pend, base + min(r0 + 32 * wave, rlast) / p.G);
   const int gfull1 = min(pend, base + min(r0 + 32 * wave + 16, rlast) / p.G);
@@ -372,11 +433,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
   uint32_t vad;
   {
     const int k0 = 4 * q4 + (r >> 2);
-    const int sw = L::swz(k0);
-    const int bb = ((r & 3) >> 1) ^ (sw & 1);  // low bit of the physical piece
-    // piece (2 md + (r&3)/2) ^ sw = 2 (md ^ (sw/2)) + bb: bits 5.. of the
-    // address hold md ^ (sw / 2), which the loop XORs with md
-    vad = (buf0 + k0 * L::ROW + 8 * (r & 1) + 16 * bb) | (32u * (sw >> 1));
+    const int sw = L::vswz(k0);
+    // piece (2 md + (r&3)/2) ^ sw = 2 (md ^ (sw/2)) + (r&3)/2: bits 5.. of
+    // the address hold md ^ (sw / 2), which the loop XORs with md
+    vad = (buf0 + k0 * L::ROW + 8 * (r & 1) + 16 * ((r & 3) >> 1)) | (32u * (sw >> 1));
   }
 
   f32x4_v acc[2][L::NMD];
@@ -400,7 +460,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
         wait_vm_barrier<0>();
       }
       const bool full[2] = {c0 + kKC <= gfull0, c0 + kKC <= gfull1};
-      compute_chunk<D, 0>(kad, vad, qf, acc, m, l, e, full, c0, p.scale_log2, lane);
+      compute_chunk<D, 0>(kad, vad, qf, acc, m, l, e, full, c0, sl, lane);
       wait_vm_barrier<63>();  // every wave is done with buffer 0
     }
     if (ch + 1 < nch) {  // odd chunk, buffer 1
@@ -412,7 +472,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
         wait_vm_barrier<0>();
       }
       const bool full[2] = {c0 + kKC <= gfull0, c0 + kKC <= gfull1};
-      compute_chunk<D, 1>(kad, vad, qf, acc, m, l, e, full, c0, p.scale_log2, lane);
+      compute_chunk<D, 1>(kad, vad, qf, acc, m, l, e, full, c0, sl, lane);
       wait_vm_barrier<63>();  // every wave is done with buffer 1
     }
   }
@@ -420,8 +480,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
   // Each lane summed its own keys of the row: add the four lanes of a row.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    l[j] += __shfl_xor(l[j], 16);
-    l[j] += __shfl_xor(l[j], 32);
+    l[j] = sum4_rows(l[j]);
   }
   // Lane (q4, r) of group j holds O^T[16 md + 4 q4 + i][row r].
 #pragma unroll

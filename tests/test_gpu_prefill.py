@@ -101,6 +101,26 @@ def test_tiled_shapes(seed):
     assert err <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 3.0])
+def test_tiled_scale_edge_cases(scale):
+    """Negative, zero and large softmax scales on the tiled kernel (a zero
+    scale weighs every visible position equally)."""
+    lens = [300, 170]
+    w = workloads.build_workload("tiled-scale", 2, 8, 2, 128, 16, "bf16", "bf16", lens, 5,
+                                 query_tokens=64)
+    w.scale = scale
+    _say(f"case tiled scale={scale}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle.paged_attention_prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                         16, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    for ps in (0, 128):
+        err = max_err(out_f64(_prefill(dw, ps)), ref)
+        _say(f"  ps={ps} max_err={err:.3e}")
+        assert err <= TOL["bf16"], (ps, err)
+
+
 def test_one_query_token_is_decode():
     w = workloads.make_config(2, reduced=True)
     _say(f"case prefill M=1 vs decode {w.name}")
