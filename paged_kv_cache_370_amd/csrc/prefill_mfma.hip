@@ -21,9 +21,10 @@
 //     them) so the K fragment reads (ds_read_b128) and the V transposed reads
 //     (ds_read_b64_tr_b16) are free of bank conflicts without padding, which
 //     the DMA cannot insert;
-//   * row maxima and sums cross lanes with the gfx950 permlane swaps, and
-//     the accumulators are rescaled only when a row maximum grows by more
-//     than 2^8.
+//   * row maxima cross lanes with the gfx950 permlane swaps, row sums come
+//     from the matrix cores (an all-ones tile times P^T), and the
+//     accumulators are rescaled only when a row maximum grows by more than
+//     2^8.
 //
 // A tile needs only the keys below its last row's position; rows of earlier
 // tokens mask the newest keys of the last chunks.  Long contexts may be split
@@ -162,19 +163,19 @@ __device__ __forceinline__ void lds_read_v(uint2 (&v)[8], uint32_t ad0, uint32_t
       : "v"(ad0), "v"(ad1), "i"(OFF), "i"(OFF + STEP), "i"(OFF + 2 * STEP), "i"(OFF + 3 * STEP));
 }
 
-// Maximum / sum over the four lanes of a row (l, l^16, l^32, l^48) with the
-// gfx950 lane swaps (no LDS round trip).
+// v_max_f32 without the canonicalising moves fmaxf adds around lane swaps.
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// Maximum over the four lanes of a row (l, l^16, l^32, l^48) with the gfx950
+// lane swaps (no LDS round trip).
 __device__ __forceinline__ float max4_rows(float v) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max2f(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float sum4_rows(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  return max2f(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 // v_max3_f32 (the compiler does not form it from fmaxf).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -214,7 +215,9 @@ struct Layout {
 template <int D, int BS>
 __device__ __forceinline__ void issue_chunk(char* buf, const PrefillParams& p, uint32_t tab,
                                             int elast, int kvh, int start, int c0, int kend,
-                                            int wave, int lane) {
+                                            int wave, int lane,
+                                            const uint32_t (&koff)[Layout<D>::ROUNDS],
+                                            const uint32_t (&voff)[Layout<D>::ROUNDS]) {
   using L = Layout<D>;
   int blk[L::ROUNDS];
   uint32_t ta[L::ROUNDS];
@@ -223,6 +226,21 @@ __device__ __forceinline__ void issue_chunk(char* buf, const PrefillParams& p, u
   for (int i = 0; i < L::ROUNDS; ++i)
     ta[i] = tab + 4 * min(cidx + (L::RPI * (i * kWaves + wave)) / BS, elast);
   lds_read_tab(blk, ta);
+  if (c0 + kKC <= kend) {
+    // Whole chunk below kend: a uniform row base per round plus the lane's
+    // fixed byte offset (c0 is a multiple of the block size).
+#pragma unroll
+    for (int i = 0; i < L::ROUNDS; ++i) {
+      const int b = __builtin_amdgcn_readfirstlane(blk[i]);
+      const size_t rb = ((size_t)b * p.H_kv + kvh) * (size_t)(BS * D * 2);
+      const char* kb = reinterpret_cast<const char*>(p.kc) + rb;
+      const char* vb = reinterpret_cast<const char*>(p.vc) + rb;
+      const int lds = (i * kWaves + wave) * 1024;
+      __builtin_amdgcn_global_load_lds(kb + koff[i], (lds_void*)(buf + lds), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + voff[i], (lds_void*)(buf + L::TILE + lds), 16, 0, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < L::ROUNDS; ++i) {
     const int k = L::RPI * (i * kWaves + wave) + lane / L::PR;
@@ -246,7 +264,7 @@ template <int D, int SEL>
 __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uint32_t vad,
                                               const uint4 (&qf)[2][D / 32],
                                               f32x4_v (&acc)[2][D / 16], float (&m)[2],
-                                              float (&l)[2], const int (&e)[2],
+                                              f32x4_v (&lacc)[2], const int (&e)[2],
                                               const bool (&full)[2], int c0, float sl,
                                               int lane) {
   using L = Layout<D>;
@@ -299,28 +317,23 @@ __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uin
       float t4 = max3f(s[j][3][0], s[j][3][1], s[j][3][2]);
       t0 = max3f(t0, t1, t2);
       t3 = max3f(t3, t4, s[j][3][3]);
-      mc = max4_rows(__builtin_fmaxf(t0, t3));
+      mc = max4_rows(max2f(t0, t3));
     }
     const float mcs = mc * sl;
     if (__any(mcs > m[j] + 8.f)) {
       const float m_new = fmaxf(m[j], mcs);
       const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
       m[j] = m_new;
-      l[j] *= alpha;
+      lacc[j] *= alpha;
 #pragma unroll
       for (int md = 0; md < L::NMD; ++md) acc[j][md] *= alpha;
     }
-    float ps = 0.f;
     float x[4][4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[T][i] = __builtin_amdgcn_exp2f(fmaf(s[j][T][i], sl, -m[j]));
-        ps += x[T][i];
-      }
+      for (int i = 0; i < 4; ++i) x[T][i] = __builtin_amdgcn_exp2f(fmaf(s[j][T][i], sl, -m[j]));
     }
-    l[j] += ps;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       pb[j][u] = make_uint4(bf16x2_rne(x[2 * u][0], x[2 * u][1]),
@@ -334,6 +347,15 @@ __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uin
   // V[those 4 keys][16 md + r]; v[4h + 2u] / v[4h + 2u + 1] are the two
   // 16-key halves of 32-key half u for d tile md + h.
   constexpr int VOFF = SEL * L::CHUNK + L::TILE;
+  // Row sums: an all-ones 16 x 32 tile times P^T leaves sum_k P[row][k] in
+  // every element of the lane's row (the sum of the same bf16 weights the
+  // products use).
+  const bf16x8_v ones = to_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    lacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, to_bf16x8(pb[0][u]), lacc[0], 0, 0, 0);
+    lacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, to_bf16x8(pb[1][u]), lacc[1], 0, 0, 0);
+  }
 #pragma unroll
   for (int md = 0; md < L::NMD; md += 2) {
     uint2 v[8];
@@ -372,7 +394,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
   const int seq = sk / p.H_kv;
   const int kvh = sk - seq * p.H_kv;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // wave through readfirstlane: the compiler then keeps it and everything
+  // derived from it (row ranges, DMA rounds) in scalar registers.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, r = lane & 15;
   const int n = p.lens[seq];
   const int MG = p.M * p.G;
@@ -439,49 +464,56 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
     vad = (buf0 + k0 * L::ROW + 8 * (r & 1) + 16 * ((r & 3) >> 1)) | (32u * (sw >> 1));
   }
 
+  // The lane's byte offsets within a block row base for each DMA round.
+  uint32_t koff[L::ROUNDS], voff[L::ROUNDS];
+#pragma unroll
+  for (int i = 0; i < L::ROUNDS; ++i) {
+    const int k = L::RPI * (i * kWaves + wave) + lane / L::PR;
+    const int pp = lane % L::PR;
+    koff[i] = 2u * (uint32_t)((k % BS) * D + 8 * (pp ^ L::swz(k)));
+    voff[i] = 2u * (uint32_t)((k % BS) * D + 8 * (pp ^ L::vswz(k)));
+  }
+
   f32x4_v acc[2][L::NMD];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int md = 0; md < L::NMD; ++md) acc[j][md] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {kMaxInit, kMaxInit}, l[2] = {0.f, 0.f};
+  float m[2] = {kMaxInit, kMaxInit};
+  f32x4_v lacc[2] = {f32x4_v{0.f, 0.f, 0.f, 0.f}, f32x4_v{0.f, 0.f, 0.f, 0.f}};
 
   __syncthreads();  // the table slice is in LDS
   if (nch > 0)
-    issue_chunk<D, BS>(s_buf, p, tab, elast, kvh, start, start, kend, wave, lane);
+    issue_chunk<D, BS>(s_buf, p, tab, elast, kvh, start, start, kend, wave, lane, koff, voff);
   for (int ch = 0; ch < nch; ch += 2) {
     {  // even chunk, buffer 0
       const int c0 = start + ch * kKC;
       if (ch + 1 < nch) {
         issue_chunk<D, BS>(s_buf + L::CHUNK, p, tab, elast, kvh, start, c0 + kKC, kend, wave,
-                           lane);
+                           lane, koff, voff);
         wait_vm_barrier<2 * L::ROUNDS>();
       } else {
         wait_vm_barrier<0>();
       }
       const bool full[2] = {c0 + kKC <= gfull0, c0 + kKC <= gfull1};
-      compute_chunk<D, 0>(kad, vad, qf, acc, m, l, e, full, c0, sl, lane);
+      compute_chunk<D, 0>(kad, vad, qf, acc, m, lacc, e, full, c0, sl, lane);
       wait_vm_barrier<63>();  // every wave is done with buffer 0
     }
     if (ch + 1 < nch) {  // odd chunk, buffer 1
       const int c0 = start + (ch + 1) * kKC;
       if (ch + 2 < nch) {
-        issue_chunk<D, BS>(s_buf, p, tab, elast, kvh, start, c0 + kKC, kend, wave, lane);
+        issue_chunk<D, BS>(s_buf, p, tab, elast, kvh, start, c0 + kKC, kend, wave, lane, koff, voff);
         wait_vm_barrier<2 * L::ROUNDS>();
       } else {
         wait_vm_barrier<0>();
       }
       const bool full[2] = {c0 + kKC <= gfull0, c0 + kKC <= gfull1};
-      compute_chunk<D, 1>(kad, vad, qf, acc, m, l, e, full, c0, sl, lane);
+      compute_chunk<D, 1>(kad, vad, qf, acc, m, lacc, e, full, c0, sl, lane);
       wait_vm_barrier<63>();  // every wave is done with buffer 1
     }
   }
 
-  // Each lane summed its own keys of the row: add the four lanes of a row.
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    l[j] = sum4_rows(l[j]);
-  }
+  const float l[2] = {lacc[0][0], lacc[1][0]};
   // Lane (q4, r) of group j holds O^T[16 md + 4 q4 + i][row r].
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
