@@ -35,6 +35,7 @@ WORKLOADS = {"tiny-fp32": 1, "7b-decode-bf16": 2, "32k-gqa-bf16": 3,
 DEFAULT_WORKLOAD = "7b-decode-bf16"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
 KERNEL_SOURCES = ("decode_valu.hip", "decode_mfma.hip", "pkv_device.h")
+PREFILL_SOURCES = ("prefill_mfma.hip", "pkv_device.h")
 
 
 def parse():
@@ -87,21 +88,22 @@ def kv_bytes(w):
     return total, len(rows)
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         p = os.path.join(ROOT, "paged_kv_cache_370_amd", "csrc", name)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload):
-    """HBM bytes per partition-kernel launch from the committed rocprofv3 PMC
-    summary, if it was taken on the current kernel sources; else None."""
+def recorded_traffic(workload, sources=KERNEL_SOURCES):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed rocprofv3 PMC summary, if it was taken on the current kernel
+    sources; else None."""
     if not os.path.exists(COUNTERS_FILE):
         return None
-    src = kernel_source_hash()
+    src = kernel_source_hash(sources)
     for line in open(COUNTERS_FILE):
         parts = line.split()
         if len(parts) >= 4 and parts[0] == "traffic" and parts[1] == workload and parts[2] == src:
@@ -387,8 +389,6 @@ def prefill_bench(pkv, torch, name, reps):
     key, value, slots = (t(x) for x in w.writes[-1])
     out = torch.empty_like(q)
     M = w.query_tokens
-    P = pkv.decode_partition_size(w.S, w.H, w.H_kv, w.D, w.block_size, w.max_context_len, 1, 1,
-                                  0)
     need = pkv.prefill_workspace_size(w.S, M, w.H, w.H_kv, w.D, w.block_size, w.max_context_len,
                                       1, 1, 0)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
@@ -415,16 +415,21 @@ def prefill_bench(pkv, torch, name, reps):
 
     step_ms, attn_ms = timed(step), timed(attn)
     flops = prefill_flops(w.context_lens, M, w.H, w.D)
+    kv, _ = kv_bytes(w)   # each sequence's K and V read once
     tflops = flops / (attn_ms * 1e-3) / 1e12
     return {"workload": w.name, "seqs": w.S, "chunk_tokens": M, "q_heads": w.H,
             "kv_heads": w.H_kv, "head_size": w.D, "block_size": w.block_size,
-            "context": int(w.max_context_len), "partition_size": P,
+            "context": int(w.max_context_len), "workspace_bytes": need,
             "flops_per_step": flops, "ms_per_step": round(step_ms, 5),
             "tokens_per_s": round(w.S * M / (step_ms * 1e-3), 1),
             "attention_ms": round(attn_ms, 5),
+            "kv_bytes": kv,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": recorded_traffic(w.name, PREFILL_SOURCES),
+                         "kernel": "tiled prefill kernel",
+                         "kernel_sources": kernel_source_hash(PREFILL_SOURCES)}}
 
 
 def cpu_baseline_for(w, writes, budget):
