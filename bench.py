@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", default="prefill-chunk-gqa-bf16",
                     help="chunked-prefill workload timed beside the decode step ('none': skip)")
+    ap.add_argument("--beam-fork", default="beam-fork-gqa-bf16",
+                    help="multi-query step over forked tables timed beside the decode step "
+                         "('none': skip)")
     ap.add_argument("--no-block-copy", action="store_true",
                     help="skip the block copy / swap measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -304,6 +307,8 @@ def main():
         result["block_copy"] = block_copy_bench(pkv, torch, kc, vc, ks, vs, args.steps)
     if args.prefill != "none":
         result["prefill"] = prefill_bench(pkv, torch, args.prefill, args.steps)
+    if args.beam_fork != "none":
+        result["beam_fork"] = beam_fork_bench(pkv, torch, args.beam_fork, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_for(w, writes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -430,6 +435,65 @@ def prefill_bench(pkv, torch, name, reps):
                          "traffic": recorded_traffic(w.name, PREFILL_SOURCES),
                          "kernel": "tiled prefill kernel",
                          "kernel_sources": kernel_source_hash(PREFILL_SOURCES)}}
+
+
+def beam_fork_bench(pkv, torch, name, reps):
+    """Times one multi-query step over forked tables (paged_kv_cache_write of
+    each beam's query tokens, then paged_attention_prefill) on a synthetic
+    beam-search batch.  Bytes count each distinct (block, KV head) tile once:
+    the prompt blocks the beams share are read from HBM once."""
+    import workloads
+    w = workloads.make_beam_fork(name)
+    dev = torch.device("cuda:0")
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, kc, vc = t(w.q), t(w.key_cache), t(w.value_cache)
+    tables, lens = t(w.block_tables), t(w.context_lens)
+    key, value, slots = (t(x) for x in w.writes[-1])
+    out = torch.empty_like(q)
+    M = w.query_tokens
+    need = pkv.prefill_workspace_size(w.S, M, w.H, w.H_kv, w.D, w.block_size, w.max_context_len,
+                                      1, 1, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+
+    def attn():
+        pkv.paged_attention_prefill(out, q, kc, vc, tables, lens, w.max_context_len, w.scale,
+                                    workspace=ws)
+
+    def step():
+        pkv.paged_kv_cache_write(key, value, kc, vc, slots)
+        attn()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    step_ms, attn_ms = timed(step), timed(attn)
+    unique, nblocks = kv_bytes(w)
+    logical = int(np.sum(w.context_lens)) * w.H_kv * w.D * 2 * 2
+    gbs = unique / (attn_ms * 1e-3) / 1e9
+    return {"workload": w.name, "beams": w.S, "query_tokens_per_beam": M, "q_heads": w.H,
+            "kv_heads": w.H_kv, "head_size": w.D, "block_size": w.block_size,
+            "context": int(w.max_context_len), "kv_bytes_unique": unique,
+            "kv_bytes_logical": logical, "ms_per_step": round(step_ms, 5),
+            "attention_ms": round(attn_ms, 5),
+            "beam_tokens_per_s": round(w.S * M / (step_ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "kernel": "decode kernel, multi-token mode (unique bytes)"}}
 
 
 def cpu_baseline_for(w, writes, budget):

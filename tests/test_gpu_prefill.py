@@ -121,6 +121,27 @@ def test_tiled_scale_edge_cases(scale):
         assert err <= TOL["bf16"], (ps, err)
 
 
+def test_beam_fork_multi_query():
+    """Beams forked from shared prompts, four query tokens each (decode
+    kernel's multi-token mode): parity with the oracle, and bitwise the same
+    output as with every beam owning private copies of the prompt blocks."""
+    w = workloads.make_beam_fork(reduced=True)
+    _say(f"case beam fork S={w.S} M={w.query_tokens} lens={list(w.context_lens)}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle.paged_attention_prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                         w.block_size)
+    outs = []
+    for x in (w, workloads.unshare_blocks(w)):
+        dw = DeviceWorkload(x)
+        dw.write()
+        outs.append(to_host(_prefill(dw, 0)))
+    got = (outs[0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # bf16 bits
+    err = max_err(got, ref)
+    _say(f"  max_err={err:.3e}")
+    assert err <= TOL["bf16"], err
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_one_query_token_is_decode():
     w = workloads.make_config(2, reduced=True)
     _say(f"case prefill M=1 vs decode {w.name}")

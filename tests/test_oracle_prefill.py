@@ -86,3 +86,20 @@ def test_future_positions_are_never_read():
     out = paged_attention_prefill(q, kc, vc, tables, lens, 0.5, bs)
     assert np.array_equal(out[:, :t + 1], ref[:, :t + 1])
     assert np.all(np.isnan(out[:, t + 1:]))
+
+
+def test_beam_fork_sharing_is_invisible():
+    """Beams that reference their prompt's blocks give exactly the output of
+    the same beams each owning private copies of those blocks."""
+    import workloads
+    from gpu_helpers import oracle_caches
+    w = workloads.make_beam_fork(reduced=True)
+    u = workloads.unshare_blocks(w)
+    assert u.num_blocks > w.num_blocks
+    outs = []
+    for x in (w, u):
+        kc, vc, _, _ = oracle_caches(x)
+        outs.append(paged_attention_prefill(x.q, kc, vc, x.block_tables, x.context_lens, x.scale,
+                                            x.block_size))
+    assert np.all(np.isfinite(outs[0]))
+    assert np.array_equal(outs[0], outs[1])

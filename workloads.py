@@ -289,6 +289,102 @@ def make_prefill(name: str, reduced: bool = False, seed: int = 31) -> Workload:
                           fill="write" if cache == "fp8" else "random", query_tokens=M)
 
 
+BEAM_CONFIGS = {
+    # name: (prompts, beams, prompt length, tokens generated since the fork,
+    #        query tokens per beam, H, H_kv, D, bs)
+    "beam-fork-gqa-bf16": (16, 4, 2001, 64, 4, 32, 8, 128, 16),
+}
+
+
+def make_beam_fork(name: str = "beam-fork-gqa-bf16", reduced: bool = False,
+                   seed: int = 41) -> Workload:
+    """Beams forked from shared prompts (beam-search style), several query
+    tokens per beam.
+
+    Each of P prompts of L tokens is forked into B beams.  The beams of a
+    prompt reference the prompt's whole blocks (one physical copy); the
+    prompt's last, partial block was copied per beam when the beam first
+    wrote into it (copy-on-write), so its first L % bs rows hold the prompt's
+    values in every beam's private copy.  Each beam then holds T tokens of
+    its own, and this step's M query tokens (positions n-M .. n-1, written by
+    the step) end the sequence: n = L + T + M.  Free blocks and rows past n
+    hold NaN.  q is [P*B][M][H][D]."""
+    P, B, L, T, M, H, H_kv, D, bs = BEAM_CONFIGS[name]
+    if reduced:
+        P, L, T = 2, 70, 9
+    rng_layout = np.random.default_rng(seed + 7919)
+    rng = np.random.default_rng(seed)
+    S = P * B
+    n = L + T + M
+    nb = -(-n // bs)
+    shared = L // bs                      # whole prompt blocks
+    private = nb - shared                 # the copied partial block and the beam's own
+    used = P * shared + S * private
+    num_blocks = int(np.ceil(used * 1.05))
+    perm = rng_layout.permutation(num_blocks).astype(np.int32)
+    tables = np.full((S, nb), perm[-1], dtype=np.int32)
+    cur = 0
+    for p in range(P):
+        ids = perm[cur:cur + shared]
+        cur += shared
+        for b in range(B):
+            tables[p * B + b, :shared] = ids
+    for i in range(S):
+        tables[i, shared:] = perm[cur:cur + private]
+        cur += private
+    kc = np.full((num_blocks, H_kv, bs, D), _poison("bf16"), dtype=np.uint16)
+    vc = np.full((num_blocks, H_kv, bs, D), _poison("bf16"), dtype=np.uint16)
+    q = _normal(rng, (S, M, H, D), "bf16")
+    for p in range(P):
+        pk = _normal(rng, (L, H_kv, D), "bf16")
+        pv = _normal(rng, (L, H_kv, D), "bf16")
+        for b in range(B):
+            i = p * B + b
+            for pos in range(L):
+                kc[tables[i, pos // bs], :, pos % bs] = pk[pos]
+                vc[tables[i, pos // bs], :, pos % bs] = pv[pos]
+    for i in range(S):
+        bk = _normal(rng, (T, H_kv, D), "bf16")
+        bv = _normal(rng, (T, H_kv, D), "bf16")
+        for t in range(T):
+            pos = L + t
+            kc[tables[i, pos // bs], :, pos % bs] = bk[t]
+            vc[tables[i, pos // bs], :, pos % bs] = bv[t]
+    writes = [_step_write(rng, tables, [np.arange(n - M, n)] * S, H_kv, D, bs, "bf16")]
+    return Workload(name=name + ("-reduced" if reduced else ""), S=S, H=H, H_kv=H_kv, D=D,
+                    block_size=bs, q_dtype="bf16", cache_dtype="bf16", src_dtype="bf16",
+                    num_blocks=num_blocks, q=q, key_cache=kc, value_cache=vc,
+                    block_tables=tables, context_lens=np.full(S, n, dtype=np.int32),
+                    writes=writes, scale=float(np.float32(1.0 / np.sqrt(D))),
+                    query_tokens=M)
+
+
+def unshare_blocks(w: Workload) -> Workload:
+    """Twin of a workload in which every sequence owns a private copy (same
+    bytes) of each block that more than one table references."""
+    counts = {}
+    nbs = [-(-int(n) // w.block_size) for n in w.context_lens]
+    for i in range(w.S):
+        for b in w.block_tables[i, :nbs[i]]:
+            counts[int(b)] = counts.get(int(b), 0) + 1
+    tables = w.block_tables.copy()
+    extra_k, extra_v = [], []
+    nxt = w.num_blocks
+    for i in range(w.S):
+        for j in range(nbs[i]):
+            b = int(w.block_tables[i, j])
+            if counts[b] > 1:
+                extra_k.append(w.key_cache[b])
+                extra_v.append(w.value_cache[b])
+                tables[i, j] = nxt
+                nxt += 1
+    kc = np.concatenate([w.key_cache, np.stack(extra_k)]) if extra_k else w.key_cache
+    vc = np.concatenate([w.value_cache, np.stack(extra_v)]) if extra_v else w.value_cache
+    return Workload(**{**w.__dict__, "name": w.name + "-unshared", "num_blocks": nxt,
+                       "key_cache": kc, "value_cache": vc, "block_tables": tables,
+                       "shared_blocks": 0})
+
+
 def duplicate_shared_blocks(w: Workload) -> Workload:
     """Twin of a shared-prefix workload: each sequence gets private copies of
     the shared blocks (same bytes), appended to the pool."""
