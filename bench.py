@@ -305,6 +305,9 @@ def main():
                                  "GB_per_s_source_read": round(setup_bytes / setup_ms / 1e6, 1)}
     if not args.no_block_copy:
         result["block_copy"] = block_copy_bench(pkv, torch, kc, vc, ks, vs, args.steps)
+    if w.shared_blocks > 0:
+        result["read_once"] = read_once_bench(pkv, torch, w, out, q, kc, vc, ks, vs, tables, lens,
+                                              total_bytes, args.steps)
     if args.prefill != "none":
         result["prefill"] = prefill_bench(pkv, torch, args.prefill, args.steps)
     if args.beam_fork != "none":
@@ -435,6 +438,36 @@ def prefill_bench(pkv, torch, name, reps):
                          "traffic": recorded_traffic(w.name, PREFILL_SOURCES),
                          "kernel": "tiled prefill kernel",
                          "kernel_sources": kernel_source_hash(PREFILL_SOURCES)}}
+
+
+def read_once_bench(pkv, torch, w, out, q, kc, vc, ks, vs, tables, lens, unique_bytes, reps):
+    """Times paged_attention_decode_shared_prefix on the shared-prefix
+    workload: the prefix once per KV head for all sequences, each sequence's
+    suffix, and the merge (three launches), K calls back to back."""
+    prefix = w.shared_blocks * w.block_size
+    qc, cc = pkv.dtype_code(q), pkv.dtype_code(kc)
+    need = pkv.shared_prefix_workspace_size(w.S, w.H, w.H_kv, w.D, w.block_size,
+                                            w.max_context_len, prefix, qc, cc, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=q.device)
+
+    def call():
+        pkv.paged_attention_decode_shared_prefix(out, q, kc, vc, tables, lens, w.max_context_len,
+                                                 w.scale, prefix, ks, vs, workspace=ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"prefix_tokens": prefix, "ms_per_call": round(ms, 5),
+            "GB_per_s_unique": round(unique_bytes / (ms * 1e-3) / 1e9, 1),
+            "note": "decode of the same batch (prefix pass + suffix partitions + reduce); "
+                    "compare with kernel_ms decode_partitions + decode_reduce"}
 
 
 def beam_fork_bench(pkv, torch, name, reps):

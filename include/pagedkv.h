@@ -241,6 +241,47 @@ size_t paged_attention_prefill_workspace_size(
     int32_t q_dtype, int32_t cache_dtype, int32_t partition_size);
 
 /*
+ * paged_attention_decode_shared_prefix -- paged_attention_decode for a batch
+ * whose tables all begin with the same physical blocks: a prompt prefix
+ * shared by reference (dpshk.com article, section 2.3: blocks shared between
+ * sequences with a reference count; page "PagedAttention 与连续批处理…",
+ * section "PagedAttention：把显存做成虚拟内存": common prompt prefixes
+ * shared, only page-aligned ones per its advice section).  The prefix is
+ * read once per KV head for all sequences (rows = every sequence's query
+ * heads of that KV head), each sequence's remaining positions as a decode
+ * of its own, and the two merged per (sequence, head); the result is
+ * paged_attention_decode's.
+ *   prefix_tokens: a multiple of block_size, at most max_context_len; the
+ *   first prefix_tokens / block_size entries of every table must name the
+ *   same blocks (the caller's contract; the prefix is read through
+ *   sequence 0's table).  A sequence shorter than the prefix sees only its
+ *   own positions.  0 makes this paged_attention_decode.
+ *   bf16 queries (PKV_ERR_DTYPE otherwise); bf16 or FP8 caches.  Other
+ *   arguments are as for paged_attention_decode; the workspace is
+ *   paged_attention_decode_shared_prefix_workspace_size bytes, its first
+ *   4096 zero, and is left so.
+ */
+pkv_status_t paged_attention_decode_shared_prefix(
+    void* out, const void* query,
+    const void* key_cache, const void* value_cache,
+    const float* key_scale, const float* value_scale,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t prefix_tokens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float scale,
+    int32_t q_dtype, int32_t cache_dtype, int32_t partition_size,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/* Workspace bytes paged_attention_decode_shared_prefix needs (0 for invalid
+ * arguments). */
+size_t paged_attention_decode_shared_prefix_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_context_len, int32_t prefix_tokens,
+    int32_t q_dtype, int32_t cache_dtype, int32_t partition_size);
+
+/*
  * paged_kv_block_copy -- copy whole blocks from one pool to another: the
  * copy-on-write of a shared block before a sequence writes into it (page
  * "vLLM的诞生背景：大模型推理的痛点与PagedAttention的破局", the limitations

@@ -1,4 +1,5 @@
-"""PagedAttention decode and paged KV write for AMD MI355X (gfx950).
+"""PagedAttention decode, paged KV write, block copy and multi-token attention
+for AMD MI355X (gfx950).
 
 The compute lives in libpagedkv.so (hand-written HIP kernels behind a C ABI,
 declared in include/pagedkv.h); this package is its thin Python binding plus
@@ -18,10 +19,12 @@ from ._lib import (
     paged_attention_decode,
     paged_attention_decode_partitions,
     paged_attention_decode_reduce,
+    paged_attention_decode_shared_prefix,
     paged_attention_prefill,
     paged_kv_block_copy,
     prefill_workspace_size,
     paged_kv_cache_write,
+    shared_prefix_workspace_size,
     status_string,
     write_workspace_size,
 )
@@ -31,8 +34,9 @@ __all__ = [
     "PKV_BF16", "PKV_F32", "PKV_FP8_E4M3", "PagedKVError", "BlockManager", "OutOfBlocks",
     "decode_partition_size", "decode_workspace_size", "dtype_code", "load",
     "paged_attention_decode", "paged_attention_decode_partitions",
-    "paged_attention_decode_reduce", "paged_attention_prefill", "paged_kv_block_copy",
-    "paged_kv_cache_write", "prefill_workspace_size",
+    "paged_attention_decode_reduce", "paged_attention_decode_shared_prefix",
+    "paged_attention_prefill", "paged_kv_block_copy", "paged_kv_cache_write",
+    "prefill_workspace_size", "shared_prefix_workspace_size",
     "status_string",
     "write_workspace_size",
 ]

@@ -28,6 +28,8 @@ EXPORTS = (
     "paged_kv_block_copy",
     "paged_attention_prefill",
     "paged_attention_prefill_workspace_size",
+    "paged_attention_decode_shared_prefix",
+    "paged_attention_decode_shared_prefix_workspace_size",
     "pkv_status_string",
     "pkv_version",
 )
@@ -76,6 +78,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                             + [vp, sz, vp])
     lib.paged_attention_prefill_workspace_size.restype = sz
     lib.paged_attention_prefill_workspace_size.argtypes = [i32] * 10
+    lib.paged_attention_decode_shared_prefix.restype = i32
+    lib.paged_attention_decode_shared_prefix.argtypes = ([vp] * 8 + [i32] * 8 + [fp] + [i32] * 3
+                                                         + [vp, sz, vp])
+    lib.paged_attention_decode_shared_prefix_workspace_size.restype = sz
+    lib.paged_attention_decode_shared_prefix_workspace_size.argtypes = [i32] * 10
     lib.paged_kv_block_copy.restype = i32
     lib.paged_kv_block_copy.argtypes = [vp] * 9 + [i32] * 5 + [vp]
     lib.pkv_status_string.restype = ctypes.c_char_p
@@ -243,6 +250,38 @@ def paged_kv_block_copy(src_key_cache, src_value_cache, dst_key_cache, dst_value
 
 
 # ----------------------------------------------------------------- prefill
+
+def shared_prefix_workspace_size(num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                                 max_context_len, prefix_tokens, q_code, c_code,
+                                 partition_size=0) -> int:
+    return int(load().paged_attention_decode_shared_prefix_workspace_size(
+        num_seqs, num_heads, num_kv_heads, head_size, block_size, max_context_len,
+        prefix_tokens, q_code, c_code, partition_size))
+
+
+def paged_attention_decode_shared_prefix(out, query, key_cache, value_cache, block_tables,
+                                         context_lens, max_context_len, scale, prefix_tokens,
+                                         key_scale=None, value_scale=None, partition_size=0,
+                                         workspace=None, stream=None):
+    """paged_attention_decode for tables that all begin with the same
+    prefix_tokens / bs blocks: the prefix is read once per KV head."""
+    _contig(out, query, key_cache, value_cache, block_tables, context_lens, key_scale,
+            value_scale)
+    S, H, D = query.shape
+    _, H_kv, bs, _ = key_cache.shape
+    qc, cc = dtype_code(query), dtype_code(key_cache)
+    if workspace is None:
+        need = shared_prefix_workspace_size(S, H, H_kv, D, bs, max_context_len, prefix_tokens,
+                                            qc, cc, partition_size)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=query.device) if need else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().paged_attention_decode_shared_prefix(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
+        _ptr(value_scale), _ptr(block_tables), _ptr(context_lens), int(prefix_tokens), S, H,
+        H_kv, D, bs, block_tables.shape[1], int(max_context_len), float(scale), qc, cc,
+        int(partition_size), _ptr(workspace), wbytes, _stream(stream))
+    _check(st, "paged_attention_decode_shared_prefix")
+
 
 def prefill_workspace_size(num_seqs, num_query_tokens, num_heads, num_kv_heads, head_size,
                            block_size, max_context_len, q_code, c_code, partition_size=0) -> int:

@@ -301,6 +301,29 @@ pkv_status_t paged_attention_decode(void* out, const void* query, const void* ke
                                        stream);
 }
 
+// Shared-prefix decode: the prefix's partials (ceil(prefix / P) slots) come
+// before the suffix partitions' in every row; the prefix is cut into
+// partitions of the same P tokens.  (Cutting it finer for more parallel
+// items was measured slower: the prefix launch is not short of items.)
+struct PrefixSplit {
+  int P = -1, pre_slots = 0, suf_slots = 0;
+};
+
+static PrefixSplit prefix_split(int bs, int max_ctx, int prefix, int requested) {
+  PrefixSplit sp;
+  if (prefix <= 0 || prefix % bs != 0 || prefix > max_ctx) return sp;
+  sp.P = resolve_partition(bs, max_ctx - prefix > 0 ? max_ctx - prefix : bs, requested);
+  if (sp.P <= 0) return sp;
+  sp.pre_slots = (prefix + sp.P - 1) / sp.P;
+  sp.suf_slots = num_partitions(max_ctx - prefix, sp.P);
+  return sp;
+}
+
+static size_t shared_prefix_workspace(int S, int H, int D, const PrefixSplit& sp) {
+  const size_t rows = (size_t)S * H * (sp.pre_slots + sp.suf_slots);
+  return kSchedBytes + 2 * align256(rows * sizeof(float)) + align256(rows * D * sizeof(float));
+}
+
 // Which kernel serves a multi-token call, and its partition size.  Long
 // chunks (at least kTileMinRows (token, head) rows per KV head) over a bf16
 // cache run on the tiled prefill kernel; short ones (and FP8 caches) on the
@@ -316,7 +339,7 @@ struct PrefillPlan {
   int P;  // partition size, or <= 0 for invalid arguments
 };
 
-PrefillPlan prefill_plan(int S, int M, int H, int H_kv, int D, int bs, int max_ctx, int q,
+static PrefillPlan prefill_plan(int S, int M, int H, int H_kv, int D, int bs, int max_ctx, int q,
                          int c, int requested) {
   PrefillPlan pl{false, -1};
   if (M <= 0 || check_decode_shape(S, H, H_kv, D, bs, max_ctx, q, c) != PKV_OK ||
@@ -382,6 +405,90 @@ pkv_status_t paged_attention_prefill(void* out, const void* query, const void* k
   }
   if (st != PKV_OK || s.a.NP <= 1) return st;
   return hip_status(launch_decode_reduce(s.a));
+}
+
+pkv_status_t paged_attention_decode_shared_prefix(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const float* key_scale, const float* value_scale, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t prefix_tokens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float scale, int32_t q_dtype, int32_t cache_dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  if (prefix_tokens == 0)
+    return paged_attention_decode(out, query, key_cache, value_cache, key_scale, value_scale,
+                                  block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                                  head_size, block_size, max_blocks_per_seq, max_context_len,
+                                  scale, q_dtype, cache_dtype, partition_size, workspace,
+                                  workspace_bytes, stream);
+  const pkv_status_t shape = check_decode_shape(num_seqs, num_heads, num_kv_heads, head_size,
+                                                block_size, max_context_len, q_dtype, cache_dtype);
+  if (shape != PKV_OK) return shape;
+  if (q_dtype != PKV_BF16) return PKV_ERR_DTYPE;  // rows of many sequences: matrix cores
+  const PrefixSplit sp = prefix_split(block_size, max_context_len, prefix_tokens, partition_size);
+  if (sp.P <= 0) return PKV_ERR_SHAPE;
+  DecodeSetup s = setup_decode(out, query, key_cache, value_cache, key_scale, value_scale,
+                               block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                               head_size, block_size, max_blocks_per_seq, max_context_len, scale,
+                               q_dtype, cache_dtype, sp.P, workspace, SIZE_MAX, stream, true);
+  if (s.status != PKV_OK || s.empty) return s.status;
+  // The split's own workspace layout (setup_decode's size is a plain decode's).
+  const size_t need = shared_prefix_workspace(num_seqs, num_heads, head_size, sp);
+  if (workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  // Partials for every (sequence, head) row: pre_slots + suf_slots each.
+  DecodeArgs base = s.a;
+  {
+    const size_t rows = (size_t)num_seqs * num_heads * (sp.pre_slots + sp.suf_slots);
+    char* part = reinterpret_cast<char*>(workspace) + kSchedBytes;
+    base.ws_m = reinterpret_cast<float*>(part);
+    base.ws_l = reinterpret_cast<float*>(part + align256(rows * sizeof(float)));
+    base.ws_acc = reinterpret_cast<float*>(part + 2 * align256(rows * sizeof(float)));
+  }
+  base.np_stride = sp.pre_slots + sp.suf_slots;
+  base.force_partial = true;
+  // 1. The prefix once per KV head for all sequences: rows are the (sequence,
+  //    head) pairs, keys the prefix blocks of the first table.
+  DecodeArgs pre = base;
+  pre.S = 1;
+  pre.M = num_seqs;
+  pre.prefix_rows = prefix_tokens;
+  pre.max_ctx = prefix_tokens;
+  pre.NP = sp.pre_slots;
+  pre.slot_off = 0;
+  if (!decode_mfma_supported(pre)) return PKV_ERR_SHAPE;
+  pkv_status_t st = hip_status(launch_decode_mfma(pre));
+  if (st != PKV_OK) return st;
+  // 2. Each sequence's positions after the prefix, as a decode of its own.
+  DecodeArgs suf = base;
+  suf.len_off = prefix_tokens;
+  suf.tables = block_tables + prefix_tokens / block_size;
+  suf.max_ctx = max_context_len - prefix_tokens;
+  suf.NP = sp.suf_slots;
+  suf.slot_off = sp.pre_slots;
+  st = hip_status(launch_decode_mfma(suf));
+  if (st != PKV_OK) return st;
+  // 3. Merge the prefix and suffix partials of every row.
+  DecodeArgs red = base;
+  red.NP = sp.pre_slots + sp.suf_slots;
+  red.prefix_slots = sp.pre_slots;
+  red.len_off = prefix_tokens;
+  return hip_status(launch_decode_reduce(red));
+}
+
+size_t paged_attention_decode_shared_prefix_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_context_len, int32_t prefix_tokens, int32_t q_dtype,
+    int32_t cache_dtype, int32_t partition_size) {
+  if (prefix_tokens == 0)
+    return paged_attention_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_size,
+                                                 block_size, max_context_len, q_dtype,
+                                                 cache_dtype, partition_size);
+  if (check_decode_shape(num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                         max_context_len, q_dtype, cache_dtype) != PKV_OK ||
+      q_dtype != PKV_BF16)
+    return 0;
+  const PrefixSplit sp = prefix_split(block_size, max_context_len, prefix_tokens, partition_size);
+  if (sp.P <= 0) return 0;
+  return shared_prefix_workspace(num_seqs, num_heads, head_size, sp);
 }
 
 size_t paged_attention_prefill_workspace_size(int32_t num_seqs, int32_t num_query_tokens,

@@ -95,8 +95,32 @@ struct MfmaParams {
                // counter at [(8 + x) * kCounterStride]
   int S, H, H_kv, G, chunks, max_blocks, P, NP;
   int M;  // query tokens per sequence (1 for decode)
+  // Split attention over a shared prefix (zero / plain values otherwise):
+  int len_off;        // positions below it are not this launch's: n = lens - len_off
+  int prefix;         // prefix-rows launch: the prefix length (the one "sequence")
+  int slot_off;       // partial slot of partition 0
+  int np_stride;      // partial slots per row
+  int force_partial;  // write partials even when a context fits one partition
   float scale_log2;
 };
+
+// Item kinds of a launch: one query token per sequence; several causal
+// tokens per sequence; rows that are the (sequence, head) pairs of all
+// sequences over a prefix whose blocks every table shares; or one token per
+// sequence over the positions after that prefix.  The split parameters are
+// read only by the last two, so the others keep their scalar registers.
+enum : int { kModeDecode = 0, kModeCausal = 1, kModePrefixRows = 2, kModeSuffix = 3 };
+
+template <int MODE>
+constexpr bool kSplit = MODE == kModePrefixRows || MODE == kModeSuffix;
+
+// Context length the launch sees for sequence i.
+template <int MODE>
+__device__ __forceinline__ int seq_len(const MfmaParams& p, int i) {
+  if constexpr (MODE == kModePrefixRows) return p.prefix;
+  if constexpr (MODE == kModeSuffix) return max(0, p.lens[i] - p.len_off);
+  return p.lens[i];
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -172,9 +196,9 @@ struct Part {
 };
 
 // Index of a row's [D] vector in q / out ([S][M][H][D]) and of its partial.
-template <bool MQ>
+template <int MODE>
 __device__ __forceinline__ size_t row_of(const MfmaParams& p, const Part& w, int rho) {
-  if constexpr (MQ) {
+  if constexpr (MODE == kModeCausal || MODE == kModePrefixRows) {
     const int m = rho / p.G;
     return ((size_t)w.seq * p.M + m) * p.H + (size_t)w.kvh * p.G + (rho - m * p.G);
   } else {
@@ -405,6 +429,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_red, int* tota
 //   s_rag[i]:  short partitions of sequences 0..i-1  (s_rag[S] = R)
 //   s_len[i]:  context length of sequence i
 // Returns F (and R in *n_rag).  Every thread of the workgroup calls it.
+template <int MODE>
 __device__ int build_offsets(const MfmaParams& p, int* s_full, uint16_t* s_rag, int* s_len,
                              int* s_red, int* n_rag) {
   constexpr int NTH = kNW * 64;
@@ -415,7 +440,7 @@ __device__ int build_offsets(const MfmaParams& p, int* s_full, uint16_t* s_rag, 
   for (int k = 0; k < per; ++k) {
     const int i = base + k;
     if (i < p.S) {
-      const int n = p.lens[i];
+      const int n = seq_len<MODE>(p, i);
       s_len[i] = n;
       nf += n / p.P;
       nr += (n % p.P != 0 || n == 0) ? 1 : 0;
@@ -464,7 +489,7 @@ struct Item {
   Part w;
 };
 
-template <int BS, bool SCAN>
+template <int BS, bool SCAN, int MODE>
 __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y, int n_full,
                                             const int* s_full, const uint16_t* s_rag,
                                             const int* s_len) {
@@ -487,7 +512,7 @@ __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y
   } else {
     seq = rest / p.NP;
     it.part = rest - seq * p.NP;
-    it.n = p.lens[seq];
+    it.n = seq_len<MODE>(p, seq);
     it.live = it.part == 0 || it.part * p.P < it.n;
   }
   it.w.seq = seq;
@@ -523,7 +548,7 @@ __device__ __forceinline__ void store_tab(int tab, int* wtab, int lane) {
 
 // Q operand fragments of an item, one element per thread (thread t owns
 // element t), shared by the waves; heads past the group are zeros.
-template <typename CT, int D, bool MQ>
+template <typename CT, int D, int MODE>
 __device__ __forceinline__ uint4 fetch_q(const MfmaParams& p, const Part& w, int tid) {
   using Gm = Geometry<CT, D>;
   // fragment c = tid / 64 for lane l = (q, r) = tid % 64; threads past the
@@ -533,7 +558,7 @@ __device__ __forceinline__ uint4 fetch_q(const MfmaParams& p, const Part& w, int
   const int hq = l & 15;
   return *reinterpret_cast<const uint4*>(
       reinterpret_cast<const uint16_t*>(p.q) +
-      row_of<MQ>(p, w, w.r0 + min(hq, w.nh - 1)) * D + Gm::DQ * (l >> 4) + 8 * c);
+      row_of<MODE>(p, w, w.r0 + min(hq, w.nh - 1)) * D + Gm::DQ * (l >> 4) + 8 * c);
 }
 
 template <typename CT, int D>
@@ -544,7 +569,7 @@ __device__ __forceinline__ void store_q(uint4 v, const Part& w, uint4* qf, int t
   }
 }
 
-template <typename CT, int D, int BS, bool SCAN, bool MQ>
+template <typename CT, int D, int BS, bool SCAN, int MODE>
 __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   using Gm = Geometry<CT, D>;
   static_assert(kMaxTable == kNW * 64, "one table entry per thread");
@@ -588,7 +613,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   int total, n_full = 0;
   if constexpr (SCAN) {
     int n_rag;
-    n_full = build_offsets(p, s_full, s_rag, s_len, s_red, &n_rag);  // has barriers
+    n_full = build_offsets<MODE>(p, s_full, s_rag, s_len, s_red, &n_rag);  // has barriers
     total = Y * (n_full + n_rag);
   } else {
     total = Y * p.S * p.NP;
@@ -598,15 +623,15 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   int nxt = s_next[1];
   int buf = 0;
   constexpr int EPC = Gm::CHUNK / BS;  // block ids per chunk
-  Item it = decode_item<BS, SCAN>(p, min(cur, total - 1), Y, n_full, s_full, s_rag, s_len);
+  Item it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, s_full, s_rag, s_len);
   if (cur < total) {
     store_tab(fetch_tab<CT, D, BS>(p, it.w, wave, lane), s_wtab[0][wave], lane);
-    store_q<CT, D>(fetch_q<CT, D, MQ>(p, it.w, tid), it.w, s_qf[0], tid);
+    store_q<CT, D>(fetch_q<CT, D, MODE>(p, it.w, tid), it.w, s_qf[0], tid);
   }
   // The second item's block ids travel in a register until the first
   // item's last chunk (each item's are fetched one item ahead).
   int tab_next = fetch_tab<CT, D, BS>(
-      p, decode_item<BS, SCAN>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len).w, wave,
+      p, decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len).w, wave,
       lane);
   __syncthreads();
 
@@ -643,8 +668,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     store_tab(tab_next, wt_nxt, lane);
     // Prefetch the next item's Q and claim the item after it.  Nothing reads
     // the other buffers until the next item.
-    const Item nx = decode_item<BS, SCAN>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len);
-    const uint4 q_next = fetch_q<CT, D, MQ>(p, nx.w, tid);
+    const Item nx = decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len);
+    const uint4 q_next = fetch_q<CT, D, MODE>(p, nx.w, tid);
     // The claim's result is used only after barrier X.  (Only thread 0 sets
     // and reads it: initialising it in the other lanes would make the
     // compiler wait for every pending load first.)
@@ -673,10 +698,16 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     // positions up to it.  With one token per sequence every row sees the
     // whole partition.
     int full_end = it.w.end, row_end = it.w.end;
-    if constexpr (MQ) {
+    if constexpr (MODE == kModeCausal) {
       const int base = it.n - p.M + 1;  // end of token 0's row
       row_end = min(it.w.end, base + (it.w.r0 + r) / p.G);
       full_end = min(it.w.end, base + it.w.r0 / p.G);
+    } else if constexpr (MODE == kModePrefixRows) {
+      // Row r belongs to sequence (r0 + r) / G, which sees the prefix only
+      // up to its own length.
+      const int sq = min((it.w.r0 + r) / p.G, p.M - 1);
+      row_end = min(it.w.end, p.lens[sq]);
+      full_end = __all(row_end >= it.w.end) ? it.w.end : it.w.start;
     }
     int ci = wave;
     do {
@@ -737,14 +768,14 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     // are stored during the next item's last chunk.
     const int nn = __builtin_amdgcn_readfirstlane(s_next[0]);
     tab_next = fetch_tab<CT, D, BS>(
-        p, decode_item<BS, SCAN>(p, min(nn, total - 1), Y, n_full, s_full, s_rag, s_len).w, wave,
+        p, decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, s_full, s_rag, s_len).w, wave,
         lane);
 
     // Thread t merges 4 consecutive d of one head: one 16-byte LDS read per
     // wave state and one 16-byte (8-byte for bf16) store, so few stores
     // are left for the next item's first wait to drain.
     if (it.live) {
-      const bool single = it.n <= p.P;
+      const bool single = !kSplit<MODE> && it.n <= p.P;
       for (int idx = tid * 4; idx < it.w.nh * D; idx += kNW * 64 * 4) {
         const int g = idx / D;
         const int d = idx - g * D;
@@ -765,7 +796,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
           O.z = fmaf(a.z, wt, O.z);
           O.w = fmaf(a.w, wt, O.w);
         }
-        const size_t row = row_of<MQ>(p, it.w, it.w.r0 + g);
+        const size_t row = row_of<MODE>(p, it.w, it.w.r0 + g);
         if (single) {
           const bool ok = L > 0.f;
           const float ox = ok ? O.x / L : 0.f, oy = ok ? O.y / L : 0.f;
@@ -773,7 +804,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * D + d) =
               make_uint2(pack_bf16x2(ox, oy), pack_bf16x2(oz, ow));
         } else {
-          const size_t pi = row * p.NP + it.part;
+          const size_t pi = kSplit<MODE> ? row * p.np_stride + it.part + p.slot_off
+                                         : row * p.NP + it.part;
           // Streaming store: the reduce kernel reads the partial once.
           const f32x4_t o4 = {O.x, O.y, O.z, O.w};
           __builtin_nontemporal_store(o4, reinterpret_cast<f32x4_t*>(p.ws_acc + pi * D + d));
@@ -801,11 +833,11 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
 // Workgroups of a persistent launch: as many as are resident at once (CUs x
 // the kernel's occupancy, a multiple of the 8 XCDs), never more than items.
 // The occupancy query runs once per kernel variant and device.
-template <typename CT, int D, int BS, bool SCAN, bool MQ>
+template <typename CT, int D, int BS, bool SCAN, int MODE>
 unsigned persistent_grid(long long items) {
   constexpr int kMaxDev = 64;
   static int resident[kMaxDev];  // per device, for this kernel variant only
-  const void* kern = reinterpret_cast<const void*>(decode_mfma_kernel<CT, D, BS, SCAN, MQ>);
+  const void* kern = reinterpret_cast<const void*>(decode_mfma_kernel<CT, D, BS, SCAN, MODE>);
   int dev = 0;
   int per_dev = 0;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDev) per_dev = resident[dev];
@@ -823,15 +855,15 @@ unsigned persistent_grid(long long items) {
   return (unsigned)(per_dev < items ? per_dev : items);
 }
 
-template <typename CT, int D, int BS, bool MQ>
+template <typename CT, int D, int BS, int MODE>
 hipError_t launch_mode(const DecodeArgs& a, const MfmaParams& p, long long items) {
   if (a.S <= kMaxScanSeqs) {
-    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, true, MQ>),
-                       dim3(persistent_grid<CT, D, BS, true, MQ>(items)), dim3(kNW * 64), 0,
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, true, MODE>),
+                       dim3(persistent_grid<CT, D, BS, true, MODE>(items)), dim3(kNW * 64), 0,
                        a.stream, p);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, false, MQ>),
-                       dim3(persistent_grid<CT, D, BS, false, MQ>(items)), dim3(kNW * 64), 0,
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, false, MODE>),
+                       dim3(persistent_grid<CT, D, BS, false, MODE>(items)), dim3(kNW * 64), 0,
                        a.stream, p);
   }
   return hipGetLastError();
@@ -846,10 +878,15 @@ hipError_t launch_bs(const DecodeArgs& a) {
   p.S = a.S; p.H = a.H; p.H_kv = a.H_kv; p.G = a.H / a.H_kv; p.M = a.M;
   p.chunks = (a.M * p.G + 15) / 16;
   p.max_blocks = a.max_blocks; p.P = a.P; p.NP = a.NP;
+  p.len_off = a.len_off; p.prefix = a.prefix_rows; p.slot_off = a.slot_off;
+  p.np_stride = a.np_stride > 0 ? a.np_stride : a.NP;
+  p.force_partial = a.force_partial ? 1 : 0;
   p.scale_log2 = a.scale * kLog2e;
   const long long items = (long long)a.H_kv * p.chunks * a.S * a.NP;
-  return a.M > 1 ? launch_mode<CT, D, BS, true>(a, p, items)
-                 : launch_mode<CT, D, BS, false>(a, p, items);
+  if (a.prefix_rows > 0) return launch_mode<CT, D, BS, kModePrefixRows>(a, p, items);
+  if (a.len_off > 0 || a.force_partial) return launch_mode<CT, D, BS, kModeSuffix>(a, p, items);
+  return a.M > 1 ? launch_mode<CT, D, BS, kModeCausal>(a, p, items)
+                 : launch_mode<CT, D, BS, kModeDecode>(a, p, items);
 }
 
 template <typename CT, int D>

@@ -47,7 +47,7 @@ template <bool OUT_BF16, int D>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(
     void* __restrict__ out, const int32_t* __restrict__ lens, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const float* __restrict__ ws_acc, int H, int P, int NP,
-    int M) {
+    int M, int pre_slots, int len_off) {
   constexpr int U0 = kFirst, U = kChunk;
   // One workgroup per row (seq * M + t) * H + h: query token t of sequence
   // seq, query head h (M = 1 for decode).
@@ -75,9 +75,11 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
   }
   const int n = lens[seq];
   // Token t sits at position n - M + t and sees the positions up to it: its
-  // partitions are the first ceil(end / P) of the sequence's.
+  // partitions are the first ceil(end / P) of the sequence's.  With a shared
+  // prefix split off, the prefix's pre_slots partials come first and the
+  // partitions cover the positions from len_off on.
   const int end = n - M + t + 1;
-  const int np = (end + P - 1) / P;
+  const int np = pre_slots + (max(end - len_off, 0) + P - 1) / P;
   float Mx = kNegInf, L = 0.f, O = 0.f;
   merge_chunk<U0>(m0, l0, a0, 0, np, Mx, L, O);
   for (int q0 = U0; q0 < np; q0 += U) {
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
   // No branch before this point, so the first chunk's loads are issued
   // before the length arrives.  A sequence of at most P tokens was written
   // directly by the partition kernel.
-  if (n <= P) return;
+  if (pre_slots == 0 && n <= P) return;
   const float res = L > 0.f ? O / L : 0.f;
   const size_t oi = row * D + d;
   if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16(res);
@@ -106,10 +108,12 @@ hipError_t launch_d(const DecodeArgs& a) {
   const unsigned grid = (unsigned)((size_t)a.S * a.M * a.H);
   if (a.q_dtype == PKV_BF16) {
     hipLaunchKernelGGL((decode_reduce_kernel<true, D>), grid, dim3(D), 0, a.stream, a.out, a.lens,
-                       a.ws_m, a.ws_l, a.ws_acc, a.H, a.P, a.NP, a.M);
+                       a.ws_m, a.ws_l, a.ws_acc, a.H, a.P, a.NP, a.M, a.prefix_slots,
+                       a.len_off);
   } else {
     hipLaunchKernelGGL((decode_reduce_kernel<false, D>), grid, dim3(D), 0, a.stream, a.out,
-                       a.lens, a.ws_m, a.ws_l, a.ws_acc, a.H, a.P, a.NP, a.M);
+                       a.lens, a.ws_m, a.ws_l, a.ws_acc, a.H, a.P, a.NP, a.M,
+                       a.prefix_slots, a.len_off);
   }
   return hipGetLastError();
 }

@@ -35,6 +35,13 @@ struct DecodeArgs {
   int S, H, H_kv, D, bs, max_blocks, max_ctx;
   int M = 1;  // query tokens per sequence: 1 for decode, the chunk for prefill;
               // q and out are [S][M][H][D]
+  // Attention split at a prefix shared by every table (zero otherwise):
+  int len_off = 0;        // the launch sees positions from len_off on (tables offset to match)
+  int prefix_rows = 0;    // > 0: one launch over the prefix, rows = (sequence, head) pairs
+  int slot_off = 0;       // partial slot of the launch's partition 0
+  int np_stride = 0;      // partial slots per row (0: NP)
+  bool force_partial = false;  // partials even for contexts within one partition
+  int prefix_slots = 0;   // reduce: slots before the suffix partitions
   float scale;
   int q_dtype, cache_dtype;
   int P;   // partition size in tokens (multiple of bs)

@@ -187,3 +187,33 @@ def test_prefill_workspace_grows_with_tokens():
     expect = 4096 + 2 * ((rows * 4 + 255) // 256 * 256) + (rows * 128 * 4 + 255) // 256 * 256
     assert pkv.prefill_workspace_size(4, 16, 8, 2, 128, 16, 3000, 1, 1, 512) == expect
     assert pkv.prefill_workspace_size(4, 0, 8, 2, 128, 16, 3000, 1, 1, 512) == 0
+
+
+def _shared(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None, tables=FAKE, lens=FAKE, pre=64,
+             S=2, H=8, H_kv=2, D=128, bs=16, max_blocks=64, max_ctx=1000, scale=0.1, qd=1, cd=1,
+             ps=0, ws=None, wsb=0)
+    a.update(kw)
+    return pkv.load().paged_attention_decode_shared_prefix(
+        a["out"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["tables"], a["lens"], a["pre"],
+        a["S"], a["H"], a["H_kv"], a["D"], a["bs"], a["max_blocks"], a["max_ctx"], a["scale"],
+        a["qd"], a["cd"], a["ps"], a["ws"], a["wsb"], None)
+
+
+def test_shared_prefix_argument_checks():
+    assert _shared(pre=40) == 2                       # not a multiple of the block size
+    assert _shared(pre=1024) == 2                     # longer than the longest context
+    assert _shared(qd=0, cd=0) == 3                   # fp32 queries: plain decode only
+    assert _shared(out=None) == 1
+    assert _shared(cd=2) == 1                         # FP8 without scales
+    assert _shared(ws=None, wsb=0) == 4
+    assert _shared(S=0, out=None, q=None, kc=None, vc=None, tables=None, lens=None) == 0
+    # the prefix's partials (one partition of up to 512 tokens) come before
+    # the suffix partitions' in every row
+    need = pkv.shared_prefix_workspace_size(2, 8, 2, 128, 16, 1000, 64, 1, 1, 0)
+    rows = 2 * 8 * (1 + 2)
+    assert need == 4096 + 2 * ((rows * 4 + 255) // 256 * 256) + (rows * 128 * 4 + 255) // 256 * 256
+    assert _shared(ws=FAKE, wsb=need - 1) == 4
+    # no prefix: plain decode and its workspace
+    assert pkv.shared_prefix_workspace_size(2, 8, 2, 128, 16, 1000, 0, 1, 1, 0) == \
+        pkv.decode_workspace_size(2, 8, 2, 128, 16, 1000, 1, 1, 0)
