@@ -51,7 +51,7 @@ pkv_status_t check_decode_shape(int S, int H, int H_kv, int D, int bs, int max_c
   return PKV_OK;
 }
 
-// Workspace: a 4 KiB header of work-queue counters (16 counters, 256 bytes
+// Workspace: a 4 KiB header of work-queue counters (10 counters, 256 bytes
 // apart), then the split partials (m, l, acc) when a context can span more
 // than one partition.
 constexpr size_t kSchedBytes = 4096;

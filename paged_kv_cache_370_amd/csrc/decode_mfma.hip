@@ -18,8 +18,10 @@
 // blockIdx.x = x mod 8, which the hardware places on XCD x; with the KV head
 // as the fastest item index each XCD's L2 then serves a fixed set of KV
 // heads (blocks shared between sequences come from HBM once per XCD).  The
-// last workgroup of a queue to finish resets its counters to zero for the
-// next call.  Items are software-pipelined: while one item streams, the next
+// last items of the order (about one per workgroup) form a ninth queue that
+// every workgroup serves once its own queue is empty, so XCDs that run
+// slower than the others do not set the end of the kernel.  The last
+// workgroup to finish resets the counters to zero for the next call.  Items are software-pipelined: while one item streams, the next
 // item's block ids and Q are fetched and the item after it is claimed, and
 // each wave issues the next item's first chunk before the merge.
 //
@@ -59,6 +61,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kMaxTable = 256;      // block-table entries one partition may span
@@ -91,8 +94,9 @@ struct MfmaParams {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
-  int* sched;  // claim counter of queue x at [x * kCounterStride], finished-workgroup
-               // counter at [(8 + x) * kCounterStride]
+  int* sched;  // claim counter of queue x at [x * kCounterStride], of the shared
+               // queue at [8 * kCounterStride], finished-workgroup counter at
+               // [9 * kCounterStride]
   int S, H, H_kv, G, chunks, max_blocks, P, NP;
   int M;  // query tokens per sequence (1 for decode)
   // Split attention over a shared prefix (zero / plain values otherwise):
@@ -595,16 +599,21 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   const int q = lane >> 4, r = lane & 15;
   const int Y = p.H_kv * p.chunks;
 
-  // Queue `queue` holds items k * nq + queue.  Its first 2 * queue_wgs items
-  // are taken statically (workgroup b starts with items b and
-  // (queue_wgs + b / nq) * nq + queue, so the launch makes no atomic traffic);
-  // claim c of the queue's counter is item (2 * queue_wgs + c) * nq + queue.
-  // Each claim is made two items ahead, so its latency is hidden.
+  // Items [0, n_local) form the per-XCD queues: queue `queue` holds items
+  // k * nq + queue.  Its first 2 * queue_wgs items are taken statically
+  // (workgroup b starts with items b and (queue_wgs + b / nq) * nq + queue,
+  // so the launch makes no atomic traffic); claim c of the queue's counter
+  // is item (2 * queue_wgs + c) * nq + queue.  Items [n_local, total) form
+  // the shared queue: its claim c is item n_local + c.  A workgroup claims
+  // the item after next at the start of its last chunk step, so the claim's
+  // latency is hidden and a slow workgroup does not hold back an item for
+  // long while others run dry.
   const int nq = min(8, (int)gridDim.x);
   const int queue = blockIdx.x % nq;
   const int queue_wgs = ((int)gridDim.x - queue + nq - 1) / nq;
   int* claim_ctr = p.sched + queue * kCounterStride;
-  int* done_ctr = p.sched + (8 + queue) * kCounterStride;
+  int* shared_ctr = p.sched + 8 * kCounterStride;
+  int* done_ctr = p.sched + 9 * kCounterStride;
   if (tid == 0) {
     s_next[0] = blockIdx.x;
     s_next[1] = (queue_wgs + (int)blockIdx.x / nq) * nq + queue;
@@ -619,6 +628,10 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     total = Y * p.S * p.NP;
     __syncthreads();
   }
+  // About one shared item per workgroup, and never so many that a static
+  // item would fall in the shared range.
+  const int n_local = total - max(0, min((int)gridDim.x, total - 2 * (int)gridDim.x - 16));
+  bool use_shared = false;  // thread 0 only: its own queue is empty
   int cur = s_next[0];
   int nxt = s_next[1];
   int buf = 0;
@@ -661,20 +674,17 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
 
   while (cur < total) {
     // The next item's block ids go to the slice buffer the previous item
-    // used.  Stored first: waiting for them also waits for this item's
-    // first chunk, which the first step needs next, and for nothing issued
-    // later (inside the loop the wait would be placed on every step).
+    // used, inside the chunk loop (below).
     int* wt_nxt = s_wtab[buf ^ 1][wave];
-    store_tab(tab_next, wt_nxt, lane);
-    // Prefetch the next item's Q and claim the item after it.  Nothing reads
-    // the other buffers until the next item.
+    // Prefetch the next item's Q.  Nothing reads the other buffers until the
+    // next item.
     const Item nx = decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len);
     const uint4 q_next = fetch_q<CT, D, MODE>(p, nx.w, tid);
-    // The claim's result is used only after barrier X.  (Only thread 0 sets
-    // and reads it: initialising it in the other lanes would make the
-    // compiler wait for every pending load first.)
+    // The claim of the item after the next one, made at the start of wave
+    // 0's last step (before its loads) and used only after barrier X.
+    // (Only thread 0 sets and reads it: initialising it in the other lanes
+    // would make the compiler wait for every pending load first.)
     int claim;
-    if (tid == 0) claim = atomicAdd(claim_ctr, 1);
 
     f32x4_t acc[Gm::NMD];
 #pragma unroll
@@ -713,6 +723,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     do {
       const int c0 = it.w.start + ci * Gm::CHUNK;
       const bool last = ci + kNW >= nvalid;
+      if (last && tid == 0) claim = atomicAdd(use_shared ? shared_ctr : claim_ctr, 1);
       // Where the prefetch goes: this wave's next chunk of the item, else
       // its first chunk of the next item, else the dummy row (scalar
       // selects, no branch).
@@ -722,7 +733,16 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       const Part lw = to_next ? nx.w : (idle ? dummy_part : it.w);
       const int* ntab = to_next ? wt_nxt : (idle ? s_zero : ctab + EPC);
       const int cn = to_next ? nx.w.start + wave * Gm::CHUNK : (idle ? 0 : c0 + kNW * Gm::CHUNK);
+      // The next item's block ids are written at the wave's second step,
+      // after that step's wait for its V rows: those were requested after
+      // the ids, so the write waits for nothing more.  A wave whose last
+      // step comes first writes them before that step's loads.  (At the top
+      // of the item the write would wait for the previous item's partial
+      // stores as well.)  store_v's wave barrier publishes the write.
+      const bool tab_early = last && ci <= wave + kNW;
+      if (tab_early) wt_nxt[lane] = tab_next;
       store_v<CT, D>(vs, c0, it.w.end, s_v, lane);
+      if (!last && ci == wave + kNW) wt_nxt[lane] = tab_next;
       load_v<CT, D, BS>(vs, p, src, lw, ntab, cn, lane);
       // Keep the scheduler from sinking the prefetch below the products:
       // the loads must be in flight while this chunk is computed.
@@ -750,7 +770,21 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
 
     if (more) store_q<CT, D>(q_next, nx.w, s_qf[buf ^ 1], tid);
     __syncthreads();  // X: V tiles and s_qf[buf] are free; s_qf[buf^1] is complete
-    if (tid == 0) s_next[0] = (2 * queue_wgs + claim) * nq + queue;
+    if (tid == 0) {
+      // A claim past the local items moves this workgroup to the shared
+      // queue for good; that first shared claim is the only one made here.
+      int item;
+      if (!use_shared) {
+        item = (2 * queue_wgs + claim) * nq + queue;
+        if (item >= n_local) {
+          use_shared = true;
+          item = n_local + atomicAdd(shared_ctr, 1);
+        }
+      } else {
+        item = n_local + claim;
+      }
+      s_next[0] = item;
+    }
 
     // Merge the wave-level softmax states of this partition.
     float* s_acc = reinterpret_cast<float*>(s_raw);
@@ -806,9 +840,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
         } else {
           const size_t pi = kSplit<MODE> ? row * p.np_stride + it.part + p.slot_off
                                          : row * p.NP + it.part;
-          // Streaming store: the reduce kernel reads the partial once.
-          const f32x4_t o4 = {O.x, O.y, O.z, O.w};
-          __builtin_nontemporal_store(o4, reinterpret_cast<f32x4_t*>(p.ws_acc + pi * D + d));
+          // bf16 partial output (the result is rounded to bf16 anyway);
+          // streaming store: the reduce kernel reads the partial once.
+          // Partial writes interleaved with the K/V reads cost far more
+          // HBM time than their bytes, so they are kept small.
+          const u32x2_t o4 = {pack_bf16x2(O.x, O.y), pack_bf16x2(O.z, O.w)};
+          __builtin_nontemporal_store(
+              o4, reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(p.ws_acc) + pi * D + d));
           if (d == 0) {
             p.ws_m[pi] = M;
             p.ws_l[pi] = L;
@@ -823,9 +861,10 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     it = nx;
     buf ^= 1;
   }
-  // The last workgroup of this queue to finish returns its counters to zero.
-  if (tid == 0 && atomicAdd(done_ctr, 1) == queue_wgs - 1) {
-    atomicExch(claim_ctr, 0);
+  // The last workgroup to finish returns the counters to zero.
+  if (tid == 0 && atomicAdd(done_ctr, 1) == (int)gridDim.x - 1) {
+    for (int x = 0; x < 8; ++x) atomicExch(p.sched + x * kCounterStride, 0);
+    atomicExch(shared_ctr, 0);
     atomicExch(done_ctr, 0);
   }
 }

@@ -4,6 +4,7 @@
 // the whole context is recovered exactly (up to rounding) by
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p acc_p / sum_p w_p l_p.
 // (Whole-context softmax: dpshk.com PagedAttention article, section 2.2.)
+// acc_p is fp32 for fp32 queries and bf16 for bf16 queries.
 //
 // One workgroup of D threads per (sequence, query token, query head); thread d merges
 // acc_p[d] over the partitions in batches with an online maximum, all in
@@ -46,7 +47,7 @@ __device__ __forceinline__ void merge_chunk(const float (&m)[U], const float (&l
 template <bool OUT_BF16, int D>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(
     void* __restrict__ out, const int32_t* __restrict__ lens, const float* __restrict__ ws_m,
-    const float* __restrict__ ws_l, const float* __restrict__ ws_acc, int H, int P, int NP,
+    const float* __restrict__ ws_l, const void* __restrict__ ws_acc, int H, int P, int NP,
     int M, int pre_slots, int len_off) {
   constexpr int U0 = kFirst, U = kChunk;
   // One workgroup per row (seq * M + t) * H + h: query token t of sequence
@@ -59,11 +60,18 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
   const size_t base = row * NP;
   const float* pm = ws_m + base;
   const float* pl = ws_l + base;
-  const float* pa = ws_acc + base * D + d;
+  // acc_p[d] of partition q, as float
+  auto acc_at = [&](int q) -> float {
+    const size_t i = (base + (size_t)q) * D + d;
+    if constexpr (OUT_BF16)
+      return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(ws_acc)[i] << 16);
+    else
+      return reinterpret_cast<const float*>(ws_acc)[i];
+  };
 
   float m0[U0], l0[U0], a0[U0];
 #pragma unroll
-  for (int u = 0; u < U0; ++u) a0[u] = pa[(size_t)min(u, NP - 1) * D];
+  for (int u = 0; u < U0; ++u) a0[u] = acc_at(min(u, NP - 1));
   // Keep the scheduler from putting these vector loads behind the waits for
   // the scalar loads below.
   __builtin_amdgcn_sched_barrier(0);
@@ -89,7 +97,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
       const int q = min(q0 + u, np - 1);
       mm[u] = pm[q];
       l[u] = pl[q];
-      a[u] = pa[(size_t)q * D];
+      a[u] = acc_at(q);
     }
     merge_chunk<U>(mm, l, a, q0, np, Mx, L, O);
   }

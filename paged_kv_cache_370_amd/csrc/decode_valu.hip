@@ -207,7 +207,8 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(ValuParams p) {
       else reinterpret_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(o);
     } else {
       const size_t pi = ((size_t)seq * H + h) * p.NP + part;
-      p.ws_acc[pi * D + d] = O;
+      if constexpr (sizeof(typename QT::storage) == 4) p.ws_acc[pi * D + d] = O;
+      else reinterpret_cast<uint16_t*>(p.ws_acc)[pi * D + d] = f32_to_bf16(O);
       if (d == 0) {
         p.ws_m[pi] = M;
         p.ws_l[pi] = L;

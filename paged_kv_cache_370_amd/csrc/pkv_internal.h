@@ -50,7 +50,9 @@ struct DecodeArgs {
                   // between calls
   float* ws_m;    // [S][H][NP]  running max (base-2 units) per partition
   float* ws_l;    // [S][H][NP]  running sum per partition
-  float* ws_acc;  // [S][H][NP][D]  unnormalised output per partition
+  float* ws_acc;  // [S][H][NP][D]  unnormalised output per partition: fp32 for
+                  // fp32 queries, bf16 (in the first half of the region) for
+                  // bf16 queries, whose output is bf16 anyway
   hipStream_t stream;
 };
 

@@ -529,10 +529,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
       }
     } else {
       const size_t pi = orow[j] * p.NP + part;
-      float* o = p.ws_acc + pi * D + 4 * q4;
+      // bf16 partial outputs, as the decode kernel writes them.
+      uint16_t* o = reinterpret_cast<uint16_t*>(p.ws_acc) + pi * D + 4 * q4;
 #pragma unroll
-      for (int md = 0; md < L::NMD; ++md)
-        __builtin_nontemporal_store(acc[j][md], reinterpret_cast<f32x4_v*>(o + 16 * md));
+      for (int md = 0; md < L::NMD; ++md) {
+        typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_v;
+        const f32x4_v a = acc[j][md];
+        const u32x2_v w = {bf16x2_rne(a[0], a[1]), bf16x2_rne(a[2], a[3])};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2_v*>(o + 16 * md));
+      }
       if (q4 == 0) {
         p.ws_m[pi] = m[j];
         p.ws_l[pi] = l[j];
