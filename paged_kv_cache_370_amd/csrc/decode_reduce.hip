@@ -6,11 +6,12 @@
 // (Whole-context softmax: dpshk.com PagedAttention article, section 2.2.)
 // acc_p is fp32 for fp32 queries and bf16 for bf16 queries.
 //
-// One workgroup of D threads per (sequence, query token, query head); thread d merges
-// acc_p[d] over the partitions in batches with an online maximum, all in
-// registers.  The first batch's loads do not wait for the context length:
-// they are clamped to the NP partition rows the workspace holds for every
-// sequence, so they are in flight together with the load of the length.
+// One workgroup per (sequence, query token, query head); a thread merges
+// acc_p[d] (two adjacent d for bf16 partials) over the partitions in
+// batches with an online maximum, all in registers.  The first batch's
+// loads do not wait for the context length: they are clamped to the NP
+// partition rows the workspace holds for every sequence, so they are in
+// flight together with the load of the length.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -21,10 +22,10 @@ constexpr int kFirst = 4;   // partitions loaded before the context length is kn
 constexpr int kChunk = 16;  // partitions per later batch of independent loads
 
 // Fold partitions [q0, q0 + U) (those below np) into the running (M, L, O).
-template <int U>
+template <int U, int E>
 __device__ __forceinline__ void merge_chunk(const float (&m)[U], const float (&l)[U],
-                                            const float (&a)[U], int q0, int np, float& M,
-                                            float& L, float& O) {
+                                            const float (&a)[U][E], int q0, int np, float& M,
+                                            float& L, float (&O)[E]) {
   float mc = kNegInf;
 #pragma unroll
   for (int u = 0; u < U; ++u)
@@ -32,20 +33,24 @@ __device__ __forceinline__ void merge_chunk(const float (&m)[U], const float (&l
   const float mn = fmaxf(M, mc);  // finite: every partition below np holds tokens
   const float r = __builtin_amdgcn_exp2f(M - mn);  // 0 while M is still -inf
   L *= r;
-  O *= r;
+#pragma unroll
+  for (int e = 0; e < E; ++e) O[e] *= r;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (q0 + u < np) {
       const float w = __builtin_amdgcn_exp2f(m[u] - mn);
       L = fmaf(l[u], w, L);
-      O = fmaf(a[u], w, O);
+#pragma unroll
+      for (int e = 0; e < E; ++e) O[e] = fmaf(a[u][e], w, O[e]);
     }
   }
   M = mn;
 }
 
+// bf16 partials: each thread merges two adjacent elements (one 4-byte load
+// per partition); fp32 partials: one element per thread.
 template <bool OUT_BF16, int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(
+__global__ __launch_bounds__(OUT_BF16 ? D / 2 : D) void decode_reduce_kernel(
     void* __restrict__ out, const int32_t* __restrict__ lens, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const void* __restrict__ ws_acc, int H, int P, int NP,
     int M, int pre_slots, int len_off) {
@@ -56,22 +61,27 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
   const int st = (int)(row / H);
   const int seq = st / M;
   const int t = st - seq * M;
-  const int d = threadIdx.x;
+  constexpr int E = OUT_BF16 ? 2 : 1;
+  const int d = threadIdx.x * E;
   const size_t base = row * NP;
   const float* pm = ws_m + base;
   const float* pl = ws_l + base;
-  // acc_p[d] of partition q, as float
-  auto acc_at = [&](int q) -> float {
+  // acc_p[d .. d + E) of partition q, as floats
+  auto acc_at = [&](int q, float (&v)[E]) {
     const size_t i = (base + (size_t)q) * D + d;
-    if constexpr (OUT_BF16)
-      return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(ws_acc)[i] << 16);
-    else
-      return reinterpret_cast<const float*>(ws_acc)[i];
+    if constexpr (OUT_BF16) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(
+          reinterpret_cast<const uint16_t*>(ws_acc) + i);
+      v[0] = bf16_lo(w);
+      v[1] = bf16_hi(w);
+    } else {
+      v[0] = reinterpret_cast<const float*>(ws_acc)[i];
+    }
   };
 
-  float m0[U0], l0[U0], a0[U0];
+  float m0[U0], l0[U0], a0[U0][E];
 #pragma unroll
-  for (int u = 0; u < U0; ++u) a0[u] = acc_at(min(u, NP - 1));
+  for (int u = 0; u < U0; ++u) acc_at(min(u, NP - 1), a0[u]);
   // Keep the scheduler from putting these vector loads behind the waits for
   // the scalar loads below.
   __builtin_amdgcn_sched_barrier(0);
@@ -88,34 +98,40 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
   // partitions cover the positions from len_off on.
   const int end = n - M + t + 1;
   const int np = pre_slots + (max(end - len_off, 0) + P - 1) / P;
-  float Mx = kNegInf, L = 0.f, O = 0.f;
-  merge_chunk<U0>(m0, l0, a0, 0, np, Mx, L, O);
+  float Mx = kNegInf, L = 0.f, O[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) O[e] = 0.f;
+  merge_chunk<U0, E>(m0, l0, a0, 0, np, Mx, L, O);
   for (int q0 = U0; q0 < np; q0 += U) {
-    float mm[U], l[U], a[U];
+    float mm[U], l[U], a[U][E];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int q = min(q0 + u, np - 1);
       mm[u] = pm[q];
       l[u] = pl[q];
-      a[u] = acc_at(q);
+      acc_at(q, a[u]);
     }
-    merge_chunk<U>(mm, l, a, q0, np, Mx, L, O);
+    merge_chunk<U, E>(mm, l, a, q0, np, Mx, L, O);
   }
   // No branch before this point, so the first chunk's loads are issued
   // before the length arrives.  A sequence of at most P tokens was written
   // directly by the partition kernel.
   if (pre_slots == 0 && n <= P) return;
-  const float res = L > 0.f ? O / L : 0.f;
   const size_t oi = row * D + d;
-  if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16(res);
-  else reinterpret_cast<float*>(out)[oi] = res;
+  if constexpr (OUT_BF16) {
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + oi) =
+        (uint32_t)f32_to_bf16(L > 0.f ? O[0] / L : 0.f) |
+        ((uint32_t)f32_to_bf16(L > 0.f ? O[1] / L : 0.f) << 16);
+  } else {
+    reinterpret_cast<float*>(out)[oi] = L > 0.f ? O[0] / L : 0.f;
+  }
 }
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a) {
   const unsigned grid = (unsigned)((size_t)a.S * a.M * a.H);
   if (a.q_dtype == PKV_BF16) {
-    hipLaunchKernelGGL((decode_reduce_kernel<true, D>), grid, dim3(D), 0, a.stream, a.out, a.lens,
+    hipLaunchKernelGGL((decode_reduce_kernel<true, D>), grid, dim3(D / 2), 0, a.stream, a.out, a.lens,
                        a.ws_m, a.ws_l, a.ws_acc, a.H, a.P, a.NP, a.M, a.prefix_slots,
                        a.len_off);
   } else {
