@@ -637,15 +637,20 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   int buf = 0;
   constexpr int EPC = Gm::CHUNK / BS;  // block ids per chunk
   Item it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, s_full, s_rag, s_len);
-  if (cur < total) {
-    store_tab(fetch_tab<CT, D, BS>(p, it.w, wave, lane), s_wtab[0][wave], lane);
-    store_q<CT, D>(fetch_q<CT, D, MODE>(p, it.w, tid), it.w, s_qf[0], tid);
-  }
-  // The second item's block ids travel in a register until the first
-  // item's last chunk (each item's are fetched one item ahead).
+  // The first item's block ids and Q and the second item's block ids are
+  // requested together (one memory round trip before the first chunk's
+  // loads, not three).  The second item's ids travel in a register until
+  // the first item's loop stores them (each item's are fetched one item
+  // ahead).
+  const int tab_first = fetch_tab<CT, D, BS>(p, it.w, wave, lane);
+  const uint4 q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
   int tab_next = fetch_tab<CT, D, BS>(
       p, decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len).w, wave,
       lane);
+  if (cur < total) {
+    store_tab(tab_first, s_wtab[0][wave], lane);
+    store_q<CT, D>(q_first, it.w, s_qf[0], tid);
+  }
   __syncthreads();
 
   const Src cache{p.kc, p.vc, p.ks, p.vs};
