@@ -134,7 +134,9 @@ size_t paged_kv_cache_write_workspace_size(
  *   the host never reads device memory.
  *   partition_size (tokens, multiple of bs, or 0 = library choice): contexts
  *   longer than one partition are split, each partition is attended on its
- *   own, and a second kernel merges the partial results.
+ *   own, and a second kernel merges the partial results (each partition's
+ *   running maximum and sum in float32, its unnormalised output in float32
+ *   for F32 queries and in bf16 for BF16 queries, whose output is bf16).
  *   workspace: at least paged_attention_decode_workspace_size(...) bytes
  *   (always >= 4096).  Its first 4096 bytes are work-queue counters: they
  *   must be zero before the first call that uses the workspace (allocate it
