@@ -92,6 +92,47 @@ def test_random_shapes(seed):
     assert np.all(out_f64(out)[np.asarray(lens) == 0] == 0)
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_batch_beyond_the_scan_limit(cache):
+    """More sequences than a workgroup scans in LDS (512): the decode kernel
+    walks (sequence, partition) items directly, with placeholders past each
+    sequence's end."""
+    rng = np.random.default_rng(61)
+    S = 600
+    lens = rng.integers(1, 300, size=S)
+    lens[[5, 77]] = 0
+    w = workloads.build_workload(f"wide-batch-{cache}", S, 4, 2, 128, 16, "bf16", cache, lens, 61,
+                                 fill="write" if cache == "fp8" else "random")
+    _say(f"case batch S={S} cache={cache}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle_decode(w, kc, vc, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    _check_caches(dw, kc, vc, ks, vs)
+    for ps in (0, 64):
+        err = max_err(out_f64(dw.decode(partition_size=ps)), ref)
+        _say(f"  ps={ps} max_err={err:.3e}")
+        assert err <= TOL[cache], (ps, err)
+
+
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+def test_more_than_sixteen_heads_per_kv_head(cache):
+    """40 query heads over one KV head (the matrix-core kernel takes them in
+    three 16-row chunks, the vector kernel in 8-head chunks)."""
+    qd = "f32" if cache == "f32" else "bf16"
+    w = workloads.build_workload(f"g40-{cache}", 3, 40, 1, 128, 16, qd, cache, [900, 513, 7], 62,
+                                 fill="write" if cache == "fp8" else "random")
+    _say(f"case G=40 cache={cache}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle_decode(w, kc, vc, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    for ps in (0, 256):
+        err = max_err(out_f64(dw.decode(partition_size=ps)), ref)
+        _say(f"  ps={ps} max_err={err:.3e}")
+        assert err <= TOL[cache], (ps, err)
+
+
 def test_single_token_is_exact():
     for cache, qd in (("f32", "f32"), ("bf16", "bf16")):
         w = workloads.build_workload("one", 3, 8, 2, 128, 16, qd, cache, [1, 1, 1], 7,
