@@ -132,8 +132,9 @@ size_t paged_kv_cache_write_workspace_size(
  *   likewise); scales are ignored otherwise (may be NULL).
  *   max_context_len must be >= every context_lens[i]; it sizes the grid so
  *   the host never reads device memory.
- *   partition_size (tokens, multiple of bs, or 0 = library choice): contexts
- *   longer than one partition are split, each partition is attended on its
+ *   partition_size (tokens, multiple of bs, or 0 = library choice: the
+ *   whole context up to 512 tokens, 1024 for FP8 caches, else partitions of
+ *   that size): contexts longer than one partition are split, each partition is attended on its
  *   own, and a second kernel merges the partial results (each partition's
  *   running maximum and sum in float32, its unnormalised output in float32
  *   for F32 queries and in bf16 for BF16 queries, whose output is bf16).

@@ -26,16 +26,20 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Partition size in tokens, or -1.  A context that fits one partition is
 // finished by the partition kernel itself; longer contexts are split into
-// partitions of kDefaultPartition tokens so that long sequences spread over
-// many workgroups.
-int resolve_partition(int bs, int max_ctx, int requested) {
+// partitions of kDefaultPartition tokens (twice that for FP8 caches, so a
+// partition holds the same K/V bytes and the per-item costs, the merge and
+// the partial store, are spread over as many bytes; on the FP8 workload
+// 1024-token partitions took 169 us against 176 us) so that long sequences
+// spread over many workgroups.
+int resolve_partition(int bs, int max_ctx, int requested, int cache_dtype) {
   if (requested < 0) return -1;
   if (requested > 0) return requested % bs == 0 ? requested : -1;
-  if (max_ctx <= kDefaultPartition) {
+  const int def = cache_dtype == PKV_FP8_E4M3 ? 2 * kDefaultPartition : kDefaultPartition;
+  if (max_ctx <= def) {
     const int p = ((max_ctx + bs - 1) / bs) * bs;
     return p < bs ? bs : p;
   }
-  return kDefaultPartition;
+  return def;
 }
 
 int num_partitions(int max_ctx, int P) {
@@ -84,7 +88,7 @@ DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
     r.status = PKV_ERR_SHAPE;
     return r;
   }
-  const int P = resolve_partition(bs, max_ctx, partition);
+  const int P = resolve_partition(bs, max_ctx, partition, c);
   if (P <= 0) {
     r.status = PKV_ERR_SHAPE;
     return r;
@@ -233,7 +237,7 @@ int32_t paged_attention_decode_partition_size(int32_t num_seqs, int32_t num_head
   if (check_decode_shape(num_seqs, num_heads, num_kv_heads, head_size, block_size,
                          max_context_len, q_dtype, cache_dtype) != PKV_OK)
     return -1;
-  return resolve_partition(block_size, max_context_len, partition_size);
+  return resolve_partition(block_size, max_context_len, partition_size, cache_dtype);
 }
 
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
@@ -309,10 +313,12 @@ struct PrefixSplit {
   int P = -1, pre_slots = 0, suf_slots = 0;
 };
 
-static PrefixSplit prefix_split(int bs, int max_ctx, int prefix, int requested) {
+static PrefixSplit prefix_split(int bs, int max_ctx, int prefix, int requested,
+                                int cache_dtype) {
   PrefixSplit sp;
   if (prefix <= 0 || prefix % bs != 0 || prefix > max_ctx) return sp;
-  sp.P = resolve_partition(bs, max_ctx - prefix > 0 ? max_ctx - prefix : bs, requested);
+  sp.P = resolve_partition(bs, max_ctx - prefix > 0 ? max_ctx - prefix : bs, requested,
+                           cache_dtype);
   if (sp.P <= 0) return sp;
   sp.pre_slots = (prefix + sp.P - 1) / sp.P;
   sp.suf_slots = num_partitions(max_ctx - prefix, sp.P);
@@ -348,7 +354,7 @@ static PrefillPlan prefill_plan(int S, int M, int H, int H_kv, int D, int bs, in
   const long long rows = (long long)M * (H / H_kv);
   pl.tiled = c == PKV_BF16 && rows >= kTileMinRows;
   if (!pl.tiled) {
-    pl.P = resolve_partition(bs, max_ctx, requested);
+    pl.P = resolve_partition(bs, max_ctx, requested, c);
     return pl;
   }
   if (requested != 0) {
@@ -424,7 +430,8 @@ pkv_status_t paged_attention_decode_shared_prefix(
                                                 block_size, max_context_len, q_dtype, cache_dtype);
   if (shape != PKV_OK) return shape;
   if (q_dtype != PKV_BF16) return PKV_ERR_DTYPE;  // rows of many sequences: matrix cores
-  const PrefixSplit sp = prefix_split(block_size, max_context_len, prefix_tokens, partition_size);
+  const PrefixSplit sp =
+      prefix_split(block_size, max_context_len, prefix_tokens, partition_size, cache_dtype);
   if (sp.P <= 0) return PKV_ERR_SHAPE;
   DecodeSetup s = setup_decode(out, query, key_cache, value_cache, key_scale, value_scale,
                                block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
@@ -486,7 +493,8 @@ size_t paged_attention_decode_shared_prefix_workspace_size(
                          max_context_len, q_dtype, cache_dtype) != PKV_OK ||
       q_dtype != PKV_BF16)
     return 0;
-  const PrefixSplit sp = prefix_split(block_size, max_context_len, prefix_tokens, partition_size);
+  const PrefixSplit sp =
+      prefix_split(block_size, max_context_len, prefix_tokens, partition_size, cache_dtype);
   if (sp.P <= 0) return 0;
   return shared_prefix_workspace(num_seqs, num_heads, head_size, sp);
 }

@@ -47,6 +47,10 @@ def test_status_strings_and_version():
 def test_partition_and_workspace_queries():
     # context fits one partition: only the 4 KiB work-queue header
     assert pkv.decode_partition_size(4, 8, 8, 128, 16, 300, 1, 1, 0) == 304
+    # library choice: 512-token partitions for bf16 caches, 1024 for FP8
+    assert pkv.decode_partition_size(8, 64, 8, 128, 8, 32768, 1, 1, 0) == 512
+    assert pkv.decode_partition_size(256, 40, 8, 128, 16, 8192, 1, 2, 0) == 1024
+    assert pkv.decode_partition_size(256, 40, 8, 128, 16, 900, 1, 2, 0) == 912
     assert pkv.decode_workspace_size(4, 8, 8, 128, 16, 300, 1, 1, 0) == 4096
     # long contexts: 512-token partitions, partials for m, l and acc
     assert pkv.decode_partition_size(8, 64, 8, 128, 8, 32768, 1, 1, 512) == 512
