@@ -21,9 +21,10 @@
 // last items of the order (about one per workgroup) form a ninth queue that
 // every workgroup serves once its own queue is empty, so XCDs that run
 // slower than the others do not set the end of the kernel.  The last
-// workgroup to finish resets the counters to zero for the next call.  Items are software-pipelined: while one item streams, the next
-// item's block ids and Q are fetched and the item after it is claimed, and
-// each wave issues the next item's first chunk before the merge.
+// workgroup to finish resets the counters to zero for the next call.
+// Items are software-pipelined: while one item streams, the next item's
+// block ids and Q are fetched, the item after it is claimed during the last
+// step, and each wave issues the next item's first chunk before the merge.
 //
 // Why MFMA: the query heads that share a KV head turn both products into
 // small dense contractions, [16 tokens x D] . [D x 16 heads] for the scores
