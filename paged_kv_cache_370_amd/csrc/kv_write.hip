@@ -61,43 +61,79 @@ __global__ __launch_bounds__(64) void fp8_clear_kernel(
   if (threadIdx.x == 0) fresh[b] = 0;
 }
 
+// Row geometry of the FP8 write kernels: a lane handles VEC consecutive
+// source elements (one 16-byte load), LPR lanes cover a (token, KV head) row
+// of D elements, and a wave handles RPW rows at once.
 template <typename ST, int D>
-__device__ __forceinline__ float src_elem(const ST* p, int i) {
-  if constexpr (sizeof(ST) == 4) return p[i];
-  else return __uint_as_float((uint32_t)p[i] << 16);
+struct Fp8Rows {
+  static constexpr int VEC = 16 / (int)sizeof(ST);
+  static constexpr int LPR = D / VEC;
+  static constexpr int RPW = 64 / LPR;
+};
+
+// The lane's VEC source elements as floats (bf16 bits or fp32).
+template <typename ST>
+__device__ __forceinline__ void load_src(const ST* p, float (&x)[16 / sizeof(ST)]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  if constexpr (sizeof(ST) == 4) {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_lo(w[i]);
+      x[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
 }
 
-// One wave per (token, KV head); lanes stride over D for K and V.
+// Maximum over the LPR lanes of a row (aligned groups of LPR lanes).
+template <int LPR>
+__device__ __forceinline__ float row_group_max(float x) {
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+// Per (token, KV head) row: amax of |K| and |V| over the row, folded into the
+// block's entry with atomicMax on the float bits (NaN wins, as in an ordinary
+// maximum), and the block marked fresh when the row is its offset 0.
 template <typename ST, int D>
 __global__ __launch_bounds__(256) void fp8_amax_kernel(
     const ST* __restrict__ key, const ST* __restrict__ value,
     const int32_t* __restrict__ slots, int T, int bs, int H_kv,
     int32_t* __restrict__ fresh, uint32_t* __restrict__ amax) {
-  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  using R = Fp8Rows<ST, D>;
+  const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
-  if (wave >= T * H_kv) return;
-  const int t = wave / H_kv;
-  const int h = wave - t * H_kv;
-  const int s = slots[t];
-  if (s < 0) return;
-  const int b = s / bs;
-  const int o = s - b * bs;
-  const ST* kp = key + ((size_t)t * H_kv + h) * D;
-  const ST* vp = value + ((size_t)t * H_kv + h) * D;
-  float mk = 0.f, mv = 0.f;
+  const int row = gw * R::RPW + lane / R::LPR;
+  const int part = lane % R::LPR;
+  const bool ok = row < T * H_kv;
+  const int rr = ok ? row : 0;
+  const int t = rr / H_kv;
+  const int h = rr - t * H_kv;
+  float xk[R::VEC], xv[R::VEC];
+  load_src<ST>(key + (size_t)rr * D + part * R::VEC, xk);
+  load_src<ST>(value + (size_t)rr * D + part * R::VEC, xv);
+  float mk = 0.f, mv = 0.f, nk = 0.f, nv = 0.f;
 #pragma unroll
-  for (int d = lane; d < D; d += 64) {
-    mk = fmaxf(mk, fabsf(src_elem<ST, D>(kp, d)));
-    mv = fmaxf(mv, fabsf(src_elem<ST, D>(vp, d)));
+  for (int i = 0; i < R::VEC; ++i) {
+    mk = fmaxf(mk, fabsf(xk[i]));
+    mv = fmaxf(mv, fabsf(xv[i]));
+    nk = (xk[i] != xk[i]) ? 1.f : nk;
+    nv = (xv[i] != xv[i]) ? 1.f : nv;
   }
-  // NaN must win the maximum, as it does in an ordinary max over the values.
-  const float nk = (mk != mk) ? 1.f : 0.f, nv = (mv != mv) ? 1.f : 0.f;
-  mk = wave_max(mk);
-  mv = wave_max(mv);
-  const float any_nk = wave_max(nk), any_nv = wave_max(nv);
-  if (lane == 0) {
-    uint32_t bk = any_nk > 0.f ? 0x7fc00000u : __float_as_uint(mk);
-    uint32_t bv = any_nv > 0.f ? 0x7fc00000u : __float_as_uint(mv);
+  mk = row_group_max<R::LPR>(mk);
+  mv = row_group_max<R::LPR>(mv);
+  nk = row_group_max<R::LPR>(nk);
+  nv = row_group_max<R::LPR>(nv);
+  const int s = ok ? slots[t] : -1;
+  if (part == 0 && s >= 0) {
+    const int b = s / bs;
+    const int o = s - b * bs;
+    const uint32_t bk = nk > 0.f ? 0x7fc00000u : __float_as_uint(mk);
+    const uint32_t bv = nv > 0.f ? 0x7fc00000u : __float_as_uint(mv);
     atomicMax(&amax[((size_t)b * H_kv + h) * 2 + 0], bk);
     atomicMax(&amax[((size_t)b * H_kv + h) * 2 + 1], bv);
     if (o == 0 && h == 0) fresh[b] = 1;
@@ -110,7 +146,9 @@ __device__ __forceinline__ float fp8_scale_from_amax(uint32_t bits) {
   return (s < flt_min) ? flt_min : s;  // NaN stays NaN
 }
 
-// One wave per (token, KV head): encode D elements of K and of V.
+// Per (token, KV head) row: the block's scales (set from amax when the
+// block is fresh, else the stored ones), then the row's codes, VEC per lane
+// in one store.
 template <typename ST, int D>
 __global__ __launch_bounds__(256) void fp8_quant_kernel(
     const ST* __restrict__ key, const ST* __restrict__ value,
@@ -118,21 +156,27 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(
     float* __restrict__ key_scale, float* __restrict__ value_scale,
     const int32_t* __restrict__ slots, int T, int bs, int H_kv,
     const int32_t* __restrict__ fresh, const uint32_t* __restrict__ amax) {
-  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  using R = Fp8Rows<ST, D>;
+  const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
-  if (wave >= T * H_kv) return;
-  const int t = wave / H_kv;
-  const int h = wave - t * H_kv;
+  const int row = gw * R::RPW + lane / R::LPR;
+  const int part = lane % R::LPR;
+  if (row >= T * H_kv) return;
+  const int t = row / H_kv;
+  const int h = row - t * H_kv;
   const int s = slots[t];
   if (s < 0) return;
   const int b = s / bs;
   const int o = s - b * bs;
   const size_t sidx = (size_t)b * H_kv + h;
+  float xk[R::VEC], xv[R::VEC];
+  load_src<ST>(key + (size_t)row * D + part * R::VEC, xk);
+  load_src<ST>(value + (size_t)row * D + part * R::VEC, xv);
   float sk, sv;
   if (fresh[b]) {
     sk = fp8_scale_from_amax(amax[sidx * 2 + 0]);
     sv = fp8_scale_from_amax(amax[sidx * 2 + 1]);
-    if (lane == 0) {  // every token of the block stores the same value
+    if (part == 0) {  // every token of the block stores the same value
       key_scale[sidx] = sk;
       value_scale[sidx] = sv;
     }
@@ -140,17 +184,27 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(
     sk = key_scale[sidx];
     sv = value_scale[sidx];
   }
-  const ST* kp = key + ((size_t)t * H_kv + h) * D;
-  const ST* vp = value + ((size_t)t * H_kv + h) * D;
-  uint8_t* kd = key_cache + (sidx * bs + o) * D;
-  uint8_t* vd = value_cache + (sidx * bs + o) * D;
   // Correctly rounded float32 quotient: the double quotient rounded once more
   // to float equals the float quotient (53 >= 2*24 + 2).
   const double dk = (double)sk, dv = (double)sv;
+  uint32_t ck[R::VEC / 4], cv[R::VEC / 4];
 #pragma unroll
-  for (int d = lane; d < D; d += 64) {
-    kd[d] = (uint8_t)f32_to_e4m3((float)((double)src_elem<ST, D>(kp, d) / dk));
-    vd[d] = (uint8_t)f32_to_e4m3((float)((double)src_elem<ST, D>(vp, d) / dv));
+  for (int i = 0; i < R::VEC / 4; ++i) {
+    ck[i] = cv[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ck[i] |= f32_to_e4m3((float)((double)xk[4 * i + j] / dk)) << (8 * j);
+      cv[i] |= f32_to_e4m3((float)((double)xv[4 * i + j] / dv)) << (8 * j);
+    }
+  }
+  uint8_t* kd = key_cache + (sidx * bs + o) * D + part * R::VEC;
+  uint8_t* vd = value_cache + (sidx * bs + o) * D + part * R::VEC;
+  if constexpr (R::VEC == 8) {
+    *reinterpret_cast<uint2*>(kd) = make_uint2(ck[0], ck[1]);
+    *reinterpret_cast<uint2*>(vd) = make_uint2(cv[0], cv[1]);
+  } else {
+    *reinterpret_cast<uint32_t*>(kd) = ck[0];
+    *reinterpret_cast<uint32_t*>(vd) = cv[0];
   }
 }
 
@@ -162,7 +216,8 @@ hipError_t fp8_launch(const WriteArgs& a) {
   const ST* value = reinterpret_cast<const ST*>(a.value);
   hipLaunchKernelGGL(fp8_clear_kernel, dim3(a.T), dim3(64), 0, a.stream, a.slots, a.T, a.bs,
                      a.H_kv, fresh, amax);
-  const int waves = a.T * a.H_kv;
+  const int rows = a.T * a.H_kv;
+  const int waves = (rows + Fp8Rows<ST, D>::RPW - 1) / Fp8Rows<ST, D>::RPW;
   const int blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((fp8_amax_kernel<ST, D>), dim3(blocks), dim3(256), 0, a.stream, key, value,
                      a.slots, a.T, a.bs, a.H_kv, fresh, amax);
