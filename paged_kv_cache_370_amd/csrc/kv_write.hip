@@ -49,16 +49,18 @@ __global__ __launch_bounds__(256) void kv_write_copy_kernel(
 //      floats order like their unsigned bit patterns);
 //   3. pick the scale (fresh: from amax; else the stored one) and encode.
 
-__global__ __launch_bounds__(64) void fp8_clear_kernel(
+// One thread per token (tokens of one block write the same zeros).
+__global__ __launch_bounds__(256) void fp8_clear_kernel(
     const int32_t* __restrict__ slots, int T, int bs, int H_kv,
     int32_t* __restrict__ fresh, uint32_t* __restrict__ amax) {
-  const int t = blockIdx.x;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const int s = slots[t];
   if (s < 0) return;
   const int b = s / bs;
-  for (int i = threadIdx.x; i < 2 * H_kv; i += blockDim.x) amax[(size_t)b * 2 * H_kv + i] = 0u;
-  if (threadIdx.x == 0) fresh[b] = 0;
+  uint32_t* a = amax + (size_t)b * 2 * H_kv;
+  for (int i = 0; i < 2 * H_kv; ++i) a[i] = 0u;
+  fresh[b] = 0;
 }
 
 // Row geometry of the FP8 write kernels: a lane handles VEC consecutive
@@ -214,8 +216,8 @@ hipError_t fp8_launch(const WriteArgs& a) {
   uint32_t* amax = reinterpret_cast<uint32_t*>(fresh + ((a.num_blocks + 63) / 64) * 64);
   const ST* key = reinterpret_cast<const ST*>(a.key);
   const ST* value = reinterpret_cast<const ST*>(a.value);
-  hipLaunchKernelGGL(fp8_clear_kernel, dim3(a.T), dim3(64), 0, a.stream, a.slots, a.T, a.bs,
-                     a.H_kv, fresh, amax);
+  hipLaunchKernelGGL(fp8_clear_kernel, dim3((a.T + 255) / 256), dim3(256), 0, a.stream, a.slots,
+                     a.T, a.bs, a.H_kv, fresh, amax);
   const int rows = a.T * a.H_kv;
   const int waves = (rows + Fp8Rows<ST, D>::RPW - 1) / Fp8Rows<ST, D>::RPW;
   const int blocks = (waves + 3) / 4;
