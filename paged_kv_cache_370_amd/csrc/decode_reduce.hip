@@ -21,6 +21,7 @@ namespace pkv {
 namespace {
 
 constexpr int kFirst = 4;   // partitions loaded before the context length is known
+constexpr int kFirstWide = 16;  // the same with several thread groups per row
 constexpr int kChunk = 16;  // partitions per later batch of independent loads
 constexpr int kRowWaves = 4;  // most thread groups that split one row's partition slots
 
@@ -58,12 +59,12 @@ __device__ __forceinline__ void merge_chunk(const float (&m)[U], const float (&l
 // D = 128) take a contiguous share of the slots each, so a long context's
 // partials are read in few round trips; the groups' states merge through
 // LDS.
-template <bool OUT_BF16, int D>
+template <bool OUT_BF16, int D, int U0>
 __global__ __launch_bounds__((OUT_BF16 ? D / 2 : D) * kRowWaves) void decode_reduce_kernel(
     void* __restrict__ out, const int32_t* __restrict__ lens, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const void* __restrict__ ws_acc, int H, int P, int NP,
     int M, int pre_slots, int len_off) {
-  constexpr int U0 = kFirst, U = kChunk;
+  constexpr int U = kChunk;
   constexpr int E = OUT_BF16 ? 2 : 1;
   constexpr int TPR = D / E;  // threads per group
   __shared__ float s_M[kRowWaves], s_L[kRowWaves];
@@ -180,20 +181,27 @@ __global__ __launch_bounds__((OUT_BF16 ? D / 2 : D) * kRowWaves) void decode_red
 // long contexts (32K tokens in 512-token partitions: 10.6 -> 8.0 us).
 int row_groups(int NP) { return NP > 32 ? kRowWaves : (NP > 8 ? 2 : 1); }
 
+template <bool OUT_BF16, int D, int U0>
+hipError_t launch_u(const DecodeArgs& a, int groups) {
+  const unsigned grid = (unsigned)((size_t)a.S * a.M * a.H);
+  hipLaunchKernelGGL((decode_reduce_kernel<OUT_BF16, D, U0>), grid,
+                     dim3((OUT_BF16 ? D / 2 : D) * groups), 0, a.stream, a.out, a.lens, a.ws_m,
+                     a.ws_l, a.ws_acc, a.H, a.P, a.NP, a.M, a.prefix_slots, a.len_off);
+  return hipGetLastError();
+}
+
+// With several groups per row each group's first batch is its whole share
+// of up to 16 slots, in flight before the context length arrives.
+template <bool OUT_BF16, int D>
+hipError_t launch_q(const DecodeArgs& a) {
+  const int groups = row_groups(a.NP);
+  return groups > 1 ? launch_u<OUT_BF16, D, kFirstWide>(a, groups)
+                    : launch_u<OUT_BF16, D, kFirst>(a, groups);
+}
+
 template <int D>
 hipError_t launch_d(const DecodeArgs& a) {
-  const unsigned grid = (unsigned)((size_t)a.S * a.M * a.H);
-  const int groups = row_groups(a.NP);
-  if (a.q_dtype == PKV_BF16) {
-    hipLaunchKernelGGL((decode_reduce_kernel<true, D>), grid, dim3(D / 2 * groups), 0,
-                       a.stream, a.out, a.lens, a.ws_m, a.ws_l, a.ws_acc, a.H, a.P, a.NP, a.M,
-                       a.prefix_slots, a.len_off);
-  } else {
-    hipLaunchKernelGGL((decode_reduce_kernel<false, D>), grid, dim3(D * groups), 0,
-                       a.stream, a.out, a.lens, a.ws_m, a.ws_l, a.ws_acc, a.H, a.P, a.NP, a.M,
-                       a.prefix_slots, a.len_off);
-  }
-  return hipGetLastError();
+  return a.q_dtype == PKV_BF16 ? launch_q<true, D>(a) : launch_q<false, D>(a);
 }
 
 }  // namespace
