@@ -354,6 +354,17 @@ static PrefillPlan prefill_plan(int S, int M, int H, int H_kv, int D, int bs, in
   const long long rows = (long long)M * (H / H_kv);
   pl.tiled = c == PKV_BF16 && rows >= kTileMinRows;
   if (!pl.tiled) {
+    // Several tokens per sequence on the decode kernel: an item's partial
+    // output is M * G rows wide, so with enough items to give every CU two
+    // (S x KV heads x 16-row chunks >= 512) a context is not split at all
+    // when its blocks fit one item: no partials and no merge (beams over
+    // forked tables, 64 beams x 4 tokens over 2069 positions: 78 -> 50 us).
+    const long long items = (long long)S * H_kv * ((rows + 15) / 16);
+    const int whole = ((max_ctx + bs - 1) / bs) * bs;
+    if (requested == 0 && items >= 512 && whole <= kDecodeMaxTable * bs) {
+      pl.P = whole < bs ? bs : whole;
+      return pl;
+    }
     pl.P = resolve_partition(bs, max_ctx, requested, c);
     return pl;
   }

@@ -65,7 +65,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int kMaxTable = 256;      // block-table entries one partition may span
+constexpr int kMaxTable = kDecodeMaxTable;  // block-table entries one partition may span
 constexpr int kMaxScanSeqs = 512;  // sequences whose offsets a workgroup keeps in LDS
 constexpr int kNW = 4;              // waves per workgroup
 constexpr int kNT = 2;              // 16-token tiles per pipeline step

@@ -9,6 +9,10 @@
 
 namespace pkv {
 
+// Block-table entries one work item of the decode kernel may span (so a
+// partition holds at most this many blocks).
+constexpr int kDecodeMaxTable = 256;
+
 struct WriteArgs {
   const void* key;
   const void* value;
