@@ -34,8 +34,8 @@ WORKLOADS = {"tiny-fp32": 1, "7b-decode-bf16": 2, "32k-gqa-bf16": 3,
              "shared-prefix-bf16": 4, "fp8-kv": 5}
 DEFAULT_WORKLOAD = "7b-decode-bf16"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
-KERNEL_SOURCES = ("decode_valu.hip", "decode_mfma.hip", "pkv_device.h")
-PREFILL_SOURCES = ("prefill_mfma.hip", "pkv_device.h")
+KERNEL_SOURCES = ("decode_valu.hip", "decode_mfma.hip", "pkv_device.h", "pkv_internal.h")
+PREFILL_SOURCES = ("prefill_mfma.hip", "pkv_device.h", "pkv_internal.h")
 
 
 def parse():
