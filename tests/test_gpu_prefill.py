@@ -142,6 +142,26 @@ def test_beam_fork_multi_query():
     assert np.array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_many_short_chunks_whole_contexts(cache):
+    """64 sequences x 8 KV heads of 4-token chunks (512 items): the library
+    attends each whole context in one item, without partials."""
+    rng = np.random.default_rng(91)
+    lens = rng.integers(4, 900, size=64)
+    w = workloads.build_workload(f"short-chunks-{cache}", 64, 32, 8, 128, 16, "bf16", cache, lens,
+                                 91, fill="write" if cache == "fp8" else "random", query_tokens=4)
+    _say(f"case many short chunks {cache}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle.paged_attention_prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                         w.block_size, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    for ps in (0, 256):
+        err = max_err(out_f64(_prefill(dw, ps)), ref)
+        _say(f"  ps={ps} max_err={err:.3e}")
+        assert err <= TOL[cache], (ps, err)
+
+
 def test_one_query_token_is_decode():
     w = workloads.make_config(2, reduced=True)
     _say(f"case prefill M=1 vs decode {w.name}")
