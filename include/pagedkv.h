@@ -223,7 +223,12 @@ pkv_status_t paged_attention_decode_reduce(
  *   ceil(max_context_len / P) must stay below 2^30 and S * M * H * D below
  *   2^31 (PKV_ERR_SHAPE otherwise).  Other arguments, partitions and the
  *   workspace (paged_attention_prefill_workspace_size bytes, its first 4096
- *   zero) are as for paged_attention_decode.
+ *   zero) are as for paged_attention_decode, except the library's choice
+ *   (partition_size 0): long chunks (M * G >= 64 over a bf16 cache) split a
+ *   context only when the grid would leave CUs idle; other calls keep
+ *   whole contexts (up to 256 blocks) when there are at least 512
+ *   (sequence, KV head, 16-row) items, and otherwise split them as decode
+ *   does.
  */
 pkv_status_t paged_attention_prefill(
     void* out, const void* query,
