@@ -588,7 +588,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   __shared__ float s_m[kNW][16];
   __shared__ float s_l[kNW][16];
   __shared__ int s_red[kNW];
-  __shared__ int s_next[2];
+  __shared__ int s_next[3];  // next claimed item, second static item, queue flag
   __shared__ int s_zero[4];  // block id 0 for the dummy row
   __shared__ int s_full[SCAN ? kMaxScanSeqs + 1 : 1];
   __shared__ uint16_t s_rag[SCAN ? kMaxScanSeqs + 1 : 1];
@@ -632,7 +632,10 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   // About one shared item per workgroup, and never so many that a static
   // item would fall in the shared range.
   const int n_local = total - max(0, min((int)gridDim.x, total - 2 * (int)gridDim.x - 16));
-  bool use_shared = false;  // thread 0 only: its own queue is empty
+  // Uniform (thread 0 decides, every thread reads it back after barrier
+  // Y): this workgroup's own queue is empty and it claims from the shared
+  // one.  Kept uniform so its selects stay scalar.
+  int use_shared = 0;
   int cur = s_next[0];
   int nxt = s_next[1];
   int buf = 0;
@@ -783,13 +786,14 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       if (!use_shared) {
         item = (2 * queue_wgs + claim) * nq + queue;
         if (item >= n_local) {
-          use_shared = true;
+          use_shared = 1;
           item = n_local + atomicAdd(shared_ctr, 1);
         }
       } else {
         item = n_local + claim;
       }
       s_next[0] = item;
+      s_next[2] = use_shared;
     }
 
     // Merge the wave-level softmax states of this partition.
@@ -807,6 +811,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     // The item after the next one is known now: fetch its block ids, which
     // are stored during the next item's last chunk.
     const int nn = __builtin_amdgcn_readfirstlane(s_next[0]);
+    use_shared = __builtin_amdgcn_readfirstlane(s_next[2]);
     tab_next = fetch_tab<CT, D, BS>(
         p, decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, s_full, s_rag, s_len).w, wave,
         lane);
