@@ -580,7 +580,10 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   static_assert(kMaxTable == kNW * 64, "one table entry per thread");
   static_assert(Gm::NKC <= kNW, "one Q fragment row per wave");
   constexpr int VTILE = Gm::CHUNK * Gm::VS;  // bf16 elements per wave
-  constexpr int MERGE = kNW * 16 * D;   // fp32 partial outputs
+  // fp32 partial outputs, rows padded by 4 floats: the 16-byte writes of
+  // 8 lanes (8 rows, same columns) then fall on distinct banks.
+  constexpr int MS = D + 4;
+  constexpr int MERGE = kNW * 16 * MS;
   constexpr int UNION_BYTES = (VTILE * kNW * 2 > MERGE * 4) ? VTILE * kNW * 2 : MERGE * 4;
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[UNION_BYTES];
   __shared__ int s_wtab[2][kNW][kMaxTable / kNW];
@@ -804,8 +807,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     }
 #pragma unroll
     for (int md = 0; md < Gm::NMD; ++md)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + r) * D + 16 * md + 4 * q + i] = acc[md][i];
+      *reinterpret_cast<f32x4_t*>(&s_acc[(wave * 16 + r) * MS + 16 * md + 4 * q]) = acc[md];
     __syncthreads();  // Y
 
     // The item after the next one is known now: fetch its block ids, which
@@ -835,7 +837,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
         for (int k = 0; k < kNW; ++k) {
           const float wt = __builtin_amdgcn_exp2f(s_m[k][g] - M);
           L = fmaf(s_l[k][g], wt, L);
-          const float4 a = *reinterpret_cast<const float4*>(&s_acc[(k * 16 + g) * D + d]);
+          const float4 a = *reinterpret_cast<const float4*>(&s_acc[(k * 16 + g) * MS + d]);
           O.x = fmaf(a.x, wt, O.x);
           O.y = fmaf(a.y, wt, O.y);
           O.z = fmaf(a.z, wt, O.z);
