@@ -287,9 +287,16 @@ __device__ __forceinline__ void store_v(const VStage<CT, D>& st, int c0, int end
       } else {
         const uint2 a = fp8x4_to_bf16x4(v.x), b = fp8x4_to_bf16x4(v.y);
         const uint2 c = fp8x4_to_bf16x4(v.z), d = fp8x4_to_bf16x4(v.w);
-        uint4* dst = reinterpret_cast<uint4*>(s_v + row * Gm::VS + piece * 16);
-        dst[0] = make_uint4(a.x, a.y, b.x, b.y);
-        dst[1] = make_uint4(c.x, c.y, d.x, d.y);
+        // A lane's 32 bytes are two 16-byte halves; pieces 4..7 of a row
+        // store their upper half first, so the 8 lanes of one store phase
+        // cover 8 different 16-byte bank groups (32-byte steps alone repeat
+        // after 4 lanes).
+        const bool sw = (piece & 4) != 0;
+        const uint4 h0 = make_uint4(sw ? c.x : a.x, sw ? c.y : a.y, sw ? d.x : b.x, sw ? d.y : b.y);
+        const uint4 h1 = make_uint4(sw ? a.x : c.x, sw ? a.y : c.y, sw ? b.x : d.x, sw ? b.y : d.y);
+        uint16_t* base = s_v + row * Gm::VS + piece * 16;
+        *reinterpret_cast<uint4*>(base + (sw ? 8 : 0)) = h0;
+        *reinterpret_cast<uint4*>(base + (sw ? 0 : 8)) = h1;
       }
     }
   }
