@@ -8,6 +8,7 @@ built, every call raises.
 """
 
 from ._lib import (
+    ContractError,
     PKV_BF16,
     PKV_F32,
     PKV_FP8_E4M3,
@@ -31,7 +32,7 @@ from ._lib import (
 from .block_manager import BlockManager, OutOfBlocks
 
 __all__ = [
-    "PKV_BF16", "PKV_F32", "PKV_FP8_E4M3", "PagedKVError", "BlockManager", "OutOfBlocks",
+    "ContractError", "PKV_BF16", "PKV_F32", "PKV_FP8_E4M3", "PagedKVError", "BlockManager", "OutOfBlocks",
     "decode_partition_size", "decode_workspace_size", "dtype_code", "load",
     "paged_attention_decode", "paged_attention_decode_partitions",
     "paged_attention_decode_reduce", "paged_attention_decode_shared_prefix",

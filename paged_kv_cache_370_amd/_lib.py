@@ -12,6 +12,9 @@ import os
 
 import torch
 
+from . import _validate as _v
+from ._validate import ContractError  # noqa: F401  (raised in PAGEDKV_DEBUG mode)
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
@@ -141,6 +144,8 @@ def paged_kv_cache_write(key, value, key_cache, value_cache, slot_mapping, key_s
     _contig(key, value, key_cache, value_cache, slot_mapping, key_scale, value_scale)
     T, H_kv, D = key.shape
     num_blocks, _, bs, _ = key_cache.shape
+    if _v.enabled():
+        _v.check_slots("paged_kv_cache_write", slot_mapping, num_blocks, bs)
     cdt = dtype_code(key_cache)
     if workspace is None:
         need = write_workspace_size(T, H_kv, num_blocks, cdt)
@@ -175,7 +180,11 @@ def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
     _contig(out, query, key_cache, value_cache, block_tables, context_lens, key_scale,
             value_scale)
     S, H, D = query.shape
-    _, H_kv, bs, _ = key_cache.shape
+    num_blocks, H_kv, bs, _ = key_cache.shape
+    if _v.enabled():
+        _v.check_decode("paged_attention_decode", context_lens, block_tables, num_blocks, bs,
+                        max_context_len)
+        _v.check_workspace_header("paged_attention_decode", workspace)
     qc, cc = dtype_code(query), dtype_code(key_cache)
     if workspace is None:
         # zero-filled: the first 4 KiB are the library's work-queue counters
@@ -212,6 +221,11 @@ def paged_attention_decode_reduce(out, context_lens, num_kv_heads, block_size, m
                                   cache_dtype_code, partition_size=0, workspace=None,
                                   stream=None):
     S, H, D = out.shape
+    if _v.enabled():
+        lens = _v._host(context_lens)
+        if lens.size and (lens.min() < 0 or lens.max() > max_context_len):
+            raise _v.ContractError("paged_attention_decode_reduce: context_lens outside "
+                                   f"[0, {max_context_len}]")
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load().paged_attention_decode_reduce(_ptr(out), _ptr(context_lens), S, H, num_kv_heads,
                                               D, block_size, int(max_context_len),
@@ -240,6 +254,10 @@ def paged_kv_block_copy(src_key_cache, src_value_cache, dst_key_cache, dst_value
         raise ValueError("source and destination pools differ in dtype or block shape")
     if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
         raise ValueError("block_pairs must be int32 [n][2]")
+    if _v.enabled():
+        _v.check_block_pairs("paged_kv_block_copy", block_pairs, src_key_cache.shape[0],
+                             dst_key_cache.shape[0],
+                             src_key_cache.data_ptr() == dst_key_cache.data_ptr())
     _, H_kv, bs, D = src_key_cache.shape
     st = load().paged_kv_block_copy(
         _ptr(src_key_cache), _ptr(src_value_cache), _ptr(src_key_scale), _ptr(src_value_scale),
@@ -268,7 +286,12 @@ def paged_attention_decode_shared_prefix(out, query, key_cache, value_cache, blo
     _contig(out, query, key_cache, value_cache, block_tables, context_lens, key_scale,
             value_scale)
     S, H, D = query.shape
-    _, H_kv, bs, _ = key_cache.shape
+    num_blocks, H_kv, bs, _ = key_cache.shape
+    if _v.enabled():
+        where = "paged_attention_decode_shared_prefix"
+        _v.check_decode(where, context_lens, block_tables, num_blocks, bs, max_context_len)
+        _v.check_shared_prefix(where, block_tables, prefix_tokens, bs)
+        _v.check_workspace_header(where, workspace)
     qc, cc = dtype_code(query), dtype_code(key_cache)
     if workspace is None:
         need = shared_prefix_workspace_size(S, H, H_kv, D, bs, max_context_len, prefix_tokens,
@@ -301,7 +324,11 @@ def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, co
     if query.dim() != 4 or out.shape != query.shape or out.dtype != query.dtype:
         raise ValueError("query and out must both be [S][M][H][D] of one dtype")
     S, M, H, D = query.shape
-    _, H_kv, bs, _ = key_cache.shape
+    num_blocks, H_kv, bs, _ = key_cache.shape
+    if _v.enabled():
+        _v.check_decode("paged_attention_prefill", context_lens, block_tables, num_blocks, bs,
+                        max_context_len, query_tokens=M)
+        _v.check_workspace_header("paged_attention_prefill", workspace)
     qc, cc = dtype_code(query), dtype_code(key_cache)
     if workspace is None:
         # zero-filled: the first 4 KiB are the library's work-queue counters
@@ -315,3 +342,4 @@ def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, co
         block_tables.shape[1], int(max_context_len), float(scale), qc, cc, int(partition_size),
         _ptr(workspace), wbytes, _stream(stream))
     _check(st, "paged_attention_prefill")
+

@@ -78,9 +78,16 @@ class BlockManager:
     def length(self, seq: int) -> int:
         return self._lens[seq]
 
+    def _resident(self, seq: int) -> None:
+        """A swapped-out sequence's table holds host block ids: nothing but
+        swap_in and finish(seq, host) may touch it."""
+        if seq in self._swapped:
+            raise ValueError(f"sequence {seq} is swapped out; swap it in first")
+
     def append_slot(self, seq: int) -> int:
         """Reserve the slot of the sequence's next token; returns the flat slot
         id (physical block * block_size + offset)."""
+        self._resident(seq)
         n = self._lens[seq]
         table = self._tables[seq]
         if n % self.block_size == 0:
@@ -100,6 +107,7 @@ class BlockManager:
     def fork(self, src: int, dst: int) -> None:
         """dst becomes a copy of src sharing every block, the partial last one
         included; the first write into a shared block copies it."""
+        self._resident(src)
         if dst in self._tables:
             raise ValueError(f"sequence {dst} exists")
         self._tables[dst] = []
@@ -119,6 +127,7 @@ class BlockManager:
         """Move seq's blocks to host blocks of the host pool's manager; returns
         the (device block, host block) pairs to copy before the device blocks
         are reused.  Only sequences with no shared block can be swapped."""
+        self._resident(seq)
         table = self._tables[seq]
         if any(self.ref_count[b] > 1 for b in table):
             raise ValueError("a sequence with shared blocks cannot be swapped out")
@@ -152,6 +161,8 @@ class BlockManager:
 
     def share_prefix(self, src: int, dst: int, num_blocks: int) -> None:
         """Give dst the first num_blocks blocks of src (whole, full blocks)."""
+        self._resident(src)
+        self._resident(dst)
         if self._tables[dst]:
             raise ValueError("destination must be empty")
         if num_blocks * self.block_size > self._lens[src]:
@@ -161,15 +172,25 @@ class BlockManager:
             self._tables[dst].append(b)
         self._lens[dst] = num_blocks * self.block_size
 
-    def finish(self, seq: int) -> None:
-        for b in self._tables.pop(seq):
-            self.free(b)
+    def finish(self, seq: int, host: "BlockManager" = None) -> None:
+        """Release the sequence's blocks.  A swapped-out sequence holds host
+        blocks: they go back to the host pool's manager, which must be given."""
+        if seq in self._swapped:
+            if host is None:
+                raise ValueError(f"sequence {seq} is swapped out: finish it with its host manager")
+            for hb in self._tables.pop(seq):
+                host.free(hb)
+            self._swapped.discard(seq)
+        else:
+            for b in self._tables.pop(seq):
+                self.free(b)
         del self._lens[seq]
 
     # ---------------------------------------------------------------- views
     def block_tables(self, seqs, max_blocks: int, fill: int = 0) -> np.ndarray:
         out = np.full((len(seqs), max_blocks), fill, dtype=np.int32)
         for i, s in enumerate(seqs):
+            self._resident(s)
             t = self._tables[s]
             out[i, :len(t)] = t
         return out

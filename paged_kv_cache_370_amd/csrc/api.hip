@@ -477,8 +477,7 @@ pkv_status_t paged_attention_decode_shared_prefix(
   if (st != PKV_OK) return st;
   // 2. Each sequence's positions after the prefix, as a decode of its own.
   DecodeArgs suf = base;
-  suf.len_off = prefix_tokens;
-  suf.tables = block_tables + prefix_tokens / block_size;
+  suf.len_off = prefix_tokens;  // the kernel skips the prefix's table entries
   suf.max_ctx = max_context_len - prefix_tokens;
   suf.NP = sp.suf_slots;
   suf.slot_off = sp.pre_slots;

@@ -100,6 +100,8 @@ struct MfmaParams {
                // [9 * kCounterStride]
   int S, H, H_kv, G, chunks, max_blocks, P, NP;
   int M;  // query tokens per sequence (1 for decode)
+  int max_ctx;    // longest context the launch covers; longer lengths are cut to it
+  int tab_off;    // table entry of the launch's position 0 (len_off / bs)
   // Split attention over a shared prefix (zero / plain values otherwise):
   int len_off;        // positions below it are not this launch's: n = lens - len_off
   int prefix;         // prefix-rows launch: the prefix length (the one "sequence")
@@ -120,11 +122,14 @@ template <int MODE>
 constexpr bool kSplit = MODE == kModePrefixRows || MODE == kModeSuffix;
 
 // Context length the launch sees for sequence i.
+// A length above the launch's bound (a broken caller contract) is cut to
+// it, so no item, partial slot or table entry lies past what the grid and
+// workspace were sized for.
 template <int MODE>
 __device__ __forceinline__ int seq_len(const MfmaParams& p, int i) {
   if constexpr (MODE == kModePrefixRows) return p.prefix;
-  if constexpr (MODE == kModeSuffix) return max(0, p.lens[i] - p.len_off);
-  return p.lens[i];
+  if constexpr (MODE == kModeSuffix) return min(max(0, p.lens[i] - p.len_off), p.max_ctx);
+  return min(p.lens[i], p.max_ctx);
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -543,14 +548,15 @@ __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y
 // block l % EPC of its chunk number l / EPC (EPC = CHUNK / BS blocks per
 // chunk; 64 entries cover the kMaxTable blocks an item may span).  Each wave
 // writes and reads only its own slice in LDS, so no workgroup barrier guards
-// it.  Entries past the item's blocks repeat the table's last entry and are
-// never read.  Plain loads: the compiler tracks them exactly, so they never
+// it.  Entries past the item's blocks repeat the row's last entry and are
+// never used; a suffix launch's positions start tab_off entries into the
+// row, and the clamp keeps every read inside the row.  Plain loads: the compiler tracks them exactly, so they never
 // force a wait on the chunk pipeline.
 template <typename CT, int D, int BS>
 __device__ __forceinline__ int fetch_tab(const MfmaParams& p, const Part& w, int wave, int lane) {
   constexpr int EPC = Geometry<CT, D>::CHUNK / BS;
   const int blk = w.first_blk + (wave + kNW * (lane / EPC)) * EPC + lane % EPC;
-  return p.tables[(size_t)w.seq * p.max_blocks + min(blk, p.max_blocks - 1)];
+  return p.tables[(size_t)w.seq * p.max_blocks + min(p.tab_off + blk, p.max_blocks - 1)];
 }
 
 __device__ __forceinline__ void store_tab(int tab, int* wtab, int lane) {
@@ -937,6 +943,8 @@ hipError_t launch_bs(const DecodeArgs& a) {
   p.S = a.S; p.H = a.H; p.H_kv = a.H_kv; p.G = a.H / a.H_kv; p.M = a.M;
   p.chunks = (a.M * p.G + 15) / 16;
   p.max_blocks = a.max_blocks; p.P = a.P; p.NP = a.NP;
+  p.max_ctx = a.max_ctx;
+  p.tab_off = a.len_off / a.bs;
   p.len_off = a.len_off; p.prefix = a.prefix_rows; p.slot_off = a.slot_off;
   p.np_stride = a.np_stride > 0 ? a.np_stride : a.NP;
   p.force_partial = a.force_partial ? 1 : 0;

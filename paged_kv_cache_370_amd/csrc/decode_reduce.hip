@@ -115,7 +115,8 @@ __global__ __launch_bounds__((OUT_BF16 ? D / 2 : D) * kRowWaves) void decode_red
   // prefix split off, the prefix's pre_slots partials come first and the
   // partitions cover the positions from len_off on.
   const int end = n - M + t + 1;
-  const int np = pre_slots + (max(end - len_off, 0) + P - 1) / P;
+  // (never more than the NP slots a row holds, whatever the length says)
+  const int np = min(NP, pre_slots + (max(end - len_off, 0) + P - 1) / P);
   const int hi = min(np, lo + cw);
   float Mx = kNegInf, L = 0.f, O[E];
 #pragma unroll

@@ -34,7 +34,7 @@ struct ValuParams {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
-  int H, H_kv, G, chunks, max_blocks, P, NP;
+  int H, H_kv, G, chunks, max_blocks, P, NP, max_ctx;
   float scale_log2;
 };
 
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(ValuParams p) {
   const int chunk = blockIdx.y % p.chunks;
   const int kvh = blockIdx.y / p.chunks;
   const int seq = blockIdx.z;
-  const int n = p.lens[seq];
+  const int n = min(p.lens[seq], p.max_ctx);  // the grid covers max_ctx tokens
   const int start = part * p.P;
   if (part > 0 && start >= n) return;
   const int end = min(n, start + p.P);
@@ -225,7 +225,7 @@ hipError_t launch_g(const DecodeArgs& a, int chunks) {
   p.tables = a.tables; p.lens = a.lens; p.out = a.out;
   p.ws_m = a.ws_m; p.ws_l = a.ws_l; p.ws_acc = a.ws_acc;
   p.H = a.H; p.H_kv = a.H_kv; p.G = a.H / a.H_kv; p.chunks = chunks;
-  p.max_blocks = a.max_blocks; p.P = a.P; p.NP = a.NP;
+  p.max_blocks = a.max_blocks; p.P = a.P; p.NP = a.NP; p.max_ctx = a.max_ctx;
   p.scale_log2 = a.scale * kLog2e;
   dim3 grid(a.NP, a.H_kv * chunks, a.S);
   hipLaunchKernelGGL((decode_valu_kernel<QT, CT, D, BS, GMAX, NW>), grid, dim3(NW * 64), 0,

@@ -20,13 +20,14 @@ namespace {
 __global__ __launch_bounds__(256) void kv_write_copy_kernel(
     const uint4* __restrict__ key, const uint4* __restrict__ value,
     uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
-    const int32_t* __restrict__ slots, int H_kv, int row_vec, int bs, int wpt, long long pieces) {
+    const int32_t* __restrict__ slots, int H_kv, int row_vec, int bs, int wpt, long long pieces,
+    int num_slots) {
   const int per_token = H_kv * row_vec;  // 16-byte vectors per token per K or V
   for (long long g = blockIdx.x; g < pieces; g += gridDim.x) {
     const long long t = g / wpt;
     const int i = (int)(g - t * wpt) * 256 + (int)threadIdx.x;
     const int s = slots[t];
-    if (s < 0 || i >= 2 * per_token) continue;
+    if (s < 0 || s >= num_slots || i >= 2 * per_token) continue;
     const bool is_v = i >= per_token;
     const int j = is_v ? i - per_token : i;
     const int h = j / row_vec;
@@ -40,6 +41,13 @@ __global__ __launch_bounds__(256) void kv_write_copy_kernel(
   }
 }
 
+// Slots the pool holds (slot values are int32, so at most INT32_MAX + 1);
+// a slot at or past it is skipped like a negative one.
+int pool_slots(const WriteArgs& a) {
+  const long long n = (long long)a.num_blocks * a.bs;
+  return n > 0x7fffffffLL ? 0x7fffffff : (int)n;
+}
+
 // ---------------------------------------------------------------- FP8 path
 // Workspace: fresh[num_blocks] (int32) then amax[num_blocks][H_kv][2]
 // (float bits; index 0 = K, 1 = V).  Three launches:
@@ -51,12 +59,12 @@ __global__ __launch_bounds__(256) void kv_write_copy_kernel(
 
 // One thread per token (tokens of one block write the same zeros).
 __global__ __launch_bounds__(256) void fp8_clear_kernel(
-    const int32_t* __restrict__ slots, int T, int bs, int H_kv,
+    const int32_t* __restrict__ slots, int T, int bs, int H_kv, int num_slots,
     int32_t* __restrict__ fresh, uint32_t* __restrict__ amax) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const int s = slots[t];
-  if (s < 0) return;
+  if (s < 0 || s >= num_slots) return;
   const int b = s / bs;
   uint32_t* a = amax + (size_t)b * 2 * H_kv;
   for (int i = 0; i < 2 * H_kv; ++i) a[i] = 0u;
@@ -104,7 +112,7 @@ __device__ __forceinline__ float row_group_max(float x) {
 template <typename ST, int D>
 __global__ __launch_bounds__(256) void fp8_amax_kernel(
     const ST* __restrict__ key, const ST* __restrict__ value,
-    const int32_t* __restrict__ slots, int T, int bs, int H_kv,
+    const int32_t* __restrict__ slots, int T, int bs, int H_kv, int num_slots,
     int32_t* __restrict__ fresh, uint32_t* __restrict__ amax) {
   using R = Fp8Rows<ST, D>;
   const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(
   nk = row_group_max<R::LPR>(nk);
   nv = row_group_max<R::LPR>(nv);
   const int s = ok ? slots[t] : -1;
-  if (part == 0 && s >= 0) {
+  if (part == 0 && s >= 0 && s < num_slots) {
     const int b = s / bs;
     const int o = s - b * bs;
     const uint32_t bk = nk > 0.f ? 0x7fc00000u : __float_as_uint(mk);
@@ -156,7 +164,7 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(
     const ST* __restrict__ key, const ST* __restrict__ value,
     uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
     float* __restrict__ key_scale, float* __restrict__ value_scale,
-    const int32_t* __restrict__ slots, int T, int bs, int H_kv,
+    const int32_t* __restrict__ slots, int T, int bs, int H_kv, int num_slots,
     const int32_t* __restrict__ fresh, const uint32_t* __restrict__ amax) {
   using R = Fp8Rows<ST, D>;
   const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -167,7 +175,7 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(
   const int t = row / H_kv;
   const int h = row - t * H_kv;
   const int s = slots[t];
-  if (s < 0) return;
+  if (s < 0 || s >= num_slots) return;
   const int b = s / bs;
   const int o = s - b * bs;
   const size_t sidx = (size_t)b * H_kv + h;
@@ -216,17 +224,18 @@ hipError_t fp8_launch(const WriteArgs& a) {
   uint32_t* amax = reinterpret_cast<uint32_t*>(fresh + ((a.num_blocks + 63) / 64) * 64);
   const ST* key = reinterpret_cast<const ST*>(a.key);
   const ST* value = reinterpret_cast<const ST*>(a.value);
+  const int num_slots = pool_slots(a);  // slots past the pool are skipped
   hipLaunchKernelGGL(fp8_clear_kernel, dim3((a.T + 255) / 256), dim3(256), 0, a.stream, a.slots,
-                     a.T, a.bs, a.H_kv, fresh, amax);
+                     a.T, a.bs, a.H_kv, num_slots, fresh, amax);
   const int rows = a.T * a.H_kv;
   const int waves = (rows + Fp8Rows<ST, D>::RPW - 1) / Fp8Rows<ST, D>::RPW;
   const int blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((fp8_amax_kernel<ST, D>), dim3(blocks), dim3(256), 0, a.stream, key, value,
-                     a.slots, a.T, a.bs, a.H_kv, fresh, amax);
+                     a.slots, a.T, a.bs, a.H_kv, num_slots, fresh, amax);
   hipLaunchKernelGGL((fp8_quant_kernel<ST, D>), dim3(blocks), dim3(256), 0, a.stream, key, value,
                      reinterpret_cast<uint8_t*>(a.key_cache),
                      reinterpret_cast<uint8_t*>(a.value_cache), a.key_scale, a.value_scale,
-                     a.slots, a.T, a.bs, a.H_kv, fresh, amax);
+                     a.slots, a.T, a.bs, a.H_kv, num_slots, fresh, amax);
   return hipGetLastError();
 }
 
@@ -246,7 +255,7 @@ hipError_t launch_kv_write_copy(const WriteArgs& a) {
   hipLaunchKernelGGL(kv_write_copy_kernel, dim3(grid), dim3(256), 0, a.stream,
                      reinterpret_cast<const uint4*>(a.key), reinterpret_cast<const uint4*>(a.value),
                      reinterpret_cast<uint4*>(a.key_cache), reinterpret_cast<uint4*>(a.value_cache),
-                     a.slots, a.H_kv, row_vec, a.bs, wpt, pieces);
+                     a.slots, a.H_kv, row_vec, a.bs, wpt, pieces, pool_slots(a));
   return hipGetLastError();
 }
 

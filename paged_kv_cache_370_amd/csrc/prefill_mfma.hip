@@ -60,6 +60,7 @@ struct PrefillParams {
   float* ws_l;
   float* ws_acc;  // [S][M][H][NP][D]
   int M, H, H_kv, G, max_blocks, P, NP;
+  int max_ctx;  // longest context the grid covers; longer lengths are cut to it
   int RT;       // row tiles per KV head: ceil(M * G / kBM)
   int total;    // workgroups with work: S * H_kv * NP * RT
   int per_xcd;  // ceil(total / 8)
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, r = lane & 15;
-  const int n = p.lens[seq];
+  const int n = min(p.lens[seq], p.max_ctx);
   const int MG = p.M * p.G;
   const int r0 = rt * kBM;
   const int rlast = min(r0 + kBM, MG) - 1;
@@ -557,7 +558,7 @@ hipError_t launch_db(const DecodeArgs& a) {
   p.lens = a.lens;
   p.ws_m = a.ws_m; p.ws_l = a.ws_l; p.ws_acc = a.ws_acc;
   p.M = a.M; p.H = a.H; p.H_kv = a.H_kv; p.G = a.H / a.H_kv;
-  p.max_blocks = a.max_blocks; p.P = a.P; p.NP = a.NP;
+  p.max_blocks = a.max_blocks; p.P = a.P; p.NP = a.NP; p.max_ctx = a.max_ctx;
   p.RT = (a.M * p.G + kBM - 1) / kBM;
   const long long total = (long long)a.S * a.H_kv * a.NP * p.RT;
   p.total = (int)total;

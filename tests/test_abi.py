@@ -3,6 +3,7 @@ declares is exported, status codes, workspace and partition queries, and the
 argument checks that return before anything is enqueued."""
 
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -13,11 +14,11 @@ import paged_kv_cache_370_amd as pkv
 from paged_kv_cache_370_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
     keywords = {"if", "sizeof", "defined"}
@@ -221,3 +222,4 @@ def test_shared_prefix_argument_checks():
     # no prefix: plain decode and its workspace
     assert pkv.shared_prefix_workspace_size(2, 8, 2, 128, 16, 1000, 0, 1, 1, 0) == \
         pkv.decode_workspace_size(2, 8, 2, 128, 16, 1000, 1, 1, 0)
+

@@ -111,3 +111,30 @@ def test_pool_exhaustion_raises():
         bm.append_slot(0)
     with pytest.raises(OutOfBlocks):
         bm.append_slot(0)
+
+
+def test_finish_after_swap_out_frees_host_blocks_only():
+    """A swapped-out sequence's table holds host block ids: finishing it gives
+    them back to the host pool and leaves every device block alone."""
+    dev, host = BlockManager(8, 4), BlockManager(8, 4)
+    for s in (0, 1):
+        dev.add_sequence(s)
+        for _ in range(6):
+            dev.append_slot(s)
+    owned_by_1 = dev.table(1)
+    dev.swap_out(0, host)
+    assert host.num_free == 6
+    with pytest.raises(ValueError):
+        dev.finish(0)                              # needs the host manager
+    with pytest.raises(ValueError):
+        dev.append_slot(0)                         # host ids are not device slots
+    with pytest.raises(ValueError):
+        dev.fork(0, 5)
+    with pytest.raises(ValueError):
+        dev.block_tables([0], 4)
+    dev.finish(0, host)
+    assert host.num_free == 8 and np.all(host.ref_count == 0)
+    assert all(dev.ref_count[b] == 1 for b in owned_by_1)   # sequence 1 keeps its blocks
+    assert dev.num_free == 6
+    dev.finish(1)
+    assert dev.num_free == 8 and np.all(dev.ref_count == 0)

@@ -202,3 +202,67 @@ def test_workspace_reused_across_calls():
             torch.cuda.synchronize()
             assert max_err(out_f64(dw.out), ref) <= TOL[w.cache_dtype], (k, ps)
             assert int(ws[:4096].count_nonzero()) == 0, (k, ps)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_write_from_fp32_source(D):
+    """FP8 cache written from float32 K/V (4-element lanes, 4-byte code
+    stores): codes and scales bit-exact against the oracle over the whole
+    pool, for fresh blocks (the bulk write) and appends (the step write lands
+    in a fresh block for n = 1 and 129, in a started one for 16, 37 and 300),
+    then decode within the FP8 bar."""
+    lens = [37, 16, 1, 300, 129, 0]
+    w = workloads.build_workload(f"fp8-from-f32-{D}", len(lens), 8, 2, D, 16, "bf16", "fp8",
+                                 lens, 70 + D, fill="write", src_dtype="f32")
+    assert w.writes[0][0].dtype == np.float32
+    _say(f"case fp8 write from f32 D={D} lens={lens}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle_decode(w, kc, vc, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write(0)
+    okc, ovc, oks, ovs = oracle_caches(workloads_first_write(w))
+    _check_caches(dw, okc, ovc, oks, ovs)           # after the bulk write alone
+    dw.write(1)
+    _check_caches(dw, kc, vc, ks, vs)               # after the appends
+    for ps in (0, 64):
+        err = max_err(out_f64(dw.decode(partition_size=ps)), ref)
+        _say(f"  ps={ps} max_err={err:.3e}")
+        assert err <= TOL["fp8"], (ps, err)
+
+
+def workloads_first_write(w):
+    import copy
+    w1 = copy.copy(w)
+    w1.writes = w.writes[:1]
+    return w1
+
+
+@pytest.mark.parametrize("cache,bs,D", [("bf16", 8, 128), ("fp8", 16, 64), ("bf16", 32, 64)])
+def test_partitions_longer_than_256_blocks(cache, bs, D):
+    """An explicit partition spanning more than 256 blocks is beyond the
+    matrix-core kernel's per-item table, so bf16 queries run on the vector-ALU
+    kernel (bf16 and FP8 caches), with bf16 partials merged by the reduce
+    kernel: several partitions, a ragged last one, a context of exactly one
+    partition, one of one token and an empty one."""
+    import paged_kv_cache_370_amd as pkv
+    P = 512 * bs if bs == 8 else 257 * bs            # 512 or 257 blocks per partition
+    lens = [2 * P + 37, P, 1, 0, P + 1]
+    G, H_kv = 4, 2
+    w = workloads.build_workload(f"valu-{cache}-bs{bs}", len(lens), G * H_kv, H_kv, D, bs,
+                                 "bf16", cache, lens, 80 + bs,
+                                 fill="write" if cache == "fp8" else "random")
+    qc, cc = pkv.dtype_code(torch.zeros(1, dtype=torch.bfloat16)), {"bf16": 1, "fp8": 2}[cache]
+    assert pkv.decode_partition_size(w.S, w.H, w.H_kv, D, bs, w.max_context_len, qc, cc, P) == P
+    assert (P + bs - 1) // bs > 256
+    _say(f"case vector-ALU decode cache={cache} bs={bs} D={D} P={P} lens={lens}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle_decode(w, kc, vc, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    _check_caches(dw, kc, vc, ks, vs)
+    out = dw.decode(partition_size=P)
+    torch.cuda.synchronize()
+    err = max_err(out_f64(out), ref)
+    _say(f"  max_err={err:.3e}")
+    assert err <= TOL[cache], err
+    assert np.all(out_f64(out)[3] == 0)
