@@ -328,6 +328,39 @@ pkv_status_t paged_kv_block_copy(
     int32_t cache_dtype,
     void* stream);
 
+/*
+ * paged_attention_decode_noalloc -- paged_attention_decode without a caller
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, partition choice and result as paged_attention_decode; the
+ * workspace is instead a device array inside the library, one per device,
+ * of PKV_DECODE_NOALLOC_MAX_WORKSPACE bytes, held until the process ends.
+ * The call allocates nothing: it zeroes the array's 4 KiB counter header with
+ * a small kernel on `stream`, then runs the decode in it.
+ *   A call whose paged_attention_decode_workspace_size(...) exceeds
+ *   PKV_DECODE_NOALLOC_MAX_WORKSPACE returns PKV_ERR_WORKSPACE and enqueues
+ *   nothing.  Other checks and errors are paged_attention_decode's.
+ *   Every call on one device uses the same array and leaves its contents
+ *   behind: calls that may run at the same time on one device race (order
+ *   them on one stream, or with events).
+ */
+#define PKV_DECODE_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+
+pkv_status_t paged_attention_decode_noalloc(
+    void* out, const void* query,
+    const void* key_cache, const void* value_cache,
+    const float* key_scale, const float* value_scale,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size,
+    int32_t max_blocks_per_seq, int32_t max_context_len,
+    float scale, int32_t q_dtype, int32_t cache_dtype,
+    int32_t partition_size,
+    void* stream);
+
+/* PKV_DECODE_NOALLOC_MAX_WORKSPACE, as the library was built. */
+size_t paged_attention_decode_noalloc_max_workspace(void);
+
 /* Static, NUL-terminated description of a status code. */
 const char* pkv_status_string(int32_t status);
 

@@ -17,7 +17,9 @@ from ._lib import (
     decode_workspace_size,
     dtype_code,
     load,
+    decode_noalloc_max_workspace,
     paged_attention_decode,
+    paged_attention_decode_noalloc,
     paged_attention_decode_partitions,
     paged_attention_decode_reduce,
     paged_attention_decode_shared_prefix,
@@ -34,7 +36,8 @@ from .block_manager import BlockManager, OutOfBlocks
 __all__ = [
     "ContractError", "PKV_BF16", "PKV_F32", "PKV_FP8_E4M3", "PagedKVError", "BlockManager", "OutOfBlocks",
     "decode_partition_size", "decode_workspace_size", "dtype_code", "load",
-    "paged_attention_decode", "paged_attention_decode_partitions",
+    "decode_noalloc_max_workspace", "paged_attention_decode",
+    "paged_attention_decode_noalloc", "paged_attention_decode_partitions",
     "paged_attention_decode_reduce", "paged_attention_decode_shared_prefix",
     "paged_attention_prefill", "paged_kv_block_copy", "paged_kv_cache_write",
     "prefill_workspace_size", "shared_prefix_workspace_size",

@@ -33,6 +33,8 @@ EXPORTS = (
     "paged_attention_prefill_workspace_size",
     "paged_attention_decode_shared_prefix",
     "paged_attention_decode_shared_prefix_workspace_size",
+    "paged_attention_decode_noalloc",
+    "paged_attention_decode_noalloc_max_workspace",
     "pkv_status_string",
     "pkv_version",
 )
@@ -68,6 +70,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("paged_attention_decode", "paged_attention_decode_partitions"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = decode_args
+    lib.paged_attention_decode_noalloc.restype = i32
+    lib.paged_attention_decode_noalloc.argtypes = decode_args[:-3] + [vp]
+    lib.paged_attention_decode_noalloc_max_workspace.restype = sz
+    lib.paged_attention_decode_noalloc_max_workspace.argtypes = []
     lib.paged_attention_decode_reduce.restype = i32
     lib.paged_attention_decode_reduce.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                                   i32, vp, sz, vp]
@@ -205,6 +211,31 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
                            max_context_len, scale, key_scale, value_scale, partition_size,
                            workspace, stream)
     _check(load().paged_attention_decode(*args), "paged_attention_decode")
+
+
+def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables,
+                                   context_lens, max_context_len, scale, key_scale=None,
+                                   value_scale=None, partition_size=0, stream=None):
+    """paged_attention_decode with the library's own per-device workspace:
+    nothing is allocated, here or in the library.  Calls that may overlap on
+    one device race on that workspace."""
+    _contig(out, query, key_cache, value_cache, block_tables, context_lens, key_scale,
+            value_scale)
+    S, H, D = query.shape
+    num_blocks, H_kv, bs, _ = key_cache.shape
+    if _v.enabled():
+        _v.check_decode("paged_attention_decode_noalloc", context_lens, block_tables, num_blocks,
+                        bs, max_context_len)
+    st = load().paged_attention_decode_noalloc(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
+        _ptr(value_scale), _ptr(block_tables), _ptr(context_lens), S, H, H_kv, D, bs,
+        block_tables.shape[1], int(max_context_len), float(scale), dtype_code(query),
+        dtype_code(key_cache), int(partition_size), _stream(stream))
+    _check(st, "paged_attention_decode_noalloc")
+
+
+def decode_noalloc_max_workspace() -> int:
+    return int(load().paged_attention_decode_noalloc_max_workspace())
 
 
 def paged_attention_decode_partitions(out, query, key_cache, value_cache, block_tables,

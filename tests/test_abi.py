@@ -223,3 +223,22 @@ def test_shared_prefix_argument_checks():
     assert pkv.shared_prefix_workspace_size(2, 8, 2, 128, 16, 1000, 0, 1, 1, 0) == \
         pkv.decode_workspace_size(2, 8, 2, 128, 16, 1000, 1, 1, 0)
 
+
+def test_noalloc_checks_return_before_any_launch():
+    """paged_attention_decode_noalloc: sizes beyond its fixed workspace, bad
+    shapes, NULL pointers and empty batches are answered on the host."""
+    lib = pkv.load()
+    assert lib.paged_attention_decode_noalloc_max_workspace() == 64 << 20
+
+    def call(S=2, H=8, H_kv=2, D=128, bs=16, max_blocks=8, max_ctx=100, ps=0, out=FAKE, cd=1):
+        return lib.paged_attention_decode_noalloc(out, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                                                  S, H, H_kv, D, bs, max_blocks, max_ctx, 0.1, 1,
+                                                  cd, ps, None)
+
+    # 256 sequences x 64 heads x 64 partitions of partials: far beyond 64 MiB
+    assert call(S=256, H=64, H_kv=8, bs=8, max_blocks=4096, max_ctx=32768, ps=512) == 4
+    assert call(D=96) == 2
+    assert call(cd=0) == 3
+    assert call(out=None) == 1
+    assert call(cd=2) == 1                       # FP8 cache without scales
+    assert call(S=0) == 0
