@@ -1,18 +1,28 @@
-"""Benchmark one decode step (paged KV write of the step's tokens + paged
-attention decode) on one MI355X and print ONE JSON line.
+"""Benchmark the paged-decode hot path on one MI355X and print ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7b-decode-bf16]
 
 A step is the whole hot path over one batch: paged_kv_cache_write of each
-sequence's newest token, the decode partition kernel and the split reduce.
-Inputs are seeded synthetic tensors already resident in HBM.  `value` is the
-algorithmic KV bytes the decode reads per step divided by the step time
-(GB/s); `roofline` is the partition kernel's algorithmic bytes over its own
-event-timed duration against the 8 TB/s HBM peak; `cpu_baseline` times the
-CPU oracle (float64 numpy, one BLAS thread) on a bounded sample of the same
-workload.  `block_copy` times whole-block copies on the same pool: a
-device-to-device copy (copy-on-write) and swapping blocks out to pinned host
-memory and back in.
+sequence's newest token, then paged_attention_decode (the partition kernel and
+the split reduce).  Inputs are seeded synthetic tensors already resident in
+HBM.  Every GPU figure is a per-iteration HIP-event time with the MALL (256 MB)
+and L2s flushed before the iteration by writing a 512 MiB buffer outside the
+events; the median (with p10/p90) over K iterations is reported, and
+back-to-back warm times beside it.
+
+  value        algorithmic KV bytes the decode reads per step / median step
+               time (GB/s) on the headline workload;
+  roofline     the partition kernel's algorithmic bytes over its mean flushed
+               launch time, against the 8 TB/s HBM peak;
+  workloads    the 32K-context, shared-prefix and FP8 workloads measured the
+               same way, each with its own roofline;
+  ceiling_gbs  a streaming read of 1 GiB (and a 4 KiB-tile gather) by the
+               library's probe kernels: what HBM delivers to a plain read;
+  cpu_baseline the CPU oracle (float64 NumPy, untuned) on a bounded sample of
+               the headline workload, on every core of this process's CPU share
+               (one single-threaded worker per core) and on one thread.
+Beside them: block copy / swap, a chunked-prefill step and a multi-query step
+over forked tables.
 """
 
 import argparse
@@ -33,6 +43,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOADS = {"tiny-fp32": 1, "7b-decode-bf16": 2, "32k-gqa-bf16": 3,
              "shared-prefix-bf16": 4, "fp8-kv": 5}
 DEFAULT_WORKLOAD = "7b-decode-bf16"
+DEFAULT_ALSO = "32k-gqa-bf16,shared-prefix-bf16,fp8-kv"
+CPU_SHARE = 16   # host cores one GPU's jobs may use at most
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
 KERNEL_SOURCES = ("decode_valu.hip", "decode_mfma.hip", "pkv_device.h", "pkv_internal.h")
 PREFILL_SOURCES = ("prefill_mfma.hip", "pkv_device.h", "pkv_internal.h")
@@ -54,8 +66,18 @@ def parse():
                          "('none': skip)")
     ap.add_argument("--no-block-copy", action="store_true",
                     help="skip the block copy / swap measurement")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="approximate CPU time budget for the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time budget of each oracle leg (one thread, all cores)")
+    ap.add_argument("--also", default=DEFAULT_ALSO,
+                    help="comma-separated decode workloads measured beside the headline one "
+                         "('none': skip)")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="MiB written before each timed iteration to evict the MALL (0: none)")
+    ap.add_argument("--flush-mode", default="write+read",
+                    choices=["write+read", "write", "read", "none"],
+                    help="how the MALL is flushed before each timed iteration")
+    ap.add_argument("--no-probe", dest="probe", action="store_false",
+                    help="skip the HBM read / gather ceiling probes")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB (5 times), to scale "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes")
@@ -114,40 +136,286 @@ def recorded_traffic(workload, sources=KERNEL_SOURCES):
     return None
 
 
-def cpu_baseline(w, budget_s, min_s=10.0):
-    """The oracle's decode, sequence by sequence on one host thread, repeated
-    over the batch until at least min_s seconds of work (or stopped at
-    budget_s): a bounded sample of the same workload."""
-    import oracle
-    from threadpoolctl import threadpool_limits
+# ----------------------------------------------------------- CPU oracle
 
-    kc, vc, ks, vs = w.key_cache, w.value_cache, w.key_scale, w.value_scale
+_CPU_W = None     # the workload the forked oracle workers decode (inherited)
+
+
+def _oracle_one(i):
+    """The oracle's decode of sequence i of _CPU_W (one sequence, every head)."""
+    import oracle
+    w = _CPU_W
+    oracle.paged_attention_decode(w.q[i:i + 1], w.key_cache, w.value_cache,
+                                  w.block_tables[i:i + 1], w.context_lens[i:i + 1], w.scale,
+                                  w.block_size, w.key_scale, w.value_scale)
+
+
+def _oracle_worker(args):
+    """Decode sequences first, first + step, .. of _CPU_W with one BLAS thread
+    until budget_s seconds have passed; returns (sequences, KV bytes, busy s)."""
+    first, step, budget_s = args
+    from threadpoolctl import threadpool_limits
+    w = _CPU_W
     elem = {"f32": 4, "bf16": 2, "fp8": 1}[w.cache_dtype]
-    t_total = 0.0
-    done_bytes = 0
-    done = 0
+    done = nbytes = 0
+    t0 = time.perf_counter()
     with threadpool_limits(limits=1):
-        while t_total < min(min_s, budget_s):
-            for i in range(w.S):
-                n = int(w.context_lens[i])
-                sub_tab = w.block_tables[i:i + 1]
-                t0 = time.perf_counter()
-                oracle.paged_attention_decode(w.q[i:i + 1], kc, vc, sub_tab,
-                                              w.context_lens[i:i + 1], w.scale, w.block_size,
-                                              ks, vs)
-                t_total += time.perf_counter() - t0
-                done_bytes += n * w.H_kv * w.D * elem * 2
+        while time.perf_counter() - t0 < budget_s:
+            for i in range(first, w.S, step):
+                _oracle_one(i)
                 done += 1
-                if t_total >= budget_s:
+                nbytes += int(w.context_lens[i]) * w.H_kv * w.D * elem * 2
+                if time.perf_counter() - t0 >= budget_s:
                     break
-            if done == 0:
-                break
-    passes = done / w.S if w.S else 0.0
-    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 numpy oracle decode, {done} sequence decodes ({passes:.2f} passes "
-                      f"over the {w.S} sequences; {done * w.H} seq-heads, "
-                      f"{done_bytes / 1e6:.1f} MB of KV) in {t_total:.1f} s on one host thread",
-            "seq_heads_per_s": done * w.H / t_total}
+    return done, nbytes, time.perf_counter() - t0
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands (float64 NumPy, untuned), on a bounded sample of
+    the workload: one host thread, then one single-threaded worker process per
+    core of this process's CPU share, each decoding its own sequences until
+    budget_s.  Runs before anything touches the GPU (the workers are forked)."""
+    import multiprocessing as mp
+    global _CPU_W
+    _CPU_W = w
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(affinity, CPU_SHARE))
+    one_n, one_b, one_t = _oracle_worker((0, 1, budget_s))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        parts = pool.map(_oracle_worker, [(k, cores, budget_s) for k in range(cores)])
+    wall = time.perf_counter() - t0
+    n_all = sum(p[0] for p in parts)
+    b_all = sum(p[1] for p in parts)
+    return {"value": round(b_all / wall / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle decode of {w.name}: {n_all} sequence decodes "
+                      f"({n_all / w.S:.2f} passes over the {w.S} sequences, "
+                      f"{b_all / 1e6:.0f} MB of KV) in {wall:.1f} s on {cores} worker processes "
+                      f"with one BLAS thread each (os.sched_getaffinity: {affinity} cores; "
+                      f"at most {CPU_SHARE} used)",
+            "seq_heads_per_s": round(n_all * w.H / wall, 1),
+            "single_thread": {"value": round(one_b / one_t / 1e9, 4), "unit": "GB/s",
+                              "cores": 1, "sequences": one_n,
+                              "seq_heads_per_s": round(one_n * w.H / one_t, 1),
+                              "seconds": round(one_t, 1)}}
+
+
+def oracle_state(w):
+    """The workload after its writes, done by the oracle (so the CPU decodes
+    the cache state the GPU step decodes)."""
+    import oracle
+    kc, vc, ks, vs = w.key_cache, w.value_cache, w.key_scale, w.value_scale
+    for k, v, s in w.writes:
+        if w.cache_dtype == "fp8":
+            kc, vc, ks, vs = oracle.paged_kv_cache_write(k, v, kc, vc, s, w.block_size, ks, vs)
+        else:
+            kc, vc = oracle.paged_kv_cache_write(k, v, kc, vc, s, w.block_size)
+    return workloads_replace(w, key_cache=kc, value_cache=vc, key_scale=ks, value_scale=vs)
+
+
+# ------------------------------------------------------------ GPU timing
+
+def progress(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def stats(ms):
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "mean": round(float(a.mean()), 5),
+            "n": int(a.size)}
+
+
+class Timer:
+    """Per-iteration HIP events on torch's current stream (the stream the
+    library launches on), with the MALL flushed before each iteration.
+
+    Flush modes: "write+read" (default) writes flush_mib MiB and then reads a
+    second buffer of the same size, so the 256 MB MALL and the L2s hold only
+    clean lines of that buffer when the events start; "write" only writes
+    (the dirty lines it leaves are written back while the timed kernel runs,
+    which slows even a plain read); "read" only reads."""
+
+    def __init__(self, torch, flush_mib, mode="write+read"):
+        self.torch = torch
+        self.mode = mode
+        self.flush = self.flush_rd = None
+        if flush_mib > 0 and mode != "none":
+            if "write" in mode:
+                self.flush = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
+            if "read" in mode:
+                self.flush_rd = torch.ones((flush_mib << 20) // 4, dtype=torch.float32,
+                                           device="cuda")
+                self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def _flush(self, i):
+        if self.flush is not None:
+            self.flush.fill_(i & 0xFF)
+        if self.flush_rd is not None:
+            import paged_kv_cache_370_amd as pkv
+            pkv.hbm_read_probe(self.flush_rd, self.sink)
+
+    def flushed(self, fn, iters, before=None):
+        """fn timed alone in each of iters iterations; before (untimed) and the
+        flush (a 512 MiB write, evicting the 256 MB MALL and the L2s) run
+        first, outside the events."""
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        torch.cuda.synchronize()
+        for i in range(iters):
+            if before is not None:
+                before()
+            self._flush(i)
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    def warm(self, fn, iters):
+        """Mean ms of iters back-to-back calls between two events (caches
+        warm, no flush)."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+
+def to_device(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def measure_decode(pkv, torch, timer, w, ps, steps, warmup, traffic_key):
+    """One decode workload on the GPU: the step (write of the step's tokens +
+    paged_attention_decode), the decode call alone and its partition kernel
+    alone, each with flushed per-iteration events; roofline of the partition
+    kernel on the workload's algorithmic bytes."""
+    t = lambda a: to_device(torch, a)
+    total_bytes, nblocks = kv_bytes(w)
+    q = t(w.q)
+    kc, vc = t(w.key_cache), t(w.value_cache)
+    ks = t(w.key_scale) if w.key_scale is not None else None
+    vs = t(w.value_scale) if w.value_scale is not None else None
+    tables, lens = t(w.block_tables), t(w.context_lens)
+    writes = [(t(k), t(v), t(s)) for k, v, s in w.writes]
+    out = torch.empty_like(q)
+    qc, cc = pkv.dtype_code(q), pkv.dtype_code(kc)
+    P = pkv.decode_partition_size(w.S, w.H, w.H_kv, w.D, w.block_size, w.max_context_len, qc,
+                                  cc, ps)
+    ws_bytes = pkv.decode_workspace_size(w.S, w.H, w.H_kv, w.D, w.block_size,
+                                         w.max_context_len, qc, cc, ps)
+    dws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")  # counters start at 0
+    wws_bytes = pkv.write_workspace_size(max(len(x[2]) for x in writes), w.H_kv, w.num_blocks, cc)
+    wws = torch.empty(max(wws_bytes, 1), dtype=torch.uint8, device="cuda") if wws_bytes else None
+
+    res = {"workload": w.name, "seqs": w.S, "q_heads": w.H, "kv_heads": w.H_kv,
+           "head_size": w.D, "block_size": w.block_size, "cache": w.cache_dtype,
+           "max_context": w.max_context_len,
+           "mean_context": round(float(np.mean(w.context_lens)), 1), "partition_size": P,
+           "kv_bytes_per_step": total_bytes, "kv_blocks_read": nblocks}
+
+    # Setup writes (the FP8 bulk write of positions 0..n-2) are not part of a
+    # step.  Their first run loads the kernels; the timed second run writes
+    # the same tokens to the same slots with the same result.
+    setup, step_write = writes[:-1], writes[-1]
+    if setup:
+        def bulk():
+            for k, v, s in setup:
+                pkv.paged_kv_cache_write(k, v, kc, vc, s, ks, vs, workspace=wws)
+        bulk()
+        setup_ms = timer.flushed(bulk, 1)[0]
+        setup_bytes = sum(x[0].numel() * x[0].element_size() * 2 for x in setup)
+        res["setup_write"] = {"ms": round(setup_ms, 3), "source_bytes": setup_bytes,
+                              "GB_per_s_source_read": round(setup_bytes / setup_ms / 1e6, 1)}
+        if w.cache_dtype == "fp8":
+            # the source is read twice (amax, then encode), one byte written per element
+            codes = sum(x[0].numel() * 2 for x in setup)
+            res["setup_write"]["GB_per_s_hbm"] = round((2 * setup_bytes + codes) / setup_ms / 1e6,
+                                                       1)
+
+    def write():
+        k, v, s = step_write
+        pkv.paged_kv_cache_write(k, v, kc, vc, s, ks, vs, workspace=wws)
+
+    def partitions():
+        pkv.paged_attention_decode_partitions(out, q, kc, vc, tables, lens, w.max_context_len,
+                                              w.scale, ks, vs, partition_size=ps, workspace=dws)
+
+    def reduce():
+        pkv.paged_attention_decode_reduce(out, lens, w.H_kv, w.block_size, w.max_context_len, cc,
+                                          partition_size=ps, workspace=dws)
+
+    def decode():
+        partitions()
+        reduce()
+
+    def step():
+        write()
+        decode()
+
+    for _ in range(warmup):
+        step()
+    step_ms = timer.flushed(step, steps)
+    decode_ms = timer.flushed(decode, steps, before=write)
+    part_ms = timer.flushed(partitions, steps, before=write)
+    warm = {"step": round(timer.warm(step, steps), 5),
+            "decode_partitions": round(timer.warm(partitions, steps), 5),
+            "decode_reduce": round(timer.warm(reduce, steps), 5),
+            "write": round(timer.warm(write, steps), 5)}
+    st, dc, pt = stats(step_ms), stats(decode_ms), stats(part_ms)
+    res.update({
+        "ms_per_step": st["median"],
+        "GB_per_s": round(total_bytes / (st["median"] * 1e-3) / 1e9, 2),
+        "pct_hbm_peak": round(100.0 * total_bytes / (st["median"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "seq_heads_per_s": round(w.S * w.H / (st["median"] * 1e-3), 1),
+        "flushed_ms": {"step": st, "decode": dc, "decode_partitions": pt},
+        "decode_GB_per_s": round(total_bytes / (dc["median"] * 1e-3) / 1e9, 2),
+        "decode_pct_hbm_peak": round(100.0 * total_bytes / (dc["median"] * 1e-3) / 1e9
+                                     / HBM_PEAK_GBS, 2),
+        "warm_ms_back_to_back": warm,
+    })
+    achieved = total_bytes / (pt["mean"] * 1e-3) / 1e9
+    res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                       "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                       "traffic": recorded_traffic(traffic_key),
+                       "kernel": "decode partition kernel (mean flushed launch)",
+                       "kernel_sources": kernel_source_hash()}
+    if w.shared_blocks > 0:
+        res["read_once"] = read_once_bench(pkv, torch, timer, w, out, q, kc, vc, ks, vs, tables,
+                                           lens, total_bytes, steps)
+    return res
+
+
+def probe_bench(pkv, torch, timer, iters, gib=1):
+    """Practical HBM ceiling on this device: a streaming read of a 1 GiB
+    buffer, and a gather of 4 KiB tiles (one (block, KV head) tile of a bf16
+    cache at bs 16, D 128) in random order over the same buffer, flushed per
+    iteration like the decode timings."""
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tile = 4096
+    rng = np.random.default_rng(11)
+    tiles = torch.from_numpy(rng.permutation(nbytes // tile).astype(np.int32)).cuda()
+    pkv.hbm_read_probe(buf, sink)
+    pkv.hbm_gather_probe(buf, tiles, tile, sink)
+    rd = stats(timer.flushed(lambda: pkv.hbm_read_probe(buf, sink), iters))
+    ga = stats(timer.flushed(lambda: pkv.hbm_gather_probe(buf, tiles, tile, sink), iters))
+    return {"bytes": nbytes,
+            "read_GB_per_s": round(nbytes / (rd["median"] * 1e-3) / 1e9, 1),
+            "gather_4KiB_tiles_GB_per_s": round(nbytes / (ga["median"] * 1e-3) / 1e9, 1),
+            "read_ms": rd, "gather_ms": ga}
 
 
 def main():
@@ -161,228 +429,130 @@ def main():
         calibrate_copy(args.calibrate_copy_mib)
         return
 
-    import torch
-    import paged_kv_cache_370_amd as pkv
     import workloads
 
-    pkv.load()
     cfg = WORKLOADS[args.workload]
     t0 = time.perf_counter()
     w = workloads.make_config(cfg)
     gen_s = time.perf_counter() - t0
-    total_bytes, nblocks = kv_bytes(w)
     ps = w.partition_size if args.partition_size < 0 else args.partition_size
 
-    dev = torch.device("cuda:0")
+    # The CPU oracle runs first, before anything touches the GPU.
+    cpu = None
+    if not args.no_cpu_baseline:
+        progress(f"CPU oracle baseline on {w.name}")
+        cpu = cpu_baseline(oracle_state(w), args.cpu_seconds)
 
-    def t(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
-    q = t(w.q)
-    kc, vc = t(w.key_cache), t(w.value_cache)
-    ks = t(w.key_scale) if w.key_scale is not None else None
-    vs = t(w.value_scale) if w.value_scale is not None else None
-    tables, lens = t(w.block_tables), t(w.context_lens)
-    writes = [(t(k), t(v), t(s)) for k, v, s in w.writes]
-    out = torch.empty_like(q)
-    qc, cc = pkv.dtype_code(q), pkv.dtype_code(kc)
-    P = pkv.decode_partition_size(w.S, w.H, w.H_kv, w.D, w.block_size, w.max_context_len, qc, cc, ps)
-    ws_bytes = pkv.decode_workspace_size(w.S, w.H, w.H_kv, w.D, w.block_size, w.max_context_len,
-                                         qc, cc, ps)
-    dws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # counters start at 0
-    wws_bytes = pkv.write_workspace_size(max(len(x[2]) for x in writes), w.H_kv, w.num_blocks, cc)
-    wws = torch.empty(max(wws_bytes, 1), dtype=torch.uint8, device=dev) if wws_bytes else None
-
-    # Setup writes (FP8: the bulk write of positions 0..n-2) are not part of a step.
-    setup = writes[:-1]
-    step_write = writes[-1]
-    setup_ms = None
-    if setup:
-        # The first run loads the write kernels; the timed second run writes
-        # the same tokens to the same slots, with the same result (every
-        # block it writes is fresh again, so its scales are set again from
-        # the same values).
-        for k, v, s in setup:
-            pkv.paged_kv_cache_write(k, v, kc, vc, s, ks, vs, workspace=wws)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for k, v, s in setup:
-            pkv.paged_kv_cache_write(k, v, kc, vc, s, ks, vs, workspace=wws)
-        e1.record()
-        torch.cuda.synchronize()
-        setup_ms = e0.elapsed_time(e1)
-
-    def step(ev=None):
-        k, v, s = step_write
-        if ev: ev[0].record()
-        pkv.paged_kv_cache_write(k, v, kc, vc, s, ks, vs, workspace=wws)
-        if ev: ev[1].record()
-        pkv.paged_attention_decode_partitions(out, q, kc, vc, tables, lens, w.max_context_len,
-                                              w.scale, ks, vs, partition_size=ps, workspace=dws)
-        if ev: ev[2].record()
-        pkv.paged_attention_decode_reduce(out, lens, w.H_kv, w.block_size, w.max_context_len, cc,
-                                          partition_size=ps, workspace=dws)
-        if ev: ev[3].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Timed region: K whole steps back to back, bracketed by two events only
-    # (an event between kernels adds a marker packet to the queue).
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
-    # Per-kernel times: the same K steps again with an event around each
-    # kernel, on the stream the kernels run on.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    ms_step_with_events = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
-    write_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    part_ms_in_step = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    red_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    # The partition kernel's launch duration for the roofline: K launches
-    # back to back between two events (the kernel is idempotent: same
-    # inputs, same outputs, its counters return to zero), so the average
-    # holds one launch gap instead of two event packets.
-    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    p0.record()
-    for _ in range(args.steps):
-        pkv.paged_attention_decode_partitions(out, q, kc, vc, tables, lens, w.max_context_len,
-                                              w.scale, ks, vs, partition_size=ps, workspace=dws)
-    p1.record()
-    torch.cuda.synchronize()
-    part_ms = p0.elapsed_time(p1) / args.steps
-
-    value = total_bytes / (ms_step * 1e-3) / 1e9
-    achieved = total_bytes / (part_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(args.workload)
+    import torch
+    import paged_kv_cache_370_amd as pkv
+    pkv.load()
+    timer = Timer(torch, args.flush_mib, args.flush_mode)
+    progress(f"decode {w.name}")
+    head = measure_decode(pkv, torch, timer, w, ps, args.steps, args.warmup, args.workload)
+    del w
 
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["GB_per_s"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8e4m3-kv/bf16-q"}[w.cache_dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8e4m3-kv/bf16-q"}[head["cache"]],
         "data": "synthetic",
-        "config": {
-            "workload": w.name, "seqs": w.S, "q_heads": w.H, "kv_heads": w.H_kv,
-            "head_size": w.D, "block_size": w.block_size, "max_context": w.max_context_len,
-            "mean_context": round(float(np.mean(w.context_lens)), 1),
-            "partition_size": P, "kv_bytes_per_step": total_bytes, "kv_blocks_read": nblocks,
-            "step": "paged_kv_cache_write + decode partitions + reduce",
-        },
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "seq_heads_per_s": round(w.S * w.H / (ms_step * 1e-3), 1),
-        "kernel_ms": {"write": round(write_ms, 5), "decode_partitions": round(part_ms, 5),
-                      "decode_partitions_in_step": round(part_ms_in_step, 5),
-                      "decode_reduce": round(red_ms, 5),
-                      "step_with_events": round(ms_step_with_events, 5)},
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": "decode partition kernel",
-            "kernel_sources": kernel_source_hash(),
-        },
+        "config": {k: head[k] for k in ("workload", "seqs", "q_heads", "kv_heads", "head_size",
+                                        "block_size", "max_context", "mean_context",
+                                        "partition_size", "kv_bytes_per_step", "kv_blocks_read")},
+        "pct_hbm_peak": head["pct_hbm_peak"],
+        "seq_heads_per_s": head["seq_heads_per_s"],
+        "timing": (f"median of per-iteration HIP events; before each iteration, outside the "
+                   f"events, the MALL is flushed ({args.flush_mode}, {args.flush_mib} MiB)"),
+        "step": "paged_kv_cache_write + decode partitions + reduce",
+        "flushed_ms": head["flushed_ms"],
+        "decode_GB_per_s": head["decode_GB_per_s"],
+        "decode_pct_hbm_peak": head["decode_pct_hbm_peak"],
+        "warm_ms_back_to_back": head["warm_ms_back_to_back"],
+        "roofline": head["roofline"],
         "input_generation_s": round(gen_s, 2),
     }
-    if setup_ms is not None:
-        setup_bytes = sum(x[0].numel() * x[0].element_size() * 2 for x in setup)
-        result["setup_write"] = {"ms": round(setup_ms, 3),
-                                 "source_bytes": setup_bytes,
-                                 "GB_per_s_source_read": round(setup_bytes / setup_ms / 1e6, 1)}
-        if w.cache_dtype == "fp8":
-            # the source is read twice (amax, then encode), one byte written per element
-            codes = sum(x[0].numel() * 2 for x in setup)
-            result["setup_write"]["GB_per_s_hbm"] = round((2 * setup_bytes + codes) / setup_ms / 1e6, 1)
+    for k in ("setup_write", "read_once"):
+        if k in head:
+            result[k] = head[k]
+    if args.probe:
+        progress("HBM read / gather probes")
+        result["ceiling"] = probe_bench(pkv, torch, timer, args.steps)
+        result["ceiling_gbs"] = result["ceiling"]["read_GB_per_s"]
+    extra = [x for x in args.also.split(",") if x and x != "none" and x != args.workload]
+    if extra:
+        result["workloads"] = {}
+    for name in extra:
+        progress(f"decode {name}")
+        wx = workloads.make_config(WORKLOADS[name])
+        result["workloads"][name] = measure_decode(pkv, torch, timer, wx, wx.partition_size,
+                                                   args.steps, args.warmup, name)
+        del wx
+        torch.cuda.empty_cache()
     if not args.no_block_copy:
-        result["block_copy"] = block_copy_bench(pkv, torch, kc, vc, ks, vs, args.steps)
-    if w.shared_blocks > 0:
-        result["read_once"] = read_once_bench(pkv, torch, w, out, q, kc, vc, ks, vs, tables, lens,
-                                              total_bytes, args.steps)
+        progress("block copy / swap")
+        result["block_copy"] = block_copy_bench(pkv, torch, args.steps)
     if args.prefill != "none":
+        progress(f"prefill {args.prefill}")
         result["prefill"] = prefill_bench(pkv, torch, args.prefill, args.steps)
     if args.beam_fork != "none":
+        progress(f"beams over forked tables {args.beam_fork}")
         result["beam_fork"] = beam_fork_bench(pkv, torch, args.beam_fork, args.steps)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_for(w, writes, args.cpu_seconds)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
-def block_copy_bench(pkv, torch, kc, vc, ks, vs, reps, copy_pairs=1024, swap_pairs=256):
-    """Times paged_kv_block_copy on the workload's pool: copy_pairs random
+def block_copy_bench(pkv, torch, reps, pool_blocks=4096, copy_pairs=1024, swap_pairs=256):
+    """Times paged_kv_block_copy on a pool of the 7B-class shape (bf16, 32 KV
+    heads, bs 16, D 128: 256 KiB per block with K and V): copy_pairs random
     blocks into a second device pool (the copy-on-write shape: HBM read and
     write), and swap_pairs blocks out to a pinned host pool and back in
-    (PCIe).  Bytes count the K and V tiles (and FP8 scales) moved once."""
+    (PCIe).  Bytes count the K and V tiles moved once."""
     rng = np.random.default_rng(7)
-    nb = kc.shape[0]
-    dev = kc.device
-    block_bytes = 2 * kc[0].numel() * kc.element_size() + (
-        2 * ks[0].numel() * 4 if ks is not None else 0)
+    dev = torch.device("cuda")
+    shape = (pool_blocks, 32, 16, 128)
+    kc = torch.randn(shape, device=dev).to(torch.bfloat16)
+    vc = torch.randn(shape, device=dev).to(torch.bfloat16)
+    block_bytes = 2 * kc[0].numel() * kc.element_size()
 
     def pool(blocks, pinned=False):
-        mk = (lambda t: torch.empty((blocks,) + tuple(t.shape[1:]), dtype=t.dtype,
-                                    pin_memory=True)) if pinned else (
-            lambda t: torch.empty((blocks,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev))
-        return (mk(kc), mk(vc), mk(ks) if ks is not None else None,
-                mk(vs) if vs is not None else None)
+        if pinned:
+            mk = lambda: torch.empty((blocks,) + shape[1:], dtype=kc.dtype, pin_memory=True)
+        else:
+            mk = lambda: torch.empty((blocks,) + shape[1:], dtype=kc.dtype, device=dev)
+        return (mk(), mk())
 
     def timed(src, dst, pairs):
-        pkv.paged_kv_block_copy(src[0], src[1], dst[0], dst[1], pairs, src[2], src[3], dst[2],
-                                dst[3])
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            pkv.paged_kv_block_copy(src[0], src[1], dst[0], dst[1], pairs, src[2], src[3],
-                                    dst[2], dst[3])
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / reps * 1e3
+        call = lambda: pkv.paged_kv_block_copy(src[0], src[1], dst[0], dst[1], pairs)
+        call()
+        us = stats([1e3 * x for x in Timer(torch, 0).flushed(call, reps)])["median"]
         n = pairs.shape[0]
         return {"pairs": n, "us": round(us, 2), "bytes_moved": n * block_bytes,
                 "GB_per_s": round(n * block_bytes / (us * 1e-6) / 1e9, 1)}
 
-    src = (kc, vc, ks, vs)
-    n = min(copy_pairs, nb)
-    pairs = torch.from_numpy(np.stack([rng.choice(nb, n, replace=False), rng.permutation(n)],
-                                      axis=1).astype(np.int32)).to(dev)
-    out = {"block_bytes": block_bytes,
-           "device_copy": timed(src, pool(n), pairs)}
-    m = min(swap_pairs, nb)
+    src = (kc, vc)
+    n = min(copy_pairs, pool_blocks)
+    pairs = torch.from_numpy(np.stack([rng.choice(pool_blocks, n, replace=False),
+                                       rng.permutation(n)], axis=1).astype(np.int32)).to(dev)
+    out = {"block_bytes": block_bytes, "device_copy": timed(src, pool(n), pairs)}
+    m = min(swap_pairs, pool_blocks)
     host = pool(m, pinned=True)
-    out_pairs = torch.from_numpy(np.stack([rng.choice(nb, m, replace=False), rng.permutation(m)],
-                                          axis=1).astype(np.int32)).to(dev)
+    out_pairs = torch.from_numpy(np.stack([rng.choice(pool_blocks, m, replace=False),
+                                           rng.permutation(m)], axis=1).astype(np.int32)).to(dev)
     out["swap_out"] = timed(src, host, out_pairs)
     in_pairs = torch.from_numpy(np.stack([rng.permutation(m), rng.permutation(m)],
                                          axis=1).astype(np.int32)).to(dev)
     out["swap_in"] = timed(host, pool(m), in_pairs)
-    out["note"] = ("device_copy moves each byte HBM to HBM (it is read and written: 2x the "
-                   "bytes in HBM traffic); swaps cross PCIe once")
+    out["note"] = ("median of per-call events, no flush; device_copy moves each byte HBM to HBM "
+                   "(read and written: 2x the bytes in HBM traffic); swaps cross PCIe once")
     return out
 
 
@@ -456,10 +626,11 @@ def prefill_bench(pkv, torch, name, reps):
                          "kernel_sources": kernel_source_hash(PREFILL_SOURCES)}}
 
 
-def read_once_bench(pkv, torch, w, out, q, kc, vc, ks, vs, tables, lens, unique_bytes, reps):
+def read_once_bench(pkv, torch, timer, w, out, q, kc, vc, ks, vs, tables, lens, unique_bytes,
+                    reps):
     """Times paged_attention_decode_shared_prefix on the shared-prefix
-    workload: the prefix once per KV head for all sequences, each sequence's
-    suffix, and the merge (three launches), K calls back to back."""
+    workload (the prefix once per KV head for all sequences, each sequence's
+    suffix, and the merge), flushed per iteration like the decode."""
     prefix = w.shared_blocks * w.block_size
     qc, cc = pkv.dtype_code(q), pkv.dtype_code(kc)
     need = pkv.shared_prefix_workspace_size(w.S, w.H, w.H_kv, w.D, w.block_size,
@@ -472,18 +643,11 @@ def read_once_bench(pkv, torch, w, out, q, kc, vc, ks, vs, tables, lens, unique_
 
     for _ in range(3):
         call()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    return {"prefix_tokens": prefix, "ms_per_call": round(ms, 5),
-            "GB_per_s_unique": round(unique_bytes / (ms * 1e-3) / 1e9, 1),
-            "note": "decode of the same batch (prefix pass + suffix partitions + reduce); "
-                    "compare with kernel_ms decode_partitions + decode_reduce"}
+    st = stats(timer.flushed(call, reps))
+    return {"prefix_tokens": prefix, "ms_per_call": st["median"], "flushed_ms": st,
+            "GB_per_s_unique": round(unique_bytes / (st["median"] * 1e-3) / 1e9, 1),
+            "note": "decode of the same batch through the read-once call; compare with "
+                    "flushed_ms.decode"}
 
 
 def beam_fork_bench(pkv, torch, name, reps):
@@ -543,20 +707,6 @@ def beam_fork_bench(pkv, torch, name, reps):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "kernel": "decode kernel, multi-token mode (unique bytes)"}}
-
-
-def cpu_baseline_for(w, writes, budget):
-    """The oracle first performs the workload's writes itself (untimed), so it
-    decodes the same cache state the GPU step decodes."""
-    import oracle
-    kc, vc, ks, vs = w.key_cache, w.value_cache, w.key_scale, w.value_scale
-    for k, v, s in w.writes:
-        if w.cache_dtype == "fp8":
-            kc, vc, ks, vs = oracle.paged_kv_cache_write(k, v, kc, vc, s, w.block_size, ks, vs)
-        else:
-            kc, vc = oracle.paged_kv_cache_write(k, v, kc, vc, s, w.block_size)
-    w = workloads_replace(w, key_cache=kc, value_cache=vc, key_scale=ks, value_scale=vs)
-    return cpu_baseline(w, budget)
 
 
 def workloads_replace(w, **kw):

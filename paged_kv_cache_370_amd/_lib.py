@@ -37,6 +37,8 @@ EXPORTS = (
     "paged_attention_decode_noalloc_max_workspace",
     "pkv_status_string",
     "pkv_version",
+    "pkv_hbm_read_probe",
+    "pkv_hbm_gather_probe",
 )
 
 
@@ -94,6 +96,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode_shared_prefix_workspace_size.argtypes = [i32] * 10
     lib.paged_kv_block_copy.restype = i32
     lib.paged_kv_block_copy.argtypes = [vp] * 9 + [i32] * 5 + [vp]
+    lib.pkv_hbm_read_probe.restype = i32
+    lib.pkv_hbm_read_probe.argtypes = [vp, sz, vp, vp]
+    lib.pkv_hbm_gather_probe.restype = i32
+    lib.pkv_hbm_gather_probe.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [i32]
     lib.pkv_version.restype = i32
@@ -374,3 +380,23 @@ def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, co
         _ptr(workspace), wbytes, _stream(stream))
     _check(st, "paged_attention_prefill")
 
+
+# ------------------------------------------------------- measurement aids
+
+def hbm_read_probe(buf, sink, stream=None):
+    """Read every byte of the contiguous device tensor buf once."""
+    _contig(buf)
+    _check(load().pkv_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                     _stream(stream)), "pkv_hbm_read_probe")
+
+
+def hbm_gather_probe(buf, tiles, tile_bytes, sink, stream=None):
+    """Read whole tiles of tile_bytes bytes of buf in the order of the int32
+    device tensor tiles (ids must lie inside buf)."""
+    _contig(buf, tiles)
+    if tiles.dtype != torch.int32:
+        raise ValueError("tiles must be int32")
+    if tiles.numel() and int(tiles.max()) * tile_bytes + tile_bytes > buf.numel() * buf.element_size():
+        raise ValueError("a tile id lies outside the buffer")
+    _check(load().pkv_hbm_gather_probe(_ptr(buf), _ptr(tiles), tiles.numel(), int(tile_bytes),
+                                       _ptr(sink), _stream(stream)), "pkv_hbm_gather_probe")
