@@ -25,21 +25,43 @@ bool decode_pair_ok(int q, int c) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Partition size in tokens, or -1.  A context that fits one partition is
-// finished by the partition kernel itself; longer contexts are split into
-// partitions of kDefaultPartition tokens (twice that for FP8 caches, so a
-// partition holds the same K/V bytes and the per-item costs, the merge and
-// the partial store, are spread over as many bytes; on the FP8 workload
-// 1024-token partitions took 169 us against 176 us) so that long sequences
-// spread over many workgroups.
-int resolve_partition(int bs, int max_ctx, int requested, int cache_dtype) {
+// finished by the partition kernel itself.  The decode kernel takes its
+// items longest first; the choice below follows what was measured on
+// MI355X (bf16 7B-class batch, FP8 batch, shared-prefix batch):
+//   * few (sequence, KV head) items (`items` < kWholeMinItems): contexts are
+//     split into partitions of kDefaultPartition tokens (twice that for FP8
+//     caches, the same K/V bytes per item), so long sequences spread over
+//     many workgroups;
+//   * kWholeMinItems .. kHalfMaxItems items (under two per workgroup):
+//     whole contexts up to one item's table (kDecodeMaxTable blocks), so no
+//     partials are left to merge (shared-prefix batch: 90 -> 82 us);
+//   * more items: partitions of half the longest context (at least the
+//     default, at most one item's table): the workgroups sharing a CU are
+//     served at up to 3x different rates, and items that large would keep
+//     the slowest ones busy past the others (7B-class: 204 us at 512, 202
+//     at 1024, 205-210 whole; FP8: 177 us at 1024, 165 at 4096).
+constexpr long long kWholeMinItems = 1024;
+constexpr long long kHalfMaxItems = 1536;
+
+int resolve_partition(int bs, int max_ctx, int requested, int cache_dtype, long long items = 0) {
   if (requested < 0) return -1;
   if (requested > 0) return requested % bs == 0 ? requested : -1;
   const int def = cache_dtype == PKV_FP8_E4M3 ? 2 * kDefaultPartition : kDefaultPartition;
-  if (max_ctx <= def) {
-    const int p = ((max_ctx + bs - 1) / bs) * bs;
-    return p < bs ? bs : p;
+  const int whole = std::max(bs, ((max_ctx + bs - 1) / bs) * bs);
+  if (max_ctx <= def) return whole;
+  const int cap = kDecodeMaxTable * bs;
+  if (items >= kHalfMaxItems) {
+    const int half = ((max_ctx + 1) / 2 + bs - 1) / bs * bs;
+    return std::min(cap, std::max(def, half));
   }
+  if (items >= kWholeMinItems) return std::min(whole, cap);
   return def;
+}
+
+// (sequence, KV head, 16-row chunk) items of a call whose contexts are not split.
+long long context_items(int S, int H, int H_kv, int M = 1) {
+  if (H_kv <= 0 || H % H_kv != 0) return 0;
+  return (long long)S * H_kv * (((long long)M * (H / H_kv) + 15) / 16);
 }
 
 int num_partitions(int max_ctx, int P) {
@@ -88,7 +110,7 @@ DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
     r.status = PKV_ERR_SHAPE;
     return r;
   }
-  const int P = resolve_partition(bs, max_ctx, partition, c);
+  const int P = resolve_partition(bs, max_ctx, partition, c, context_items(S, H, H_kv, M));
   if (P <= 0) {
     r.status = PKV_ERR_SHAPE;
     return r;
@@ -237,7 +259,8 @@ int32_t paged_attention_decode_partition_size(int32_t num_seqs, int32_t num_head
   if (check_decode_shape(num_seqs, num_heads, num_kv_heads, head_size, block_size,
                          max_context_len, q_dtype, cache_dtype) != PKV_OK)
     return -1;
-  return resolve_partition(block_size, max_context_len, partition_size, cache_dtype);
+  return resolve_partition(block_size, max_context_len, partition_size, cache_dtype,
+                           context_items(num_seqs, num_heads, num_kv_heads));
 }
 
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads,

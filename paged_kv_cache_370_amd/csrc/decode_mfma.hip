@@ -440,25 +440,94 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_red, int* tota
 
 // Item order of the sequence scan: first every full partition (P tokens) of
 // every sequence, then every sequence's last, shorter partition (a sequence
-// of length 0 has one empty item, which writes zeros).  Short items thus run
-// last, which keeps the end of the kernel balanced across workgroups.
-//   s_full[i]: full partitions of sequences 0..i-1   (s_full[S] = F)
-//   s_rag[i]:  short partitions of sequences 0..i-1  (s_rag[S] = R)
-//   s_len[i]:  context length of sequence i
+// of length 0 has one empty item, which writes zeros).  Sequences are taken
+// in order of decreasing size of that last partition (longest processing
+// time first): with whole contexts as items (P at least the longest
+// context) the longest contexts start first and the shortest run last,
+// which keeps the end of the kernel balanced across workgroups.
+//   s_seq[k]:   the sequence at sorted position k and its context length n,
+//               packed as n << kSeqBits | sequence (n < 2^(31 - kSeqBits))
+//   s_full[k]:  full partitions of the sequences at positions 0..k-1
+//               (s_full[S] = F)
+//   s_rag[k]:   short partitions of the sequences at positions 0..k-1
+//               (s_rag[S] = R)
 // Returns F (and R in *n_rag).  Every thread of the workgroup calls it.
-template <int MODE>
-__device__ int build_offsets(const MfmaParams& p, int* s_full, uint16_t* s_rag, int* s_len,
-                             int* s_red, int* n_rag) {
+//
+// The sort is a stable counting sort on the last partition's size in blocks
+// (clamped to kSortKeys - 1), so every workgroup computes the same order:
+// thread t holds sequences t and t + 256, i.e. wave w holds the 64-sequence
+// chunks w and w + 4; per-chunk key counts give each sequence the number of
+// equal keys in earlier chunks, and a ballot within the wave its rank among
+// equal keys in its own chunk.  s_tmp: 9 KiB of LDS scratch.
+constexpr int kSortKeys = 256;
+constexpr int kSeqBits = 9;  // sequence index bits of an s_seq entry
+static_assert((1 << kSeqBits) >= kMaxScanSeqs, "sequence index field");
+
+template <int MODE, int BS>
+__device__ int build_offsets(const MfmaParams& p, int* s_full, uint16_t* s_rag, int* s_seq,
+                             int* s_red, int* s_tmp, int* n_rag) {
   constexpr int NTH = kNW * 64;
-  const int tid = threadIdx.x;
+  constexpr int NCH = kMaxScanSeqs / 64;  // 64-sequence chunks
+  static_assert(kMaxScanSeqs <= 2 * NTH && kSortKeys == NTH, "two sequences, one key per thread");
+  const int tid = threadIdx.x, lane = tid & 63;
+  int* cnt = s_tmp;                     // [NCH][kSortKeys]
+  int* first = s_tmp + NCH * kSortKeys;  // [kSortKeys]: sequences with a larger key
+  for (int k = tid; k < NCH * kSortKeys; k += NTH) cnt[k] = 0;
+  __syncthreads();
+  int key[2], len[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = tid + r * NTH;
+    key[r] = -1;
+    len[r] = 0;
+    if (i < p.S) {
+      const int n = seq_len<MODE>(p, i);
+      len[r] = n;
+      const int last = n > 0 ? n - ((n - 1) / p.P) * p.P : 0;  // tokens of the last partition
+      key[r] = min((last + BS - 1) / BS, kSortKeys - 1);
+      atomicAdd(&cnt[(i >> 6) * kSortKeys + key[r]], 1);
+    }
+  }
+  __syncthreads();
+  {
+    // thread t owns key kSortKeys - 1 - t: the scan over threads then runs
+    // over keys in decreasing order
+    const int k = kSortKeys - 1 - tid;
+    int run = 0;
+    for (int c = 0; c < NCH; ++c) {
+      const int v = cnt[c * kSortKeys + k];
+      cnt[c * kSortKeys + k] = run;  // equal keys in earlier chunks
+      run += v;
+    }
+    int total;
+    first[k] = block_exclusive_scan(run, s_red, &total);  // has barriers
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = tid + r * NTH;
+    const bool valid = key[r] >= 0;
+    unsigned long long todo = __ballot(valid);
+    int rank = 0;
+    while (todo) {  // uniform: one round per distinct key in the wave
+      const int leader = __builtin_ffsll((long long)todo) - 1;
+      const int kl = __builtin_amdgcn_readlane(key[r], leader);
+      const unsigned long long m = __ballot(valid && key[r] == kl);
+      if (valid && key[r] == kl) rank = __builtin_popcountll(m & ((1ull << lane) - 1ull));
+      todo &= ~m;
+    }
+    if (valid)
+      s_seq[first[key[r]] + cnt[(i >> 6) * kSortKeys + key[r]] + rank] = (len[r] << kSeqBits) | i;
+  }
+  __syncthreads();
+
   const int per = (p.S + NTH - 1) / NTH;
   const int base = tid * per;
   int nf = 0, nr = 0;
   for (int k = 0; k < per; ++k) {
-    const int i = base + k;
-    if (i < p.S) {
-      const int n = seq_len<MODE>(p, i);
-      s_len[i] = n;
+    const int pos = base + k;
+    if (pos < p.S) {
+      const int n = s_seq[pos] >> kSeqBits;
       nf += n / p.P;
       nr += (n % p.P != 0 || n == 0) ? 1 : 0;
     }
@@ -467,11 +536,11 @@ __device__ int build_offsets(const MfmaParams& p, int* s_full, uint16_t* s_rag, 
   int ef = block_exclusive_scan(nf, s_red, &F);
   int er = block_exclusive_scan(nr, s_red, &R);
   for (int k = 0; k < per; ++k) {
-    const int i = base + k;
-    if (i < p.S) {
-      const int n = s_len[i];
-      s_full[i] = ef;
-      s_rag[i] = (uint16_t)er;
+    const int pos = base + k;
+    if (pos < p.S) {
+      const int n = s_seq[pos] >> kSeqBits;
+      s_full[pos] = ef;
+      s_rag[pos] = (uint16_t)er;
       ef += n / p.P;
       er += (n % p.P != 0 || n == 0) ? 1 : 0;
     }
@@ -506,10 +575,16 @@ struct Item {
   Part w;
 };
 
+// The workgroup's LDS view of the item order.
+struct Order {
+  const int* full;
+  const uint16_t* rag;
+  const int* seq;  // n << kSeqBits | sequence, by sorted position
+};
+
 template <int BS, bool SCAN, int MODE>
 __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y, int n_full,
-                                            const int* s_full, const uint16_t* s_rag,
-                                            const int* s_len) {
+                                            const Order& o) {
   Item it;
   const int y = item % Y;
   const int rest = item / Y;
@@ -517,14 +592,18 @@ __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y
   if constexpr (SCAN) {
     // Values read from LDS are per-lane to the compiler; the item is uniform
     // over the workgroup, so move them to scalar registers.
+    int packed;
     if (rest < n_full) {
-      seq = __builtin_amdgcn_readfirstlane(find_seq(s_full, p.S, rest));
-      it.part = rest - __builtin_amdgcn_readfirstlane(s_full[seq]);
+      const int pos = __builtin_amdgcn_readfirstlane(find_seq(o.full, p.S, rest));
+      packed = __builtin_amdgcn_readfirstlane(o.seq[pos]);
+      it.part = rest - __builtin_amdgcn_readfirstlane(o.full[pos]);
     } else {
-      seq = __builtin_amdgcn_readfirstlane(find_seq(s_rag, p.S, rest - n_full));
-      it.part = __builtin_amdgcn_readfirstlane(s_len[seq]) / p.P;
+      const int pos = __builtin_amdgcn_readfirstlane(find_seq(o.rag, p.S, rest - n_full));
+      packed = __builtin_amdgcn_readfirstlane(o.seq[pos]);
+      it.part = (packed >> kSeqBits) / p.P;
     }
-    it.n = __builtin_amdgcn_readfirstlane(s_len[seq]);
+    seq = min(packed & ((1 << kSeqBits) - 1), p.S - 1);
+    it.n = packed >> kSeqBits;
     it.live = true;
   } else {
     seq = rest / p.NP;
@@ -608,7 +687,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   __shared__ int s_zero[4];  // block id 0 for the dummy row
   __shared__ int s_full[SCAN ? kMaxScanSeqs + 1 : 1];
   __shared__ uint16_t s_rag[SCAN ? kMaxScanSeqs + 1 : 1];
-  __shared__ int s_len[SCAN ? kMaxScanSeqs : 1];
+  __shared__ int s_seq[SCAN ? kMaxScanSeqs : 1];
+  static_assert(UNION_BYTES >= (kMaxScanSeqs / 64 + 1) * kSortKeys * 4, "sort scratch");
+  const Order order{s_full, s_rag, s_seq};
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps selects scalar
@@ -639,7 +720,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   int total, n_full = 0;
   if constexpr (SCAN) {
     int n_rag;
-    n_full = build_offsets<MODE>(p, s_full, s_rag, s_len, s_red, &n_rag);  // has barriers
+    // has barriers; s_raw is free until the first chunk
+    n_full = build_offsets<MODE, BS>(p, s_full, s_rag, s_seq, s_red,
+                                     reinterpret_cast<int*>(s_raw), &n_rag);
     total = Y * (n_full + n_rag);
   } else {
     total = Y * p.S * p.NP;
@@ -656,7 +739,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   int nxt = s_next[1];
   int buf = 0;
   constexpr int EPC = Gm::CHUNK / BS;  // block ids per chunk
-  Item it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, s_full, s_rag, s_len);
+  Item it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, order);
   // The first item's block ids and Q and the second item's block ids are
   // requested together (one memory round trip before the first chunk's
   // loads, not three).  The second item's ids travel in a register until
@@ -665,7 +748,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   const int tab_first = fetch_tab<CT, D, BS>(p, it.w, wave, lane);
   const uint4 q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
   int tab_next = fetch_tab<CT, D, BS>(
-      p, decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len).w, wave,
+      p, decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, order).w, wave,
       lane);
   if (cur < total) {
     store_tab(tab_first, s_wtab[0][wave], lane);
@@ -703,7 +786,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     int* wt_nxt = s_wtab[buf ^ 1][wave];
     // Prefetch the next item's Q.  Nothing reads the other buffers until the
     // next item.
-    const Item nx = decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, s_full, s_rag, s_len);
+    const Item nx = decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, order);
     const uint4 q_next = fetch_q<CT, D, MODE>(p, nx.w, tid);
     // The claim of the item after the next one, made at the start of wave
     // 0's last step (before its loads) and used only after barrier X.
@@ -828,7 +911,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     const int nn = __builtin_amdgcn_readfirstlane(s_next[0]);
     use_shared = __builtin_amdgcn_readfirstlane(s_next[2]);
     tab_next = fetch_tab<CT, D, BS>(
-        p, decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, s_full, s_rag, s_len).w, wave,
+        p, decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, order).w, wave,
         lane);
 
     // Thread t merges 4 consecutive d of one head: one 16-byte LDS read per
@@ -922,7 +1005,8 @@ unsigned persistent_grid(long long items) {
 
 template <typename CT, int D, int BS, int MODE>
 hipError_t launch_mode(const DecodeArgs& a, const MfmaParams& p, long long items) {
-  if (a.S <= kMaxScanSeqs) {
+  // The sorted item order packs a context length into 31 - kSeqBits bits.
+  if (a.S <= kMaxScanSeqs && a.max_ctx < (1 << (31 - kSeqBits))) {
     hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, true, MODE>),
                        dim3(persistent_grid<CT, D, BS, true, MODE>(items)), dim3(kNW * 64), 0,
                        a.stream, p);

@@ -48,10 +48,18 @@ def test_status_strings_and_version():
 def test_partition_and_workspace_queries():
     # context fits one partition: only the 4 KiB work-queue header
     assert pkv.decode_partition_size(4, 8, 8, 128, 16, 300, 1, 1, 0) == 304
-    # library choice: 512-token partitions for bf16 caches, 1024 for FP8
+    # library choice with few (sequence, KV head) items: 512-token partitions
+    # for bf16 caches, 1024 for FP8
     assert pkv.decode_partition_size(8, 64, 8, 128, 8, 32768, 1, 1, 0) == 512
-    assert pkv.decode_partition_size(256, 40, 8, 128, 16, 8192, 1, 2, 0) == 1024
+    assert pkv.decode_partition_size(64, 40, 8, 128, 16, 8192, 1, 2, 0) == 1024
     assert pkv.decode_partition_size(256, 40, 8, 128, 16, 900, 1, 2, 0) == 912
+    # 1024 .. 1535 items: whole contexts up to one item's 256-block table
+    assert pkv.decode_partition_size(128, 32, 8, 128, 16, 1536, 1, 1, 0) == 1536
+    assert pkv.decode_partition_size(128, 32, 8, 128, 8, 8192, 1, 1, 0) == 2048
+    # more items: half the longest context, within [default, table]
+    assert pkv.decode_partition_size(64, 32, 32, 128, 16, 2029, 1, 1, 0) == 1024
+    assert pkv.decode_partition_size(256, 40, 8, 128, 16, 8192, 1, 2, 0) == 4096
+    assert pkv.decode_partition_size(256, 40, 8, 128, 16, 1500, 1, 2, 0) == 1024
     assert pkv.decode_workspace_size(4, 8, 8, 128, 16, 300, 1, 1, 0) == 4096
     # long contexts: 512-token partitions, partials for m, l and acc
     assert pkv.decode_partition_size(8, 64, 8, 128, 8, 32768, 1, 1, 512) == 512

@@ -266,3 +266,28 @@ def test_partitions_longer_than_256_blocks(cache, bs, D):
     _say(f"  max_err={err:.3e}")
     assert err <= TOL[cache], err
     assert np.all(out_f64(out)[3] == 0)
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_longest_first_order_with_400_sequences(cache):
+    """400 sequences (the scan sorts sequences 256.. in its second round),
+    many equal lengths and a few empty ones, as whole-context items and as
+    partitions: every sequence is attended exactly once."""
+    rng = np.random.default_rng(63)
+    S = 400
+    lens = rng.choice([1, 16, 17, 200, 333, 700], size=S)
+    lens[[3, 299, 398]] = 0
+    w = workloads.build_workload(f"lpt-{cache}", S, 8, 2, 64, 16, "bf16", cache, lens, 64,
+                                 fill="write" if cache == "fp8" else "random")
+    _say(f"case longest-first S={S} cache={cache}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle_decode(w, kc, vc, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    for ps in (704, 256, 0):
+        out = dw.decode(partition_size=ps)
+        torch.cuda.synchronize()
+        err = max_err(out_f64(out), ref)
+        _say(f"  ps={ps} max_err={err:.3e}")
+        assert err <= TOL[cache], (ps, err)
+        assert np.all(out_f64(out)[np.asarray(lens) == 0] == 0)

@@ -1,0 +1,102 @@
+"""CPU replay of the decode kernel's item order (no GPU).
+
+Every workgroup of the persistent decode kernel sorts the batch's sequences
+by the size of their last partition, largest first (longest processing time
+first), with a stable counting sort that must give the same order in every
+workgroup: thread t holds sequences t and t + 256; key counts per 64-sequence
+chunk give the equal keys in earlier chunks; a ballot within the wave gives
+the rank among equal keys in the wave's own chunk; an exclusive scan over
+keys in decreasing order gives each key's first position.  The replay follows
+those steps and checks that the result is a permutation, in decreasing key
+order with ties by sequence index, for the workloads' length mixes and for
+edge cases (one sequence, 512, all equal, zero lengths).
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+
+NTH, NCH, KEYS = 256, 8, 256
+
+
+def kernel_order(lens, P, bs):
+    S = len(lens)
+    assert S <= 2 * NTH
+    key = np.full(2 * NTH, -1, np.int64)
+    for i in range(S):
+        n = int(lens[i])
+        last = n - ((n - 1) // P) * P if n > 0 else 0
+        key[i] = min((last + bs - 1) // bs, KEYS - 1)
+    cnt = np.zeros((NCH, KEYS), np.int64)
+    for i in range(S):
+        cnt[i >> 6, key[i]] += 1
+    run = np.zeros(KEYS, np.int64)
+    before = np.zeros((NCH, KEYS), np.int64)
+    for k in range(KEYS):
+        acc = 0
+        for c in range(NCH):
+            before[c, k] = acc
+            acc += cnt[c, k]
+        run[k] = acc
+    # thread t owns key KEYS-1-t; exclusive scan over threads
+    first = np.zeros(KEYS, np.int64)
+    acc = 0
+    for t in range(NTH):
+        k = KEYS - 1 - t
+        first[k] = acc
+        acc += run[k]
+    order = np.full(S, -1, np.int64)
+    for c in range(NCH):                   # one wave per chunk and round
+        idx = np.arange(64 * c, 64 * c + 64)
+        valid = idx < S
+        todo = valid.copy()
+        rank = np.zeros(64, np.int64)
+        while todo.any():
+            leader = int(np.flatnonzero(todo)[0])
+            kl = key[idx[leader]]
+            m = valid & (key[idx] == kl)
+            rank[m] = np.cumsum(m)[m] - 1
+            todo &= ~m
+        for lane in np.flatnonzero(valid):
+            i = idx[lane]
+            pos = first[key[i]] + before[c, key[i]] + rank[lane]
+            assert 0 <= pos < S
+            assert order[pos] == -1, "two sequences at one position"
+            order[pos] = i
+    return order, key[:S]
+
+
+def _check(lens, P, bs):
+    order, key = kernel_order(lens, P, bs)
+    assert sorted(order.tolist()) == list(range(len(lens)))
+    ks = key[order]
+    assert np.all(np.diff(ks) <= 0)
+    for k in np.unique(ks):                 # ties keep sequence order
+        same = order[ks == k]
+        assert np.all(np.diff(same) > 0)
+
+
+@pytest.mark.parametrize("cfg,P,bs", [(2, 2032, 16), (2, 512, 16), (4, 1536, 16), (5, 4096, 16),
+                                      (5, 1024, 16), (3, 512, 8)])
+def test_workload_orders(cfg, P, bs):
+    lens = workloads.config_lengths(cfg, np.random.default_rng(1000 + cfg), False)
+    _check(np.asarray(lens), P, bs)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_batches(seed):
+    rng = np.random.default_rng(seed)
+    S = int(rng.integers(1, 513))
+    bs = int(rng.choice([8, 16, 32]))
+    P = bs * int(rng.integers(1, 257))
+    lens = rng.integers(0, 3 * P, size=S)
+    lens[rng.random(S) < 0.1] = 0
+    _check(lens, P, bs)
+
+
+def test_edge_batches():
+    _check(np.array([7]), 16, 16)
+    _check(np.zeros(512, np.int64), 512, 16)          # every key equal (empty contexts)
+    _check(np.full(512, 4096), 4096, 16)               # every key clamped to the top
+    _check(np.arange(512) * 8, 4096, 16)
