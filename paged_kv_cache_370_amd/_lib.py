@@ -396,7 +396,9 @@ def hbm_gather_probe(buf, tiles, tile_bytes, sink, stream=None):
     _contig(buf, tiles)
     if tiles.dtype != torch.int32:
         raise ValueError("tiles must be int32")
-    if tiles.numel() and int(tiles.max()) * tile_bytes + tile_bytes > buf.numel() * buf.element_size():
-        raise ValueError("a tile id lies outside the buffer")
+    if _v.enabled() and tiles.numel():
+        # a device reduction and a host sync: debug mode only
+        if int(tiles.min()) < 0 or (int(tiles.max()) + 1) * tile_bytes > buf.numel() * buf.element_size():
+            raise _v.ContractError("pkv_hbm_gather_probe: a tile id lies outside the buffer")
     _check(load().pkv_hbm_gather_probe(_ptr(buf), _ptr(tiles), tiles.numel(), int(tile_bytes),
                                        _ptr(sink), _stream(stream)), "pkv_hbm_gather_probe")
