@@ -415,29 +415,6 @@ __device__ __forceinline__ void softmax_pv(const f32x4_t (&s)[kNT], const float 
   }
 }
 
-// Exclusive scan over the workgroup of one value per thread; returns the
-// thread's exclusive prefix, and the total in *total.  Every thread calls it.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* s_red, int* total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  __syncthreads();  // s_red may still be read by a previous scan
-  if (lane == 63) s_red[wave] = x;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int w = 0; w < kNW; ++w) {
-    if (w < wave) x += s_red[w];
-    t += s_red[w];
-  }
-  *total = t;
-  return x - v;
-}
-
 // Item order of the sequence scan: first every full partition (P tokens) of
 // every sequence, then every sequence's last, shorter partition (a sequence
 // of length 0 has one empty item, which writes zeros).  Sequences are taken
@@ -463,26 +440,69 @@ constexpr int kSortKeys = 256;
 constexpr int kSeqBits = 9;  // sequence index bits of an s_seq entry
 static_assert((1 << kSeqBits) >= kMaxScanSeqs, "sequence index field");
 
+// Inclusive sum over the 64 lanes of a wave on the DPP network: shifts of
+// 1, 2, 4 and 8 within each 16-lane row (lanes past a row's start add 0),
+// then row 0's and row 1's last lanes broadcast into the rows after them.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Items of one sorted position: its full partitions and its short (or
+// only) one.
+__device__ __forceinline__ void seq_items(int packed, int P, int& nf, int& nr) {
+  const int n = packed >> kSeqBits;
+  nf = n / P;
+  nr = (n % P != 0 || n == 0) ? 1 : 0;
+}
+
+// First phase of the scan: the thread's context lengths are requested
+// (their loads stay in flight) and the LDS counts are cleared.
+constexpr int kScanChunks = kMaxScanSeqs / 64;  // 64-sequence chunks
+template <int MODE>
+__device__ __forceinline__ void scan_begin(const MfmaParams& p, int* s_tmp, int (&len)[2]) {
+  constexpr int NTH = kNW * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = (p.S + 63) >> 6;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = tid + r * NTH;
+    len[r] = i < p.S ? seq_len<MODE>(p, i) : -1;
+  }
+  for (int k = tid; k < nch * kSortKeys; k += NTH) s_tmp[k] = 0;
+  unsigned long long* mask =
+      reinterpret_cast<unsigned long long*>(s_tmp + (kScanChunks + 1) * kSortKeys) +
+      wave * kSortKeys;
+  for (int k = lane; k < kSortKeys; k += 64) mask[k] = 0ull;
+}
+
 template <int MODE, int BS>
 __device__ int build_offsets(const MfmaParams& p, int* s_full, uint16_t* s_rag, int* s_seq,
-                             int* s_red, int* s_tmp, int* n_rag) {
+                             int* s_red, int* s_tmp, const int (&len)[2],
+                             int* n_rag) {
   constexpr int NTH = kNW * 64;
-  constexpr int NCH = kMaxScanSeqs / 64;  // 64-sequence chunks
+  constexpr int NCH = kScanChunks;
   static_assert(kMaxScanSeqs <= 2 * NTH && kSortKeys == NTH, "two sequences, one key per thread");
-  const int tid = threadIdx.x, lane = tid & 63;
-  int* cnt = s_tmp;                     // [NCH][kSortKeys]
-  int* first = s_tmp + NCH * kSortKeys;  // [kSortKeys]: sequences with a larger key
-  for (int k = tid; k < NCH * kSortKeys; k += NTH) cnt[k] = 0;
-  __syncthreads();
-  int key[2], len[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = (p.S + 63) >> 6;       // chunks holding sequences
+  int* cnt = s_tmp;                       // [NCH][kSortKeys]
+  int* first = s_tmp + NCH * kSortKeys;   // [kSortKeys]: sequences with a larger key
+  // [kNW][kSortKeys] 64-bit lane masks: the lanes of a wave's chunk holding each key
+  unsigned long long* mask =
+      reinterpret_cast<unsigned long long*>(s_tmp + (NCH + 1) * kSortKeys) + wave * kSortKeys;
+  __syncthreads();  // the counts cleared by scan_begin
+  int key[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int i = tid + r * NTH;
     key[r] = -1;
-    len[r] = 0;
-    if (i < p.S) {
-      const int n = seq_len<MODE>(p, i);
-      len[r] = n;
+    if (len[r] >= 0) {
+      const int n = len[r];
       const int last = n > 0 ? n - ((n - 1) / p.P) * p.P : 0;  // tokens of the last partition
       key[r] = min((last + BS - 1) / BS, kSortKeys - 1);
       atomicAdd(&cnt[(i >> 6) * kSortKeys + key[r]], 1);
@@ -490,59 +510,83 @@ __device__ int build_offsets(const MfmaParams& p, int* s_full, uint16_t* s_rag, 
   }
   __syncthreads();
   {
-    // thread t owns key kSortKeys - 1 - t: the scan over threads then runs
-    // over keys in decreasing order
+    // thread t owns key kSortKeys - 1 - t: a scan over threads then runs over
+    // keys in decreasing order
     const int k = kSortKeys - 1 - tid;
     int run = 0;
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = 0; c < nch; ++c) {
       const int v = cnt[c * kSortKeys + k];
       cnt[c * kSortKeys + k] = run;  // equal keys in earlier chunks
       run += v;
     }
-    int total;
-    first[k] = block_exclusive_scan(run, s_red, &total);  // has barriers
+    const int incl = wave_inclusive_sum(run);
+    if (lane == 63) s_red[wave] = incl;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) before += w < wave ? s_red[w] : 0;
+    first[k] = before + incl - run;
   }
   __syncthreads();
+  // Rank among equal keys within the wave's chunk: the key's lane mask (an
+  // OR, so the result does not depend on the order of the atomics), counted
+  // below the lane.
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int i = tid + r * NTH;
     const bool valid = key[r] >= 0;
-    unsigned long long todo = __ballot(valid);
-    int rank = 0;
-    while (todo) {  // uniform: one round per distinct key in the wave
-      const int leader = __builtin_ffsll((long long)todo) - 1;
-      const int kl = __builtin_amdgcn_readlane(key[r], leader);
-      const unsigned long long m = __ballot(valid && key[r] == kl);
-      if (valid && key[r] == kl) rank = __builtin_popcountll(m & ((1ull << lane) - 1ull));
-      todo &= ~m;
-    }
-    if (valid)
+    if (r == 1 && p.S <= NTH) break;  // uniform: no second round
+    if (valid) atomicOr(&mask[key[r]], 1ull << lane);
+    wave_lds_sync();
+    if (valid) {
+      const int rank = __builtin_popcountll(mask[key[r]] & ((1ull << lane) - 1ull));
       s_seq[first[key[r]] + cnt[(i >> 6) * kSortKeys + key[r]] + rank] = (len[r] << kSeqBits) | i;
+    }
+    wave_lds_sync();
+    if (valid) mask[key[r]] = 0ull;  // ready for the wave's second chunk
+    wave_lds_sync();
   }
   __syncthreads();
 
+  // Full and short partitions before each sorted position: one pass of two
+  // wave sums, one barrier.
   const int per = (p.S + NTH - 1) / NTH;
   const int base = tid * per;
   int nf = 0, nr = 0;
   for (int k = 0; k < per; ++k) {
     const int pos = base + k;
     if (pos < p.S) {
-      const int n = s_seq[pos] >> kSeqBits;
-      nf += n / p.P;
-      nr += (n % p.P != 0 || n == 0) ? 1 : 0;
+      int f, r;
+      seq_items(s_seq[pos], p.P, f, r);
+      nf += f;
+      nr += r;
     }
   }
-  int F, R;
-  int ef = block_exclusive_scan(nf, s_red, &F);
-  int er = block_exclusive_scan(nr, s_red, &R);
+  const int incf = wave_inclusive_sum(nf);
+  const int incr = wave_inclusive_sum(nr);
+  if (lane == 63) {
+    s_red[kNW + wave] = incf;
+    s_red[2 * kNW + wave] = incr;
+  }
+  __syncthreads();
+  int ef = incf - nf, er = incr - nr, F = 0, R = 0;
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) {
+    const int fw = s_red[kNW + w], rw = s_red[2 * kNW + w];
+    ef += w < wave ? fw : 0;
+    er += w < wave ? rw : 0;
+    F += fw;
+    R += rw;
+  }
   for (int k = 0; k < per; ++k) {
     const int pos = base + k;
     if (pos < p.S) {
-      const int n = s_seq[pos] >> kSeqBits;
+      int f, r;
+      seq_items(s_seq[pos], p.P, f, r);
       s_full[pos] = ef;
       s_rag[pos] = (uint16_t)er;
-      ef += n / p.P;
-      er += (n % p.P != 0 || n == 0) ? 1 : 0;
+      ef += f;
+      er += r;
     }
   }
   if (tid == 0) {
@@ -682,13 +726,14 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   __shared__ uint4 s_qf[2][Gm::NKC * 64];
   __shared__ float s_m[kNW][16];
   __shared__ float s_l[kNW][16];
-  __shared__ int s_red[kNW];
+  __shared__ int s_red[3 * kNW];
   __shared__ int s_next[3];  // next claimed item, second static item, queue flag
   __shared__ int s_zero[4];  // block id 0 for the dummy row
   __shared__ int s_full[SCAN ? kMaxScanSeqs + 1 : 1];
   __shared__ uint16_t s_rag[SCAN ? kMaxScanSeqs + 1 : 1];
   __shared__ int s_seq[SCAN ? kMaxScanSeqs : 1];
-  static_assert(UNION_BYTES >= (kMaxScanSeqs / 64 + 1) * kSortKeys * 4, "sort scratch");
+  static_assert(UNION_BYTES >= (kMaxScanSeqs / 64 + 1) * kSortKeys * 4 + kNW * kSortKeys * 8,
+                "sort scratch");
   const Order order{s_full, s_rag, s_seq};
 
   const int tid = threadIdx.x;
@@ -717,12 +762,14 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     s_next[1] = (queue_wgs + (int)blockIdx.x / nq) * nq + queue;
   }
   if (tid < 4) s_zero[tid] = 0;
+  int len[2] = {-1, -1};
+  if constexpr (SCAN) scan_begin<MODE>(p, reinterpret_cast<int*>(s_raw), len);
   int total, n_full = 0;
   if constexpr (SCAN) {
     int n_rag;
     // has barriers; s_raw is free until the first chunk
     n_full = build_offsets<MODE, BS>(p, s_full, s_rag, s_seq, s_red,
-                                     reinterpret_cast<int*>(s_raw), &n_rag);
+                                     reinterpret_cast<int*>(s_raw), len, &n_rag);
     total = Y * (n_full + n_rag);
   } else {
     total = Y * p.S * p.NP;
@@ -756,9 +803,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   }
   __syncthreads();
 
-  const Src cache{p.kc, p.vc, p.ks, p.vs};
   const Src dummy{g_dummy_row, g_dummy_row, reinterpret_cast<const float*>(g_dummy_row),
                   reinterpret_cast<const float*>(g_dummy_row)};
+  const Src cache{p.kc, p.vc, p.ks, p.vs};
   Part dummy_part{};  // token 0 of block 0, KV head 0: row 0 of the dummy
   dummy_part.end = 1;
 

@@ -100,3 +100,62 @@ def test_edge_batches():
     _check(np.zeros(512, np.int64), 512, 16)          # every key equal (empty contexts)
     _check(np.full(512, 4096), 4096, 16)               # every key clamped to the top
     _check(np.arange(512) * 8, 4096, 16)
+
+
+
+def kernel_items(lens, P, bs, Y):
+    """Every item the kernel enumerates, as (sequence, row group, partition):
+    the sorted order's full partitions, then its last partitions, decoded the
+    way the kernel decodes an item index (item % Y is the row group)."""
+    S = len(lens)
+    order, _ = kernel_order(lens, P, bs)
+    nf, nr = [], []
+    for pos in range(S):
+        n = int(lens[int(order[pos])])
+        nf.append(n // P)
+        nr.append(1 if (n % P != 0 or n == 0) else 0)
+    full = np.concatenate([[0], np.cumsum(nf)])
+    rag = np.concatenate([[0], np.cumsum(nr)])
+    F, R = int(full[-1]), int(rag[-1])
+    items = []
+    for item in range(Y * (F + R)):
+        y, rest = item % Y, item // Y
+        if rest < F:
+            pos = int(np.searchsorted(full, rest, side="right") - 1)
+            seq = int(order[pos])
+            part = rest - int(full[pos])
+        else:
+            pos = int(np.searchsorted(rag, rest - F, side="right") - 1)
+            seq = int(order[pos])
+            part = int(lens[seq]) // P
+        items.append((seq, y, part))
+    return items
+
+
+def _expected_items(lens, P, Y):
+    return {(i, y, p) for i in range(len(lens)) for y in range(Y)
+            for p in range(max(1, -(-int(lens[i]) // P)))}
+
+
+@pytest.mark.parametrize("cfg,P,bs,Y", [(2, 1024, 16, 32), (3, 512, 8, 8), (4, 1536, 16, 8),
+                                        (5, 4096, 16, 8)])
+def test_every_item_exactly_once(cfg, P, bs, Y):
+    lens = np.asarray(workloads.config_lengths(cfg, np.random.default_rng(1000 + cfg), False))
+    items = kernel_items(lens, P, bs, Y)
+    assert len(items) == len(set(items))
+    assert set(items) == _expected_items(lens, P, Y)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_every_item_exactly_once_random(seed):
+    rng = np.random.default_rng(40 + seed)
+    S = int(rng.integers(1, 300))
+    bs = int(rng.choice([8, 16, 32]))
+    P = bs * int(rng.integers(1, 20))
+    lens = rng.integers(0, 4 * P, size=S)
+    lens[rng.random(S) < 0.2] = 0
+    lens[rng.random(S) < 0.2] = P
+    Y = int(rng.choice([1, 3, 8, 32]))
+    items = kernel_items(lens, P, bs, Y)
+    assert len(items) == len(set(items))
+    assert set(items) == _expected_items(lens, P, Y)
