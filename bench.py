@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7b-decode-bf16]
 
 A step is the whole hot path over one batch: paged_kv_cache_write of each
-sequence's newest token, then paged_attention_decode (the partition kernel and
-the split reduce).  Inputs are seeded synthetic tensors already resident in
+sequence's newest token, then paged_attention_decode (one launch when every
+context spans at most 4 partitions: the decode kernel merges the partials
+itself; otherwise the partition kernel and the split reduce).  Inputs are seeded synthetic tensors already resident in
 HBM.  Every GPU figure is a per-iteration HIP-event time with the MALL (256 MB)
 and L2s flushed before the iteration by writing a 512 MiB buffer outside the
 events; the median (with p10/p90) over K iterations is reported, and
@@ -12,8 +13,9 @@ back-to-back warm times beside it.
 
   value        algorithmic KV bytes the decode reads per step / median step
                time (GB/s) on the headline workload;
-  roofline     the partition kernel's algorithmic bytes over its mean flushed
-               launch time, against the 8 TB/s HBM peak;
+  roofline     the decode kernel's algorithmic bytes over its launch time
+               (launches back to back, as rocprofv3 reports them), against the
+               8 TB/s HBM peak;
   workloads    the 32K-context, shared-prefix and FP8 workloads measured the
                same way, each with its own roofline;
   ceiling_gbs  a streaming read of 1 GiB (and a 4 KiB-tile gather) by the
@@ -298,9 +300,10 @@ def to_device(torch, a):
 
 def measure_decode(pkv, torch, timer, w, ps, steps, warmup, traffic_key):
     """One decode workload on the GPU: the step (write of the step's tokens +
-    paged_attention_decode), the decode call alone and its partition kernel
-    alone, each with flushed per-iteration events; roofline of the partition
-    kernel on the workload's algorithmic bytes."""
+    paged_attention_decode) and the decode call alone, and when the call is
+    two launches its partition kernel alone, each with flushed per-iteration
+    events; roofline of the decode kernel on the workload's algorithmic
+    bytes."""
     t = lambda a: to_device(torch, a)
     total_bytes, nblocks = kv_bytes(w)
     q = t(w.q)
@@ -313,6 +316,11 @@ def measure_decode(pkv, torch, timer, w, ps, steps, warmup, traffic_key):
     qc, cc = pkv.dtype_code(q), pkv.dtype_code(kc)
     P = pkv.decode_partition_size(w.S, w.H, w.H_kv, w.D, w.block_size, w.max_context_len, qc,
                                   cc, ps)
+    NP = -(-w.max_context_len // P)
+    # paged_attention_decode is one launch when no context needs a merge, or
+    # when the matrix-core kernel merges them itself (bf16 queries, 2 to 4
+    # partitions per context, partitions of at most 256 blocks)
+    one_launch = NP == 1 or (qc == pkv.PKV_BF16 and NP <= 4 and P // w.block_size <= 256)
     ws_bytes = pkv.decode_workspace_size(w.S, w.H, w.H_kv, w.D, w.block_size,
                                          w.max_context_len, qc, cc, ps)
     dws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")  # counters start at 0
@@ -323,6 +331,7 @@ def measure_decode(pkv, torch, timer, w, ps, steps, warmup, traffic_key):
            "head_size": w.D, "block_size": w.block_size, "cache": w.cache_dtype,
            "max_context": w.max_context_len,
            "mean_context": round(float(np.mean(w.context_lens)), 1), "partition_size": P,
+           "partitions": NP, "decode_launches": 1 if one_launch else 2,
            "kv_bytes_per_step": total_bytes, "kv_blocks_read": nblocks}
 
     # Setup writes (the FP8 bulk write of positions 0..n-2) are not part of a
@@ -357,8 +366,8 @@ def measure_decode(pkv, torch, timer, w, ps, steps, warmup, traffic_key):
                                           partition_size=ps, workspace=dws)
 
     def decode():
-        partitions()
-        reduce()
+        pkv.paged_attention_decode(out, q, kc, vc, tables, lens, w.max_context_len, w.scale, ks,
+                                   vs, partition_size=ps, workspace=dws)
 
     def step():
         write()
@@ -368,18 +377,25 @@ def measure_decode(pkv, torch, timer, w, ps, steps, warmup, traffic_key):
         step()
     step_ms = timer.flushed(step, steps)
     decode_ms = timer.flushed(decode, steps, before=write)
-    part_ms = timer.flushed(partitions, steps, before=write)
     warm = {"step": round(timer.warm(step, steps), 5),
-            "decode_partitions": round(timer.warm(partitions, steps), 5),
-            "decode_reduce": round(timer.warm(reduce, steps), 5),
+            "decode": round(timer.warm(decode, steps), 5),
             "write": round(timer.warm(write, steps), 5)}
-    st, dc, pt = stats(step_ms), stats(decode_ms), stats(part_ms)
+    st, dc = stats(step_ms), stats(decode_ms)
+    flushed = {"step": st, "decode": dc}
+    if one_launch:
+        kernel_ms, kernel_flushed = warm["decode"], dc
+    else:
+        pt = stats(timer.flushed(partitions, steps, before=write))
+        warm["decode_partitions"] = round(timer.warm(partitions, steps), 5)
+        warm["decode_reduce"] = round(timer.warm(reduce, steps), 5)
+        flushed["decode_partitions"] = pt
+        kernel_ms, kernel_flushed = warm["decode_partitions"], pt
     res.update({
         "ms_per_step": st["median"],
         "GB_per_s": round(total_bytes / (st["median"] * 1e-3) / 1e9, 2),
         "pct_hbm_peak": round(100.0 * total_bytes / (st["median"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(w.S * w.H / (st["median"] * 1e-3), 1),
-        "flushed_ms": {"step": st, "decode": dc, "decode_partitions": pt},
+        "flushed_ms": flushed,
         "decode_GB_per_s": round(total_bytes / (dc["median"] * 1e-3) / 1e9, 2),
         "decode_pct_hbm_peak": round(100.0 * total_bytes / (dc["median"] * 1e-3) / 1e9
                                      / HBM_PEAK_GBS, 2),
@@ -390,15 +406,16 @@ def measure_decode(pkv, torch, timer, w, ps, steps, warmup, traffic_key):
     # single flushed launch adds its marker packets (a few us) to the kernel.
     # Flushing does not change the kernel's time (the 256 MB MALL cannot hold
     # a ~1 GB working set), so the two differ by the event packets only.
-    kernel_ms = warm["decode_partitions"]
     achieved = total_bytes / (kernel_ms * 1e-3) / 1e9
     res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                        "traffic": recorded_traffic(traffic_key),
-                       "kernel": "decode partition kernel",
+                       "kernel": ("decode kernel (partials merged in the kernel)"
+                                  if one_launch and NP > 1 else
+                                  "decode kernel" if one_launch else "decode partition kernel"),
                        "kernel_us": round(kernel_ms * 1e3, 2),
-                       "flushed_event_us": {"mean": round(pt["mean"] * 1e3, 2),
-                                            "median": round(pt["median"] * 1e3, 2)},
+                       "flushed_event_us": {"mean": round(kernel_flushed["mean"] * 1e3, 2),
+                                            "median": round(kernel_flushed["median"] * 1e3, 2)},
                        "kernel_sources": kernel_source_hash()}
     if w.shared_blocks > 0:
         res["read_once"] = read_once_bench(pkv, torch, timer, w, out, q, kc, vc, ks, vs, tables,

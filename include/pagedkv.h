@@ -132,18 +132,24 @@ size_t paged_kv_cache_write_workspace_size(
  *   likewise); scales are ignored otherwise (may be NULL).
  *   max_context_len must be >= every context_lens[i]; it sizes the grid so
  *   the host never reads device memory.
- *   partition_size (tokens, multiple of bs, or 0 = library choice: the
- *   whole context up to 512 tokens, 1024 for FP8 caches, else partitions of
- *   that size): contexts longer than one partition are split, each partition is attended on its
- *   own, and a second kernel merges the partial results (each partition's
- *   running maximum and sum in float32, its unnormalised output in float32
- *   for F32 queries and in bf16 for BF16 queries, whose output is bf16).
+ *   partition_size (tokens, multiple of bs, or 0 = library choice, which
+ *   paged_attention_decode_partition_size reports; it depends on the batch
+ *   shape and the longest context, never on the lengths themselves):
+ *   contexts longer than one partition are split, each partition is
+ *   attended on its own, and the partial results are merged (each
+ *   partition's running maximum and sum in float32, its unnormalised output
+ *   in float32 for F32 queries and in bf16 for BF16 queries, whose output is
+ *   bf16).  With BF16 queries and at most 4 partitions per context the
+ *   decode kernel merges them itself (the last partition of a sequence's
+ *   head group to finish does it); otherwise a second kernel merges them.
  *   workspace: at least paged_attention_decode_workspace_size(...) bytes
- *   (always >= 4096).  Its first 4096 bytes are work-queue counters: they
- *   must be zero before the first call that uses the workspace (allocate it
- *   zero-filled) and every call leaves them zero again; the rest may hold
- *   anything.  Calls that may run at the same time must not share a
- *   workspace.
+ *   (always >= 4096).  Its first paged_attention_decode_workspace_counter_bytes(...)
+ *   bytes are counters (the 4096-byte work-queue header, then, when a
+ *   context can span two partitions, num_seqs * num_heads int32 partition
+ *   arrival counters rounded up to 256 bytes): they must be zero before
+ *   the first call that uses the workspace (allocate it zero-filled) and
+ *   every call leaves them zero again; the rest may hold anything.  Calls
+ *   that may run at the same time must not share a workspace.
  *   num_seqs == 0 returns PKV_OK after the size and dtype checks without
  *   inspecting any pointer.
  */
@@ -170,6 +176,13 @@ int32_t paged_attention_decode_partition_size(
 
 /* Workspace bytes paged_attention_decode needs for these arguments. */
 size_t paged_attention_decode_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_context_len,
+    int32_t q_dtype, int32_t cache_dtype, int32_t partition_size);
+
+/* Leading workspace bytes of paged_attention_decode that hold counters and
+ * must be zero at the call (0 on invalid arguments). */
+size_t paged_attention_decode_workspace_counter_bytes(
     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
     int32_t head_size, int32_t block_size, int32_t max_context_len,
     int32_t q_dtype, int32_t cache_dtype, int32_t partition_size);
@@ -335,8 +348,9 @@ pkv_status_t paged_kv_block_copy(
  * arguments, partition choice and result as paged_attention_decode; the
  * workspace is instead a device array inside the library, one per device,
  * of PKV_DECODE_NOALLOC_MAX_WORKSPACE bytes, held until the process ends.
- * The call allocates nothing: it zeroes the array's 4 KiB counter header with
- * a small kernel on `stream`, then runs the decode in it.
+ * The call allocates nothing: it zeroes the array's counters (the leading
+ * paged_attention_decode_workspace_counter_bytes(...)) with a small kernel
+ * on `stream`, then runs the decode in it.
  *   A call whose paged_attention_decode_workspace_size(...) exceeds
  *   PKV_DECODE_NOALLOC_MAX_WORKSPACE returns PKV_ERR_WORKSPACE and enqueues
  *   nothing.  Other checks and errors are paged_attention_decode's.

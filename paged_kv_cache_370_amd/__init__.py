@@ -15,6 +15,7 @@ from ._lib import (
     PagedKVError,
     decode_partition_size,
     decode_workspace_size,
+    decode_workspace_counter_bytes,
     dtype_code,
     hbm_gather_probe,
     hbm_read_probe,
@@ -37,7 +38,7 @@ from .block_manager import BlockManager, OutOfBlocks
 
 __all__ = [
     "ContractError", "PKV_BF16", "PKV_F32", "PKV_FP8_E4M3", "PagedKVError", "BlockManager", "OutOfBlocks",
-    "decode_partition_size", "decode_workspace_size", "dtype_code", "hbm_gather_probe",
+    "decode_partition_size", "decode_workspace_size", "decode_workspace_counter_bytes", "dtype_code", "hbm_gather_probe",
     "hbm_read_probe", "load",
     "decode_noalloc_max_workspace", "paged_attention_decode",
     "paged_attention_decode_noalloc", "paged_attention_decode_partitions",

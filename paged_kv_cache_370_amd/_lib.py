@@ -26,6 +26,7 @@ EXPORTS = (
     "paged_attention_decode",
     "paged_attention_decode_partition_size",
     "paged_attention_decode_workspace_size",
+    "paged_attention_decode_workspace_counter_bytes",
     "paged_attention_decode_partitions",
     "paged_attention_decode_reduce",
     "paged_kv_block_copy",
@@ -84,6 +85,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode_partition_size.argtypes = geo
     lib.paged_attention_decode_workspace_size.restype = sz
     lib.paged_attention_decode_workspace_size.argtypes = geo
+    lib.paged_attention_decode_workspace_counter_bytes.restype = sz
+    lib.paged_attention_decode_workspace_counter_bytes.argtypes = geo
     lib.paged_attention_prefill.restype = i32
     lib.paged_attention_prefill.argtypes = ([vp] * 8 + [i32] * 8 + [fp] + [i32] * 3
                                             + [vp, sz, vp])
@@ -186,6 +189,14 @@ def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_size, block_si
         c_code, partition_size))
 
 
+def decode_workspace_counter_bytes(num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                                   max_context_len, q_code, c_code, partition_size=0) -> int:
+    """Leading workspace bytes that hold counters and must be zero at a call."""
+    return int(load().paged_attention_decode_workspace_counter_bytes(
+        num_seqs, num_heads, num_kv_heads, head_size, block_size, max_context_len, q_code,
+        c_code, partition_size))
+
+
 def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
                  max_context_len, scale, key_scale, value_scale, partition_size, workspace,
                  stream):
@@ -193,13 +204,16 @@ def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
             value_scale)
     S, H, D = query.shape
     num_blocks, H_kv, bs, _ = key_cache.shape
+    qc, cc = dtype_code(query), dtype_code(key_cache)
     if _v.enabled():
         _v.check_decode("paged_attention_decode", context_lens, block_tables, num_blocks, bs,
                         max_context_len)
-        _v.check_workspace_header("paged_attention_decode", workspace)
-    qc, cc = dtype_code(query), dtype_code(key_cache)
+        _v.check_workspace_header(
+            "paged_attention_decode", workspace,
+            decode_workspace_counter_bytes(S, H, H_kv, D, bs, max_context_len, qc, cc,
+                                           partition_size))
     if workspace is None:
-        # zero-filled: the first 4 KiB are the library's work-queue counters
+        # zero-filled: the leading bytes are the library's counters
         need = decode_workspace_size(S, H, H_kv, D, bs, max_context_len, qc, cc, partition_size)
         workspace = torch.zeros(need, dtype=torch.uint8, device=query.device) if need else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

@@ -18,7 +18,8 @@ violation before anything is enqueued:
   * shared-prefix calls: every table begins with the same prefix blocks;
   * block copies: ids inside their pools, distinct destinations, and no
     destination that is also a source when both pools are one;
-  * workspaces handed in by the caller: the 4 KiB work-queue header is zero.
+  * workspaces handed in by the caller: the leading counters (the 4 KiB
+    work-queue header and the partition arrival counters) are zero.
 """
 
 import os
@@ -135,17 +136,23 @@ def check_block_pairs(where, block_pairs, src_blocks, dst_blocks, same_pool):
                                 f"destination within one pool")
 
 
-def check_workspace_header(where, workspace):
-    """The work-queue counters a persistent launch claims items from must start
-    at zero; a non-zero header would make the launch skip items."""
+def check_workspace_header(where, workspace, counter_bytes=SCHED_BYTES):
+    """The counters at the front of a decode workspace must start at zero: the
+    work-queue counters a persistent launch claims items from (non-zero, the
+    launch would skip items) and the partition arrival counters of the fused
+    merge (non-zero, a row group would be merged before all its partitions
+    arrived, or never)."""
     if workspace is None:
         return
+    n = max(int(counter_bytes), SCHED_BYTES)
     if isinstance(workspace, np.ndarray):
-        head = workspace.reshape(-1).view(np.uint8)[:SCHED_BYTES]
+        head = workspace.reshape(-1).view(np.uint8)[:n]
     else:
         import torch
-        head = workspace.reshape(-1).view(torch.uint8)[:SCHED_BYTES].cpu().numpy()
+        head = workspace.reshape(-1).view(torch.uint8)[:n].cpu().numpy()
     if np.any(head != 0):
-        raise ContractError(f"{where}: the workspace's first {SCHED_BYTES} bytes (work-queue "
-                            f"counters) are not zero: allocate it zero-filled and do not share "
-                            f"it between calls that may overlap")
+        i = _first(head != 0)
+        what = "work-queue counters" if i < SCHED_BYTES else "partition arrival counters"
+        raise ContractError(f"{where}: byte {i} of the workspace's first {n} bytes ({what}) "
+                            f"is not zero: allocate it zero-filled and do not share it between "
+                            f"calls that may overlap")

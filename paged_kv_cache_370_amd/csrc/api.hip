@@ -78,16 +78,24 @@ pkv_status_t check_decode_shape(int S, int H, int H_kv, int D, int bs, int max_c
 }
 
 // Workspace: a 4 KiB header of work-queue counters (10 counters, 256 bytes
-// apart), then the split partials (m, l, acc) when a context can span more
-// than one partition.
+// apart), then, when a context can span more than one partition, the
+// partition arrival counters of one-token decode (one per sequence and row
+// group, at most S x H) and the split partials (m, l, acc).  The counters
+// are zero between calls: each call returns them to zero.
 constexpr size_t kSchedBytes = 4096;
+
+// Row groups per sequence (H_kv x 16-row chunks) never exceed H.
+size_t arrival_bytes(int S, int H, int M) {
+  return M == 1 ? align256((size_t)S * H * sizeof(int)) : 0;
+}
 
 // rows of partials: S sequences x M query tokens x H heads x partitions
 size_t decode_workspace(int S, int H, int D, int max_ctx, int P, int M = 1) {
   const int np = num_partitions(max_ctx, P);
   if (np <= 1) return kSchedBytes;
   const size_t rows = (size_t)S * M * H * np;
-  return kSchedBytes + 2 * align256(rows * sizeof(float)) + align256(rows * D * sizeof(float));
+  return kSchedBytes + arrival_bytes(S, H, M) + 2 * align256(rows * sizeof(float)) +
+         align256(rows * D * sizeof(float));
 }
 
 struct DecodeSetup {
@@ -158,7 +166,8 @@ DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
     a.sched = reinterpret_cast<int*>(ws);
     if (a.NP > 1) {
       const size_t rows = (size_t)S * M * H * a.NP;
-      char* part = ws + kSchedBytes;
+      if (M == 1) a.arrivals = reinterpret_cast<int*>(ws + kSchedBytes);
+      char* part = ws + kSchedBytes + arrival_bytes(S, H, M);
       a.ws_m = reinterpret_cast<float*>(part);
       a.ws_l = reinterpret_cast<float*>(part + align256(rows * sizeof(float)));
       a.ws_acc = reinterpret_cast<float*>(part + 2 * align256(rows * sizeof(float)));
@@ -251,6 +260,21 @@ pkv_status_t paged_kv_block_copy(const void* src_key_cache, const void* src_valu
   return hip_status(launch_kv_block_copy(a));
 }
 
+size_t paged_attention_decode_workspace_counter_bytes(int32_t num_seqs, int32_t num_heads,
+                                                     int32_t num_kv_heads, int32_t head_size,
+                                                     int32_t block_size, int32_t max_context_len,
+                                                     int32_t q_dtype, int32_t cache_dtype,
+                                                     int32_t partition_size) {
+  if (check_decode_shape(num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                         max_context_len, q_dtype, cache_dtype) != PKV_OK)
+    return 0;
+  const int P = resolve_partition(block_size, max_context_len, partition_size, cache_dtype,
+                                  context_items(num_seqs, num_heads, num_kv_heads));
+  if (P <= 0) return 0;
+  if (num_partitions(max_context_len, P) <= 1) return kSchedBytes;
+  return kSchedBytes + arrival_bytes(num_seqs, num_heads, 1);
+}
+
 int32_t paged_attention_decode_partition_size(int32_t num_seqs, int32_t num_heads,
                                               int32_t num_kv_heads, int32_t head_size,
                                               int32_t block_size, int32_t max_context_len,
@@ -316,16 +340,24 @@ pkv_status_t paged_attention_decode(void* out, const void* query, const void* ke
                                     int32_t max_context_len, float scale, int32_t q_dtype,
                                     int32_t cache_dtype, int32_t partition_size,
                                     void* workspace, size_t workspace_bytes, void* stream) {
-  pkv_status_t st = paged_attention_decode_partitions(
-      out, query, key_cache, value_cache, key_scale, value_scale, block_tables, context_lens,
-      num_seqs, num_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
-      max_context_len, scale, q_dtype, cache_dtype, partition_size, workspace, workspace_bytes,
-      stream);
-  if (st != PKV_OK) return st;
-  return paged_attention_decode_reduce(out, context_lens, num_seqs, num_heads, num_kv_heads,
-                                       head_size, block_size, max_context_len, q_dtype,
-                                       cache_dtype, partition_size, workspace, workspace_bytes,
-                                       stream);
+  DecodeSetup s = setup_decode(out, query, key_cache, value_cache, key_scale, value_scale,
+                               block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                               head_size, block_size, max_blocks_per_seq, max_context_len, scale,
+                               q_dtype, cache_dtype, partition_size, workspace, workspace_bytes,
+                               stream, true);
+  if (s.status != PKV_OK || s.empty) return s.status;
+  // Up to kFusedMaxPartitions partitions per context, the matrix-core
+  // kernel merges the partials itself (the last partition of a row group
+  // to arrive merges them): one launch.
+  if (decode_mfma_supported(s.a) && s.a.NP > 1 && s.a.NP <= kFusedMaxPartitions &&
+      s.a.arrivals) {
+    s.a.fused = true;
+    return hip_status(launch_decode_mfma(s.a));
+  }
+  pkv_status_t st = hip_status(decode_mfma_supported(s.a) ? launch_decode_mfma(s.a)
+                                                          : launch_decode_valu(s.a));
+  if (st != PKV_OK || s.a.NP <= 1) return st;
+  return hip_status(launch_decode_reduce(s.a));
 }
 
 // Shared-prefix decode: the prefix's partials (ceil(prefix / P) slots) come

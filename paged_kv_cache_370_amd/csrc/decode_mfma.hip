@@ -95,6 +95,8 @@ struct MfmaParams {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
+  int* arrivals;  // [S][Y] arrivals of a row group's partitions (fused merge)
+  int fused;      // the last partition of a row group to arrive merges its partials
   int* sched;  // claim counter of queue x at [x * kCounterStride], of the shared
                // queue at [8 * kCounterStride], finished-workgroup counter at
                // [9 * kCounterStride]
@@ -710,6 +712,82 @@ __device__ __forceinline__ void store_q(uint4 v, const Part& w, uint4* qf, int t
   }
 }
 
+// Fused merge of split partitions (one query token per sequence, at most
+// kFusedMaxPartitions partitions per context).  Each partition item leaves
+// (m_p, l_p, acc_p) for its rows; one softmax over the whole context is
+//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p
+// (dpshk.com PagedAttention article, section 2.2), the reduce kernel's
+// arithmetic in the same order.  No workgroup waits for another: the
+// partials are stored at agent scope (coherent across the XCDs' L2s), and
+// each wave, once those stores are complete, counts itself into the row
+// group's arrival counter with one atomic.  That happens at the wave's last
+// chunk step of its next item, after a wait for everything the wave has in
+// flight (at that point only the K rows of the step it is about to compute,
+// so the wait costs little); the atomic's result is read after the next
+// item's barrier X.  The wave that brings the count to 4 x (partitions)
+// is the last: its workgroup merges the group (agent-scope loads) and
+// returns the counter to zero.
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt not waited for
+
+__device__ __forceinline__ void wait_stores_complete() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no compiler motion of memory accesses across
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ int arrive(const MfmaParams& p, int group) {
+  return __hip_atomic_fetch_add(p.arrivals + group, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D, int MODE>
+__device__ __forceinline__ void merge_group(const MfmaParams& p, int group, int np) {
+  const int Y = p.H_kv * p.chunks;
+  Part w{};
+  w.seq = group / Y;
+  const int y = group - w.seq * Y;
+  w.kvh = y / p.chunks;
+  w.r0 = (y - w.kvh * p.chunks) * 16;
+  w.nh = min(16, p.M * p.G - w.r0);
+  // Thread t merges 4 consecutive d of one row, as the epilogue writes them.
+  for (int idx = (int)threadIdx.x * 4; idx < w.nh * D; idx += kNW * 64 * 4) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    const size_t row = row_of<MODE>(p, w, w.r0 + g);
+    float pm[kFusedMaxPartitions], pl[kFusedMaxPartitions];
+    unsigned long long pa[kFusedMaxPartitions];
+#pragma unroll
+    for (int u = 0; u < kFusedMaxPartitions; ++u) {
+      const size_t pi = row * p.NP + min(u, np - 1);
+      pa[u] = __hip_atomic_load(reinterpret_cast<unsigned long long*>(
+                                    reinterpret_cast<uint16_t*>(p.ws_acc) + pi * D + d),
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pm[u] = __hip_atomic_load(p.ws_m + pi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pl[u] = __hip_atomic_load(p.ws_l + pi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float M = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kFusedMaxPartitions; ++u)
+      if (u < np) M = fmaxf(M, pm[u]);
+    float L = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kFusedMaxPartitions; ++u) {
+      if (u < np) {
+        const float wt = __builtin_amdgcn_exp2f(pm[u] - M);
+        L = fmaf(pl[u], wt, L);
+        const uint32_t lo = (uint32_t)pa[u], hi = (uint32_t)(pa[u] >> 32);
+        O[0] = fmaf(bf16_lo(lo), wt, O[0]);
+        O[1] = fmaf(bf16_hi(lo), wt, O[1]);
+        O[2] = fmaf(bf16_lo(hi), wt, O[2]);
+        O[3] = fmaf(bf16_hi(hi), wt, O[3]);
+      }
+    }
+    const bool ok = L > 0.f;
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * D + d) =
+        make_uint2(pack_bf16x2(ok ? O[0] / L : 0.f, ok ? O[1] / L : 0.f),
+                   pack_bf16x2(ok ? O[2] / L : 0.f, ok ? O[3] / L : 0.f));
+  }
+}
+
 template <typename CT, int D, int BS, bool SCAN, int MODE>
 __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   using Gm = Geometry<CT, D>;
@@ -817,6 +895,11 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   // left uninitialised (0 * NaN = NaN).
 #pragma unroll
   for (int T = 0; T < kNT; ++T) ks.ksc[T] = ks.vsc[T] = 0.f;
+  // Fused merge: the row group (sequence x Y + y) of the previous item,
+  // whose partials this workgroup stored and has not yet counted in (-1:
+  // none), and the group's partition count.  Uniform.
+  int pg = -1, pnp = 0;
+  const bool fused = MODE == kModeDecode && p.fused != 0;
   // First chunk of the first item.
   if (cur < total && it.live) {
     const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
@@ -840,6 +923,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     // (Only thread 0 sets and reads it: initialising it in the other lanes
     // would make the compiler wait for every pending load first.)
     int claim;
+    // The wave's arrival count for group pg (lane 0 only, likewise).
+    int arr;
 
     f32x4_t acc[Gm::NMD];
 #pragma unroll
@@ -878,6 +963,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     do {
       const int c0 = it.w.start + ci * Gm::CHUNK;
       const bool last = ci + kNW >= nvalid;
+      if (last && pg >= 0) {
+        // The previous item's partial stores are older than anything
+        // else in flight but this step's K rows.
+        wait_stores_complete();
+        if (lane == 0) arr = arrive(p, pg);
+      }
       if (last && tid == 0) claim = atomicAdd(use_shared ? shared_ctr : claim_ctr, 1);
       // Where the prefetch goes: this wave's next chunk of the item, else
       // its first chunk of the next item, else the dummy row (scalar
@@ -941,6 +1032,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       s_next[0] = item;
       s_next[2] = use_shared;
     }
+    // s_red is free after the prologue: flag of the wave that arrived last.
+    if (pg >= 0 && lane == 0) s_red[wave] = arr == kNW * pnp - 1;
 
     // Merge the wave-level softmax states of this partition.
     float* s_acc = reinterpret_cast<float*>(s_raw);
@@ -957,6 +1050,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     // are stored during the next item's last chunk.
     const int nn = __builtin_amdgcn_readfirstlane(s_next[0]);
     use_shared = __builtin_amdgcn_readfirstlane(s_next[2]);
+    const bool merge_prev =
+        pg >= 0 && __builtin_amdgcn_readfirstlane(s_red[0] | s_red[1] | s_red[2] | s_red[3]);
     tab_next = fetch_tab<CT, D, BS>(
         p, decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, order).w, wave,
         lane);
@@ -1001,14 +1096,37 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
           // Partial writes interleaved with the K/V reads cost far more
           // HBM time than their bytes, so they are kept small.
           const u32x2_t o4 = {pack_bf16x2(O.x, O.y), pack_bf16x2(O.z, O.w)};
-          __builtin_nontemporal_store(
-              o4, reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(p.ws_acc) + pi * D + d));
-          if (d == 0) {
-            p.ws_m[pi] = M;
-            p.ws_l[pi] = L;
+          uint16_t* pa = reinterpret_cast<uint16_t*>(p.ws_acc) + pi * D + d;
+          if (fused) {
+            // agent scope: the merging workgroup may sit on another XCD
+            __hip_atomic_store(reinterpret_cast<unsigned long long*>(pa),
+                               __builtin_bit_cast(unsigned long long, o4), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            if (d == 0) {
+              __hip_atomic_store(p.ws_m + pi, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(p.ws_l + pi, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          } else {
+            __builtin_nontemporal_store(o4, reinterpret_cast<u32x2_t*>(pa));
+            if (d == 0) {
+              p.ws_m[pi] = M;
+              p.ws_l[pi] = L;
+            }
           }
         }
       }
+    }
+    if (fused) {
+      if (merge_prev) {
+        merge_group<D, MODE>(p, pg, pnp);
+        if (tid == 0)
+          __hip_atomic_store(p.arrivals + pg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      // This item's partials are counted in at the next item's last step.
+      const bool split = it.live && it.n > p.P;
+      pg = __builtin_amdgcn_readfirstlane(split ? it.w.seq * Y + it.w.kvh * p.chunks + it.w.r0 / 16
+                                                : -1);
+      pnp = __builtin_amdgcn_readfirstlane((it.n + p.P - 1) / p.P);
     }
     __syncthreads();  // Z: merge reads of s_raw / s_m / s_l and s_next done
 
@@ -1016,6 +1134,17 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     nxt = nn;
     it = nx;
     buf ^= 1;
+  }
+  // The last item's partials.
+  if (pg >= 0) {
+    wait_stores_complete();
+    if (lane == 0) s_red[wave] = arrive(p, pg) == kNW * pnp - 1;
+    __syncthreads();
+    if (s_red[0] | s_red[1] | s_red[2] | s_red[3]) {
+      merge_group<D, MODE>(p, pg, pnp);
+      if (tid == 0)
+        __hip_atomic_store(p.arrivals + pg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   // The last workgroup to finish returns the counters to zero.
   if (tid == 0 && atomicAdd(done_ctr, 1) == (int)gridDim.x - 1) {
@@ -1071,6 +1200,8 @@ hipError_t launch_bs(const DecodeArgs& a) {
   p.q = a.q; p.kc = a.key_cache; p.vc = a.value_cache; p.ks = a.key_scale; p.vs = a.value_scale;
   p.tables = a.tables; p.lens = a.lens; p.out = a.out;
   p.ws_m = a.ws_m; p.ws_l = a.ws_l; p.ws_acc = a.ws_acc; p.sched = a.sched;
+  p.arrivals = a.arrivals;
+  p.fused = a.fused ? 1 : 0;
   p.S = a.S; p.H = a.H; p.H_kv = a.H_kv; p.G = a.H / a.H_kv; p.M = a.M;
   p.chunks = (a.M * p.G + 15) / 16;
   p.max_blocks = a.max_blocks; p.P = a.P; p.NP = a.NP;

@@ -17,7 +17,7 @@
 namespace {
 
 constexpr size_t kScratchBytes = PKV_DECODE_NOALLOC_MAX_WORKSPACE;
-constexpr size_t kHeaderBytes = 4096;  // work-queue counters: zero at every call's start
+constexpr int kClearThreads = 256;  // 16 bytes each: 4 KiB per workgroup
 constexpr int kMaxDevices = 64;
 
 __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
@@ -37,10 +37,12 @@ void* scratch_ptr(int dev) {
   return g_scratch[dev];
 }
 
-// Zeroes the counter header with plain vector stores (a fill kernel rather
-// than a memset node, so the call can be captured in a graph).
-__global__ __launch_bounds__(256) void clear_header_kernel(uint4* header) {
-  header[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+// Zeroes the leading counters (n_vec 16-byte vectors) with plain vector
+// stores: a fill kernel rather than a memset node, so the call can be
+// captured in a graph.
+__global__ __launch_bounds__(kClearThreads) void clear_counters_kernel(uint4* head, size_t n_vec) {
+  const size_t i = (size_t)blockIdx.x * kClearThreads + threadIdx.x;
+  if (i < n_vec) head[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 }  // namespace
@@ -75,8 +77,13 @@ pkv_status_t paged_attention_decode_noalloc(
   void* ws = scratch_ptr(dev);
   if (!ws) return PKV_ERR_HIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(clear_header_kernel, dim3(1), dim3(kHeaderBytes / 16), 0, s,
-                     reinterpret_cast<uint4*>(ws));
+  // a multiple of 256 bytes, within `need`
+  const size_t zero = paged_attention_decode_workspace_counter_bytes(
+      num_seqs, num_heads, num_kv_heads, head_size, block_size, max_context_len, q_dtype,
+      cache_dtype, partition_size);
+  const size_t n_vec = zero / 16;
+  hipLaunchKernelGGL(clear_counters_kernel, dim3((unsigned)((n_vec + kClearThreads - 1) / kClearThreads)),
+                     dim3(kClearThreads), 0, s, reinterpret_cast<uint4*>(ws), n_vec);
   if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   return paged_attention_decode(out, query, key_cache, value_cache, key_scale, value_scale,
                                 block_tables, context_lens, num_seqs, num_heads, num_kv_heads,

@@ -13,6 +13,10 @@ namespace pkv {
 // partition holds at most this many blocks).
 constexpr int kDecodeMaxTable = 256;
 
+// Most partitions per context whose partials the decode kernel merges
+// itself (one batch of loads per merge); longer splits use the reduce kernel.
+constexpr int kFusedMaxPartitions = 4;
+
 struct WriteArgs {
   const void* key;
   const void* value;
@@ -57,6 +61,9 @@ struct DecodeArgs {
   float* ws_acc;  // [S][H][NP][D]  unnormalised output per partition: fp32 for
                   // fp32 queries, bf16 (in the first half of the region) for
                   // bf16 queries, whose output is bf16 anyway
+  int* arrivals;  // [S][H_kv x row groups] partition arrivals (split partials
+                  // merged by the partition kernel), zero between calls
+  bool fused = false;  // the partition kernel merges the partials: no reduce launch
   hipStream_t stream;
 };
 

@@ -61,11 +61,18 @@ def test_partition_and_workspace_queries():
     assert pkv.decode_partition_size(256, 40, 8, 128, 16, 8192, 1, 2, 0) == 4096
     assert pkv.decode_partition_size(256, 40, 8, 128, 16, 1500, 1, 2, 0) == 1024
     assert pkv.decode_workspace_size(4, 8, 8, 128, 16, 300, 1, 1, 0) == 4096
-    # long contexts: 512-token partitions, partials for m, l and acc
+    assert pkv.decode_workspace_counter_bytes(4, 8, 8, 128, 16, 300, 1, 1, 0) == 4096
+    # long contexts: 512-token partitions; S x H partition arrival counters
+    # (rounded to 256 bytes) after the header, then partials for m, l and acc
     assert pkv.decode_partition_size(8, 64, 8, 128, 8, 32768, 1, 1, 512) == 512
     rows = 8 * 64 * 64
-    expect = 4096 + 2 * ((rows * 4 + 255) // 256 * 256) + (rows * 128 * 4 + 255) // 256 * 256
+    arrivals = (8 * 64 * 4 + 255) // 256 * 256
+    expect = (4096 + arrivals + 2 * ((rows * 4 + 255) // 256 * 256)
+              + (rows * 128 * 4 + 255) // 256 * 256)
     assert pkv.decode_workspace_size(8, 64, 8, 128, 8, 32768, 1, 1, 512) == expect
+    assert pkv.decode_workspace_counter_bytes(8, 64, 8, 128, 8, 32768, 1, 1, 512) == 4096 + arrivals
+    assert pkv.decode_workspace_counter_bytes(3, 5, 5, 64, 16, 200, 1, 1, 64) == 4096 + 256
+    assert pkv.decode_workspace_counter_bytes(8, 64, 8, 96, 8, 32768, 1, 1, 0) == 0
     # partition not a multiple of the block size, bad head size, bad dtype pair
     assert pkv.decode_partition_size(8, 64, 8, 128, 16, 32768, 1, 1, 40) < 0
     assert pkv.decode_partition_size(8, 64, 8, 96, 16, 32768, 1, 1, 0) < 0

@@ -80,6 +80,21 @@ def test_non_zero_workspace_header():
         _decode(q, kc, tables, lens, 40, workspace=ws)
 
 
+def test_non_zero_arrival_counter():
+    """A partition arrival counter of the fused merge left non-zero (the
+    counters after the 4 KiB header, present when a context spans two
+    partitions) is caught as well."""
+    q, kc, tables, lens = _decode_inputs()
+    zero = pkv.decode_workspace_counter_bytes(3, 4, 2, 64, 16, 40, 1, 1, 16)
+    assert zero == 4096 + 256
+    ws = torch.zeros(8192, dtype=torch.uint8)
+    _validate.check_workspace_header("t", ws, zero)
+    ws[4096 + 4 * 5] = 1                       # sequence 1's counter
+    with pytest.raises(pkv.ContractError, match="partition arrival"):
+        pkv.paged_attention_decode(torch.empty_like(q), q, kc, kc, tables, lens, 40, 0.125,
+                                   partition_size=16, workspace=ws)
+
+
 def test_prefill_chunk_longer_than_a_context():
     q, kc, tables, lens = _decode_inputs(lens=(20, 33, 5))
     q4 = torch.zeros(3, 8, 4, 64, dtype=torch.bfloat16)      # M = 8 > lens[2] = 5
