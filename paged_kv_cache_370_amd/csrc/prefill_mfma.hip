@@ -197,10 +197,17 @@ struct Layout {
   static constexpr int NKC = D / 32;                // k-steps of the score products
   static constexpr int NMD = D / 16;                // 16-wide d tiles of O^T
   // Physical 16-byte piece of logical piece p in row k: XOR with bits of the
-  // row's 256-byte line, so 16 consecutive rows (K reads) and the 16 rows of
-  // a transposed read spread over all banks.  Rows k, k + 16 and k + 32
-  // share the pattern.
-  __device__ static __forceinline__ int swz(int k) { return (k / RB) & (PR - 1); }
+  // row index, so the K fragment reads (ds_read_b128, lane (q4, r) reading
+  // row r, logical piece (D/32) q4 + c) meet no bank conflicts.  The row's
+  // bit 2 is also folded into bit 3: with the row XORed in unchanged, a
+  // probe of exactly this read pattern took 8 LDS cycles per instruction on
+  // gfx950 (half of them counted as bank conflicts), with this swizzle 4, the
+  // cost of a conflict-free 1 KiB read (D = 128 and 64).  Rows k, k + 16 and
+  // k + 32 share the pattern.
+  __device__ static __forceinline__ int swz(int k) {
+    const int s = (k ^ ((k & 4) << 1)) & 15;
+    return (s / RB) & (PR - 1);
+  }
   __device__ static __forceinline__ int phys(int k, int p) { return p ^ swz(k); }
   // V tile: XOR of the 32-byte half-piece index, so the 4 rows of a
   // transposed read group (and 8 consecutive rows) sit in distinct banks.
