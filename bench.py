@@ -494,12 +494,16 @@ def main():
         "data": "synthetic",
         "config": {k: head[k] for k in ("workload", "seqs", "q_heads", "kv_heads", "head_size",
                                         "block_size", "max_context", "mean_context",
-                                        "partition_size", "kv_bytes_per_step", "kv_blocks_read")},
+                                        "partition_size", "partitions", "decode_launches",
+                                        "kv_bytes_per_step", "kv_blocks_read")},
         "pct_hbm_peak": head["pct_hbm_peak"],
         "seq_heads_per_s": head["seq_heads_per_s"],
         "timing": (f"median of per-iteration HIP events; before each iteration, outside the "
                    f"events, the MALL is flushed ({args.flush_mode}, {args.flush_mib} MiB)"),
-        "step": "paged_kv_cache_write + decode partitions + reduce",
+        "step": ("paged_kv_cache_write + paged_attention_decode (one launch"
+                 + (", partials merged in the decode kernel)" if head["partitions"] > 1 else ")")
+                 if head["decode_launches"] == 1 else
+                 "paged_kv_cache_write + paged_attention_decode (partition kernel + reduce)"),
         "flushed_ms": head["flushed_ms"],
         "decode_GB_per_s": head["decode_GB_per_s"],
         "decode_pct_hbm_peak": head["decode_pct_hbm_peak"],
