@@ -483,8 +483,48 @@ __device__ __forceinline__ void scan_begin(const MfmaParams& p, int* s_tmp, int 
   for (int k = lane; k < kSortKeys; k += 64) mask[k] = 0ull;
 }
 
+// Full partitions in sequence order (they all hold P tokens, so their order
+// does not matter for longest-first): s_full[i] = (F_i << 1) | r_i, F_i the
+// full partitions of sequences before i and r_i whether sequence i ends in
+// a shorter (or empty) partition; s_full[S] = F << 1.  A workgroup whose
+// first item is a full partition can start it from this alone, before the
+// sort of the last partitions.  Returns F.
+__device__ int full_offsets(const MfmaParams& p, int* s_full, int* s_red, const int (&len)[2]) {
+  constexpr int NTH = kNW * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int nf[2], rg[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int n = max(len[r], 0);
+    nf[r] = len[r] >= 0 ? n / p.P : 0;
+    rg[r] = len[r] >= 0 && (n % p.P != 0 || n == 0) ? 1 : 0;
+  }
+  const int inc0 = wave_inclusive_sum(nf[0]);
+  const int inc1 = wave_inclusive_sum(nf[1]);
+  if (lane == 63) {
+    s_red[wave] = inc0;
+    s_red[kNW + wave] = inc1;
+  }
+  __syncthreads();
+  int e0 = inc0 - nf[0], e1 = inc1 - nf[1], t0 = 0, t1 = 0;
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) {
+    const int a = s_red[w], b = s_red[kNW + w];
+    e0 += w < wave ? a : 0;
+    e1 += w < wave ? b : 0;
+    t0 += a;
+    t1 += b;
+  }
+  // sequences tid (offset e0) and NTH + tid (after all of the first NTH)
+  if (len[0] >= 0) s_full[tid] = (e0 << 1) | rg[0];
+  if (len[1] >= 0) s_full[NTH + tid] = ((t0 + e1) << 1) | rg[1];
+  if (tid == 0) s_full[p.S] = (t0 + t1) << 1;
+  __syncthreads();  // s_full complete; s_red free again
+  return t0 + t1;
+}
+
 template <int MODE, int BS>
-__device__ int build_offsets(const MfmaParams& p, int* s_full, uint16_t* s_rag, int* s_seq,
+__device__ void build_offsets(const MfmaParams& p, uint16_t* s_rag, int* s_seq,
                              int* s_red, int* s_tmp, const int (&len)[2],
                              int* n_rag) {
   constexpr int NTH = kNW * 64;
@@ -550,34 +590,27 @@ __device__ int build_offsets(const MfmaParams& p, int* s_full, uint16_t* s_rag, 
   }
   __syncthreads();
 
-  // Full and short partitions before each sorted position: one pass of two
-  // wave sums, one barrier.
+  // Short (or only) partitions before each sorted position: one pass of a
+  // wave sum, one barrier.
   const int per = (p.S + NTH - 1) / NTH;
   const int base = tid * per;
-  int nf = 0, nr = 0;
+  int nr = 0;
   for (int k = 0; k < per; ++k) {
     const int pos = base + k;
     if (pos < p.S) {
       int f, r;
       seq_items(s_seq[pos], p.P, f, r);
-      nf += f;
       nr += r;
     }
   }
-  const int incf = wave_inclusive_sum(nf);
   const int incr = wave_inclusive_sum(nr);
-  if (lane == 63) {
-    s_red[kNW + wave] = incf;
-    s_red[2 * kNW + wave] = incr;
-  }
+  if (lane == 63) s_red[2 * kNW + wave] = incr;
   __syncthreads();
-  int ef = incf - nf, er = incr - nr, F = 0, R = 0;
+  int er = incr - nr, R = 0;
 #pragma unroll
   for (int w = 0; w < kNW; ++w) {
-    const int fw = s_red[kNW + w], rw = s_red[2 * kNW + w];
-    ef += w < wave ? fw : 0;
+    const int rw = s_red[2 * kNW + w];
     er += w < wave ? rw : 0;
-    F += fw;
     R += rw;
   }
   for (int k = 0; k < per; ++k) {
@@ -585,19 +618,13 @@ __device__ int build_offsets(const MfmaParams& p, int* s_full, uint16_t* s_rag, 
     if (pos < p.S) {
       int f, r;
       seq_items(s_seq[pos], p.P, f, r);
-      s_full[pos] = ef;
       s_rag[pos] = (uint16_t)er;
-      ef += f;
       er += r;
     }
   }
-  if (tid == 0) {
-    s_full[p.S] = F;
-    s_rag[p.S] = (uint16_t)R;
-  }
+  if (tid == 0) s_rag[p.S] = (uint16_t)R;
   __syncthreads();
   *n_rag = R;
-  return F;
 }
 
 // Largest i in [0, S) with off[i] <= rest, for non-decreasing off with
@@ -613,6 +640,18 @@ __device__ __forceinline__ int find_seq(const T* off, int S, int rest) {
   return lo;
 }
 
+// Largest i in [0, S) with full[i] >> 1 <= rest (full offsets in sequence
+// order, flag bit 0; see full_offsets).
+__device__ __forceinline__ int find_full(const int* full, int S, int rest) {
+  int lo = 0, hi = S;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((full[mid] >> 1) <= rest) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // Decoded work item: its partition and whether it exists (without the
 // sequence scan, items past a sequence's end are placeholders).
 struct Item {
@@ -623,9 +662,9 @@ struct Item {
 
 // The workgroup's LDS view of the item order.
 struct Order {
-  const int* full;
-  const uint16_t* rag;
-  const int* seq;  // n << kSeqBits | sequence, by sorted position
+  const int* full;      // full partitions before each sequence, in sequence order (full_offsets)
+  const uint16_t* rag;  // short partitions before each sorted position
+  const int* seq;       // n << kSeqBits | sequence, by sorted position
 };
 
 template <int BS, bool SCAN, int MODE>
@@ -638,18 +677,28 @@ __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y
   if constexpr (SCAN) {
     // Values read from LDS are per-lane to the compiler; the item is uniform
     // over the workgroup, so move them to scalar registers.
-    int packed;
     if (rest < n_full) {
-      const int pos = __builtin_amdgcn_readfirstlane(find_seq(o.full, p.S, rest));
-      packed = __builtin_amdgcn_readfirstlane(o.seq[pos]);
-      it.part = rest - __builtin_amdgcn_readfirstlane(o.full[pos]);
+      // A full partition of sequence i.  Its length stands in as
+      // (full partitions) x P, plus one if a shorter partition follows: the
+      // same partition ends, the same "fits one partition" test and the same
+      // partition count as the true length.  Causal rows need the true
+      // length (their positions), read from memory.
+      const int i = __builtin_amdgcn_readfirstlane(find_full(o.full, p.S, rest));
+      const int e0 = __builtin_amdgcn_readfirstlane(o.full[i]);
+      const int e1 = __builtin_amdgcn_readfirstlane(o.full[i + 1]);
+      seq = i;
+      it.part = rest - (e0 >> 1);
+      if constexpr (MODE == kModeCausal)
+        it.n = __builtin_amdgcn_readfirstlane(seq_len<MODE>(p, i));
+      else
+        it.n = ((e1 >> 1) - (e0 >> 1)) * p.P + (e0 & 1);
     } else {
       const int pos = __builtin_amdgcn_readfirstlane(find_seq(o.rag, p.S, rest - n_full));
-      packed = __builtin_amdgcn_readfirstlane(o.seq[pos]);
+      const int packed = __builtin_amdgcn_readfirstlane(o.seq[pos]);
       it.part = (packed >> kSeqBits) / p.P;
+      seq = min(packed & ((1 << kSeqBits) - 1), p.S - 1);
+      it.n = packed >> kSeqBits;
     }
-    seq = min(packed & ((1 << kSeqBits) - 1), p.S - 1);
-    it.n = packed >> kSeqBits;
     it.live = true;
   } else {
     seq = rest / p.NP;
@@ -842,12 +891,51 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   if (tid < 4) s_zero[tid] = 0;
   int len[2] = {-1, -1};
   if constexpr (SCAN) scan_begin<MODE>(p, reinterpret_cast<int*>(s_raw), len);
+  constexpr int EPC = Gm::CHUNK / BS;  // block ids per chunk
+  const Src dummy{g_dummy_row, g_dummy_row, reinterpret_cast<const float*>(g_dummy_row),
+                  reinterpret_cast<const float*>(g_dummy_row)};
+  const Src cache{p.kc, p.vc, p.ks, p.vs};
+  Part dummy_part{};  // token 0 of block 0, KV head 0: row 0 of the dummy
+  dummy_part.end = 1;
+
+  KStage<CT, D> ks;
+  VStage<CT, D> vs;
+  // A wave without a chunk of its first item runs a masked step on
+  // whatever its registers hold: selects turn those scores into -inf and V
+  // rows into zeros, but the FP8 V scale multiplies p = 0, so it must not be
+  // left uninitialised (0 * NaN = NaN).
+#pragma unroll
+  for (int T = 0; T < kNT; ++T) ks.ksc[T] = ks.vsc[T] = 0.f;
+
   int total, n_full = 0;
+  Item it{};
+  int tab_first = 0;
+  uint4 q_first = make_uint4(0u, 0u, 0u, 0u);
+  // Uniform: the first item is a full partition, found from the full
+  // offsets alone; its block ids and Q are fetched and its first chunk's
+  // loads issued before the sort of the last partitions, which then runs
+  // while they are in flight.
+  bool early = false;
   if constexpr (SCAN) {
+    n_full = full_offsets(p, s_full, s_red, len);  // has barriers: s_next is visible
+    const int first = __builtin_amdgcn_readfirstlane(s_next[0]);
+    early = first < Y * n_full;
+    if (early) {
+      it = decode_item<BS, SCAN, MODE>(p, first, Y, n_full, order);
+      tab_first = fetch_tab<CT, D, BS>(p, it.w, wave, lane);
+      q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
+      store_tab(tab_first, s_wtab[0][wave], lane);  // the wave's own slice
+      wave_lds_sync();
+      const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
+      if (nvalid > wave) {
+        const int c0 = it.w.start + wave * Gm::CHUNK;
+        load_v<CT, D, BS>(vs, p, cache, it.w, s_wtab[0][wave], c0, lane);
+        load_k<CT, D, BS>(ks, p, cache, it.w, s_wtab[0][wave], c0, lane);
+      }
+    }
     int n_rag;
-    // has barriers; s_raw is free until the first chunk
-    n_full = build_offsets<MODE, BS>(p, s_full, s_rag, s_seq, s_red,
-                                     reinterpret_cast<int*>(s_raw), len, &n_rag);
+    // has barriers; s_raw is free until the first chunk's V rows are stored
+    build_offsets<MODE, BS>(p, s_rag, s_seq, s_red, reinterpret_cast<int*>(s_raw), len, &n_rag);
     total = Y * (n_full + n_rag);
   } else {
     total = Y * p.S * p.NP;
@@ -863,45 +951,32 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   int cur = s_next[0];
   int nxt = s_next[1];
   int buf = 0;
-  constexpr int EPC = Gm::CHUNK / BS;  // block ids per chunk
-  Item it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, order);
-  // The first item's block ids and Q and the second item's block ids are
-  // requested together (one memory round trip before the first chunk's
-  // loads, not three).  The second item's ids travel in a register until
-  // the first item's loop stores them (each item's are fetched one item
-  // ahead).
-  const int tab_first = fetch_tab<CT, D, BS>(p, it.w, wave, lane);
-  const uint4 q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
+  // Otherwise the first item's block ids and Q and the second item's block
+  // ids are requested together (one memory round trip before the first
+  // chunk's loads, not three).  The second item's ids travel in a register
+  // until the first item's loop stores them (each item's are fetched one
+  // item ahead).
+  if (!early) {
+    it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, order);
+    tab_first = fetch_tab<CT, D, BS>(p, it.w, wave, lane);
+    q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
+  }
   int tab_next = fetch_tab<CT, D, BS>(
       p, decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, order).w, wave,
       lane);
   if (cur < total) {
-    store_tab(tab_first, s_wtab[0][wave], lane);
+    if (!early) store_tab(tab_first, s_wtab[0][wave], lane);
     store_q<CT, D>(q_first, it.w, s_qf[0], tid);
   }
   __syncthreads();
 
-  const Src dummy{g_dummy_row, g_dummy_row, reinterpret_cast<const float*>(g_dummy_row),
-                  reinterpret_cast<const float*>(g_dummy_row)};
-  const Src cache{p.kc, p.vc, p.ks, p.vs};
-  Part dummy_part{};  // token 0 of block 0, KV head 0: row 0 of the dummy
-  dummy_part.end = 1;
-
-  KStage<CT, D> ks;
-  VStage<CT, D> vs;
-  // A wave without a chunk of its first item runs a masked step on
-  // whatever its registers hold: selects turn those scores into -inf and V
-  // rows into zeros, but the FP8 V scale multiplies p = 0, so it must not be
-  // left uninitialised (0 * NaN = NaN).
-#pragma unroll
-  for (int T = 0; T < kNT; ++T) ks.ksc[T] = ks.vsc[T] = 0.f;
   // Fused merge: the row group (sequence x Y + y) of the previous item,
   // whose partials this workgroup stored and has not yet counted in (-1:
   // none), and the group's partition count.  Uniform.
   int pg = -1, pnp = 0;
   const bool fused = MODE == kModeDecode && p.fused != 0;
-  // First chunk of the first item.
-  if (cur < total && it.live) {
+  // First chunk of the first item (an early one's went out before the sort).
+  if (!early && cur < total && it.live) {
     const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
     if (nvalid > wave) {
       const int c0 = it.w.start + wave * Gm::CHUNK;

@@ -94,3 +94,46 @@ def test_zero_prefix_is_decode():
     dw.write()
     dec = dw.decode().clone()
     assert np.array_equal(to_host(_shared(dw, 0)), to_host(dec))
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_repeated_calls_on_one_workspace(cache):
+    """One workspace serves repeated shared-prefix calls (sequences shorter
+    than the prefix and an empty one included): its work-queue counters are
+    zero after each call, and every call gives the same bits."""
+    import paged_kv_cache_370_amd as pkv
+    rng = np.random.default_rng(880)
+    S, H_kv, G, bs = 40, 2, 4, 16
+    prefix = 20 * bs
+    lens = prefix + rng.integers(1, 300, size=S)
+    w = workloads.build_workload(f"shared-merged-{cache}", S, H_kv * G, H_kv, 128, bs, "bf16",
+                                 cache, lens, 881, prefix_tokens=prefix,
+                                 fill="write" if cache == "fp8" else "random")
+    short = w.context_lens.copy()
+    short[3] = prefix - 5                    # shorter than the prefix
+    short[4] = 0
+    w.context_lens = short
+    _say(f"case shared merged {cache} S={S} prefix={prefix}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle_decode(w, kc, vc, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    qc, cc = 1, {"bf16": 1, "fp8": 2}[cache]
+    need = pkv.shared_prefix_workspace_size(S, w.H, H_kv, 128, bs, w.max_context_len, prefix,
+                                            qc, cc, 0)
+    zero = 4096
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for k in range(3):
+        out = torch.full_like(dw.q, float("nan"))
+        pkv.paged_attention_decode_shared_prefix(out, dw.q, dw.kc, dw.vc, dw.tables, dw.lens,
+                                                 w.max_context_len, w.scale, prefix, dw.ks,
+                                                 dw.vs, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:zero].count_nonzero()) == 0, k
+        err = max_err(out_f64(out), ref)
+        _say(f"  call {k} max_err={err:.3e}")
+        assert err <= TOL[cache], (k, err)
+        assert np.all(out_f64(out)[4] == 0)
+        outs.append(to_host(out))
+    assert all(np.array_equal(o, outs[0]) for o in outs[1:])

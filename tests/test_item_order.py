@@ -105,25 +105,27 @@ def test_edge_batches():
 
 def kernel_items(lens, P, bs, Y):
     """Every item the kernel enumerates, as (sequence, row group, partition):
-    the sorted order's full partitions, then its last partitions, decoded the
-    way the kernel decodes an item index (item % Y is the row group)."""
+    the full partitions first, in sequence order (every one holds P tokens,
+    so their order does not matter for longest-first; a workgroup can start
+    one from a prefix sum over the lengths, before the sort), then the last
+    (shorter or only) partitions in the sorted order, decoded the way the
+    kernel decodes an item index (item % Y is the row group)."""
     S = len(lens)
     order, _ = kernel_order(lens, P, bs)
-    nf, nr = [], []
+    nf = [int(lens[i]) // P for i in range(S)]
+    nr = []
     for pos in range(S):
         n = int(lens[int(order[pos])])
-        nf.append(n // P)
         nr.append(1 if (n % P != 0 or n == 0) else 0)
-    full = np.concatenate([[0], np.cumsum(nf)])
-    rag = np.concatenate([[0], np.cumsum(nr)])
+    full = np.concatenate([[0], np.cumsum(nf)])      # by sequence index
+    rag = np.concatenate([[0], np.cumsum(nr)])       # by sorted position
     F, R = int(full[-1]), int(rag[-1])
     items = []
     for item in range(Y * (F + R)):
         y, rest = item % Y, item // Y
         if rest < F:
-            pos = int(np.searchsorted(full, rest, side="right") - 1)
-            seq = int(order[pos])
-            part = rest - int(full[pos])
+            seq = int(np.searchsorted(full, rest, side="right") - 1)
+            part = rest - int(full[seq])
         else:
             pos = int(np.searchsorted(rag, rest - F, side="right") - 1)
             seq = int(order[pos])
