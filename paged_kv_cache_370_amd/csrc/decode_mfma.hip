@@ -22,9 +22,13 @@
 // every workgroup serves once its own queue is empty, so XCDs that run
 // slower than the others do not set the end of the kernel.  The last
 // workgroup to finish resets the counters to zero for the next call.
-// Items are software-pipelined: while one item streams, the next item's
-// block ids and Q are fetched, the item after it is claimed during the last
-// step, and each wave issues the next item's first chunk before the merge.
+// Items are software-pipelined.  With several query tokens per sequence
+// (or a split context), a workgroup holds one item in reserve: while one
+// item streams, the next item's block ids and Q are fetched, the item after
+// it is claimed during the last step, and each wave issues the next item's
+// first chunk before the merge.  With one query token per sequence it holds
+// none: the next item is claimed during the last step, its block ids and Q
+// are fetched during the merge, and its first chunk follows.
 //
 // Why MFMA: the query heads that share a KV head turn both products into
 // small dense contractions, [16 tokens x D] . [D x 16 heads] for the scores
@@ -122,6 +126,12 @@ enum : int { kModeDecode = 0, kModeCausal = 1, kModePrefixRows = 2, kModeSuffix 
 
 template <int MODE>
 constexpr bool kSplit = MODE == kModePrefixRows || MODE == kModeSuffix;
+
+// Launches whose workgroups claim each item only when the one before it
+// ends (one query token per sequence); in the other kinds every workgroup
+// holds one item in reserve.
+template <int MODE>
+constexpr bool kOneDeep = MODE == kModeDecode;
 
 // Context length the launch sees for sequence i.
 // A length above the launch's bound (a broken caller contract) is cut to
@@ -870,14 +880,21 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   const int Y = p.H_kv * p.chunks;
 
   // Items [0, n_local) form the per-XCD queues: queue `queue` holds items
-  // k * nq + queue.  Its first 2 * queue_wgs items are taken statically
-  // (workgroup b starts with items b and (queue_wgs + b / nq) * nq + queue,
-  // so the launch makes no atomic traffic); claim c of the queue's counter
-  // is item (2 * queue_wgs + c) * nq + queue.  Items [n_local, total) form
-  // the shared queue: its claim c is item n_local + c.  A workgroup claims
-  // the item after next at the start of its last chunk step, so the claim's
-  // latency is hidden and a slow workgroup does not hold back an item for
-  // long while others run dry.
+  // k * nq + queue.  Workgroup b starts with item b and, where workgroups
+  // hold a reserve, with item (queue_wgs + b / nq) * nq + queue as well, so
+  // the launch makes no atomic traffic.  Claim c of the queue's counter is
+  // item (n_static * queue_wgs + c) * nq + queue, n_static the static items
+  // per workgroup.  Items [n_local, total) form the shared queue: its claim
+  // c is item n_local + c.  A workgroup claims at the start of its current
+  // item's last chunk step, so the claim's latency is hidden.  One that
+  // holds a reserve claims the item after next and streams the next item's
+  // first chunk during the last step.  A CU serves its resident workgroups
+  // by age, though (the youngest runs at about a third of the oldest's rate
+  // while the others are busy), so a reserve held by a slow workgroup
+  // starts late and ends last.  With one query token per sequence no
+  // workgroup holds one: each claims its next item itself and starts it
+  // after a short pause for its first chunk, which the other workgroups on
+  // its CU fill.
   const int nq = min(8, (int)gridDim.x);
   const int queue = blockIdx.x % nq;
   const int queue_wgs = ((int)gridDim.x - queue + nq - 1) / nq;
@@ -944,26 +961,29 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   // About one shared item per workgroup, and never so many that a static
   // item would fall in the shared range.
   const int n_local = total - max(0, min((int)gridDim.x, total - 2 * (int)gridDim.x - 16));
+  constexpr int n_static = kOneDeep<MODE> ? 1 : 2;
   // Uniform (thread 0 decides, every thread reads it back after barrier
   // Y): this workgroup's own queue is empty and it claims from the shared
   // one.  Kept uniform so its selects stay scalar.
   int use_shared = 0;
   int cur = s_next[0];
-  int nxt = s_next[1];
+  int nxt = kOneDeep<MODE> ? total : s_next[1];
   int buf = 0;
-  // Otherwise the first item's block ids and Q and the second item's block
-  // ids are requested together (one memory round trip before the first
-  // chunk's loads, not three).  The second item's ids travel in a register
-  // until the first item's loop stores them (each item's are fetched one
-  // item ahead).
+  // Otherwise the first item's block ids and Q and, with a reserve, the
+  // second item's block ids are requested together (one memory round trip
+  // before the first chunk's loads, not three).  The second item's ids
+  // travel in a register until the first item's loop stores them (each
+  // item's are fetched one item ahead).
   if (!early) {
     it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, order);
     tab_first = fetch_tab<CT, D, BS>(p, it.w, wave, lane);
     q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
   }
-  int tab_next = fetch_tab<CT, D, BS>(
-      p, decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, order).w, wave,
-      lane);
+  int tab_next = 0;
+  if constexpr (!kOneDeep<MODE>)
+    tab_next = fetch_tab<CT, D, BS>(
+        p, decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, order).w, wave,
+        lane);
   if (cur < total) {
     if (!early) store_tab(tab_first, s_wtab[0][wave], lane);
     store_q<CT, D>(q_first, it.w, s_qf[0], tid);
@@ -975,26 +995,32 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   // none), and the group's partition count.  Uniform.
   int pg = -1, pnp = 0;
   const bool fused = MODE == kModeDecode && p.fused != 0;
-  // First chunk of the first item (an early one's went out before the sort).
-  if (!early && cur < total && it.live) {
-    const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
-    if (nvalid > wave) {
-      const int c0 = it.w.start + wave * Gm::CHUNK;
-      load_v<CT, D, BS>(vs, p, cache, it.w, s_wtab[0][wave], c0, lane);
-      load_k<CT, D, BS>(ks, p, cache, it.w, s_wtab[0][wave], c0, lane);
-    }
-  }
+  // Uniform: the item's first chunk is still to be requested (the first
+  // item's, unless it went out before the sort; every claimed one's
+  // without a reserve).
+  bool prime = !early;
 
   while (cur < total) {
+    if (prime && it.live) {
+      const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
+      if (nvalid > wave) {
+        const int c0 = it.w.start + wave * Gm::CHUNK;
+        load_v<CT, D, BS>(vs, p, cache, it.w, s_wtab[buf][wave], c0, lane);
+        load_k<CT, D, BS>(ks, p, cache, it.w, s_wtab[buf][wave], c0, lane);
+      }
+    }
+    prime = false;
     // The next item's block ids go to the slice buffer the previous item
     // used, inside the chunk loop (below).
     int* wt_nxt = s_wtab[buf ^ 1][wave];
     // Prefetch the next item's Q.  Nothing reads the other buffers until the
     // next item.
     const Item nx = decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, order);
-    const uint4 q_next = fetch_q<CT, D, MODE>(p, nx.w, tid);
-    // The claim of the item after the next one, made at the start of wave
-    // 0's last step (before its loads) and used only after barrier X.
+    uint4 q_next = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (!kOneDeep<MODE>) q_next = fetch_q<CT, D, MODE>(p, nx.w, tid);
+    // The claim of the item after the next one (of the next one, without a
+    // reserve), made at the start of wave 0's last step (before its loads)
+    // and used only after barrier X.
     // (Only thread 0 sets and reads it: initialising it in the other lanes
     // would make the compiler wait for every pending load first.)
     int claim;
@@ -1008,7 +1034,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
 
     uint16_t* s_v = reinterpret_cast<uint16_t*>(s_raw) + wave * VTILE;
     const uint4* qf_cur = s_qf[buf];
-    const bool more = nxt < total;
+    const bool more = !kOneDeep<MODE> && nxt < total;
     const int nvalid = it.live ? (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK : 0;
     const int nvalid_n = more && nx.live ? (nx.w.end - nx.w.start + Gm::CHUNK - 1) / Gm::CHUNK : 0;
     // After its last chunk of this item a wave streams its first chunk of
@@ -1096,7 +1122,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       // queue for good; that first shared claim is the only one made here.
       int item;
       if (!use_shared) {
-        item = (2 * queue_wgs + claim) * nq + queue;
+        item = (n_static * queue_wgs + claim) * nq + queue;
         if (item >= n_local) {
           use_shared = 1;
           item = n_local + atomicAdd(shared_ctr, 1);
@@ -1127,9 +1153,11 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     use_shared = __builtin_amdgcn_readfirstlane(s_next[2]);
     const bool merge_prev =
         pg >= 0 && __builtin_amdgcn_readfirstlane(s_red[0] | s_red[1] | s_red[2] | s_red[3]);
-    tab_next = fetch_tab<CT, D, BS>(
-        p, decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, order).w, wave,
-        lane);
+    const Item ni = decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, order);
+    tab_next = fetch_tab<CT, D, BS>(p, ni.w, wave, lane);
+    // Without a reserve nn is the next item: its Q as well, stored after Z.
+    uint4 q_nn = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (kOneDeep<MODE>) q_nn = fetch_q<CT, D, MODE>(p, ni.w, tid);
 
     // Thread t merges 4 consecutive d of one head: one 16-byte LDS read per
     // wave state and one 16-byte (8-byte for bf16) store, so few stores
@@ -1209,6 +1237,20 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     nxt = nn;
     it = nx;
     buf ^= 1;
+    if constexpr (kOneDeep<MODE>) {
+      // The claimed item is the next one: started as the prologue starts
+      // the first (block ids and Q to this buffer, then, at the loop's top,
+      // every wave's first chunk).
+      cur = nn;
+      nxt = total;
+      it = ni;
+      if (cur < total) {
+        store_tab(tab_next, s_wtab[buf][wave], lane);
+        store_q<CT, D>(q_nn, it.w, s_qf[buf], tid);
+        __syncthreads();
+        prime = true;
+      }
+    }
   }
   // The last item's partials.
   if (pg >= 0) {

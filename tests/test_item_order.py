@@ -161,3 +161,84 @@ def test_every_item_exactly_once_random(seed):
     items = kernel_items(lens, P, bs, Y)
     assert len(items) == len(set(items))
     assert set(items) == _expected_items(lens, P, Y)
+
+
+def queue_items(G, total, one_deep, seed=0):
+    """Replay of the decode kernel's work distribution over a grid of G
+    persistent workgroups.  Every workgroup starts with item b.  Holding a
+    reserve (the multi-token and split launches), it also starts with item
+    (queue_wgs + b / nq) * nq + queue and claims the item after next at each
+    item's last step; one deep (one query token per sequence), it claims the
+    next item itself.  Claims come from the workgroup's per-XCD queue (claim
+    c is item (n_static * queue_wgs + c) * nq + queue) until one runs past
+    the local items, then from the shared queue (claim c is item n_local +
+    c), interleaved across workgroups in a seeded random order.  A workgroup
+    runs items while its current one is below total.  Returns the items each
+    workgroup processed, in order, and n_local."""
+    rng = np.random.default_rng(seed)
+    nq = min(8, G)
+    n_local = total - max(0, min(G, total - 2 * G - 16))
+    n_static = 1 if one_deep else 2
+    local_ctr = [0] * nq
+    shared_ctr = [0]
+    state = {}
+    for b in range(G):
+        queue = b % nq
+        queue_wgs = (G - queue + nq - 1) // nq
+        nxt = total if one_deep else (queue_wgs + b // nq) * nq + queue
+        state[b] = dict(cur=b, nxt=nxt, shared=False, done=[], base=n_static * queue_wgs)
+    active = [b for b in range(G) if state[b]["cur"] < total]
+    while active:
+        b = active[int(rng.integers(len(active)))]
+        st = state[b]
+        st["done"].append(st["cur"])
+        if not st["shared"]:
+            claim = local_ctr[b % nq]
+            local_ctr[b % nq] += 1
+            nn = (st["base"] + claim) * nq + b % nq
+            if nn >= n_local:
+                st["shared"] = True
+                nn = n_local + shared_ctr[0]
+                shared_ctr[0] += 1
+        else:
+            nn = n_local + shared_ctr[0]
+            shared_ctr[0] += 1
+        if one_deep:
+            st["cur"] = nn
+        else:
+            st["cur"], st["nxt"] = st["nxt"], nn
+        if st["cur"] >= total:
+            assert st["nxt"] >= total, "a claimed item dropped"
+            active.remove(b)
+    return [st["done"] for st in state.values()], n_local
+
+
+@pytest.mark.parametrize("one_deep", [True, False])
+@pytest.mark.parametrize("G", [768, 1024, 512, 96, 7, 13, 1, 800])
+@pytest.mark.parametrize("total", [1, 5, 100, 767, 1536, 1551, 1552, 1553, 1600, 2320, 3090,
+                                   4096, 20000])
+def test_queue_distribution_covers_every_item_once(one_deep, G, total):
+    for seed in range(3):
+        done, n_local = queue_items(G, total, one_deep, seed)
+        taken = [i for d in done for i in d]
+        assert len(taken) == len(set(taken)), "an item taken twice"
+        assert set(taken) == set(range(total)), "an item never taken"
+
+
+def test_claims_follow_the_static_items():
+    """The per-XCD queues' claims start right after the static items: item
+    G onwards one deep, 2 G onwards with a reserve (whose static second
+    items are G .. 2 G - 1)."""
+    G, total, nq = 768, 3090, 8
+    for one_deep, first_claimed in ((True, G), (False, 2 * G)):
+        done, n_local = queue_items(G, total, one_deep, seed=5)
+        assert n_local == total - G
+        assert sorted(d[0] for d in done) == list(range(G))
+        if not one_deep:
+            assert sorted(d[1] for d in done) == list(range(G, 2 * G))
+        claimed = sorted(i for d in done for i in d[n_static_of(one_deep):] if i < n_local)
+        assert claimed[:nq] == list(range(first_claimed, first_claimed + nq))
+
+
+def n_static_of(one_deep):
+    return 1 if one_deep else 2
