@@ -22,13 +22,11 @@
 // every workgroup serves once its own queue is empty, so XCDs that run
 // slower than the others do not set the end of the kernel.  The last
 // workgroup to finish resets the counters to zero for the next call.
-// Items are software-pipelined.  With several query tokens per sequence
-// (or a split context), a workgroup holds one item in reserve: while one
-// item streams, the next item's block ids and Q are fetched, the item after
-// it is claimed during the last step, and each wave issues the next item's
-// first chunk before the merge.  With one query token per sequence it holds
-// none: the next item is claimed during the last step, its block ids and Q
-// are fetched during the merge, and its first chunk follows.
+// Items are software-pipelined: the next item is claimed during the current
+// one's last step, its block ids and Q are fetched during the merge, and its
+// first chunk follows.  A workgroup holds no item in reserve: the workgroups
+// on a CU are served by age, so a reserve held by a young one would start
+// late and set the kernel's end.
 //
 // Why MFMA: the query heads that share a KV head turn both products into
 // small dense contractions, [16 tokens x D] . [D x 16 heads] for the scores
@@ -126,12 +124,6 @@ enum : int { kModeDecode = 0, kModeCausal = 1, kModePrefixRows = 2, kModeSuffix 
 
 template <int MODE>
 constexpr bool kSplit = MODE == kModePrefixRows || MODE == kModeSuffix;
-
-// Launches whose workgroups claim each item only when the one before it
-// ends (one query token per sequence); in the other kinds every workgroup
-// holds one item in reserve.
-template <int MODE>
-constexpr bool kOneDeep = MODE == kModeDecode;
 
 // Context length the launch sees for sequence i.
 // A length above the launch's bound (a broken caller contract) is cut to
@@ -859,12 +851,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   constexpr int MERGE = kNW * 16 * MS;
   constexpr int UNION_BYTES = (VTILE * kNW * 2 > MERGE * 4) ? VTILE * kNW * 2 : MERGE * 4;
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[UNION_BYTES];
-  __shared__ int s_wtab[2][kNW][kMaxTable / kNW];
-  __shared__ uint4 s_qf[2][Gm::NKC * 64];
+  __shared__ int s_wtab[kNW][kMaxTable / kNW];
+  __shared__ uint4 s_qf[Gm::NKC * 64];
   __shared__ float s_m[kNW][16];
   __shared__ float s_l[kNW][16];
   __shared__ int s_red[3 * kNW];
-  __shared__ int s_next[3];  // next claimed item, second static item, queue flag
+  __shared__ int s_next[2];  // next claimed item, queue flag
   __shared__ int s_zero[4];  // block id 0 for the dummy row
   __shared__ int s_full[SCAN ? kMaxScanSeqs + 1 : 1];
   __shared__ uint16_t s_rag[SCAN ? kMaxScanSeqs + 1 : 1];
@@ -880,31 +872,22 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   const int Y = p.H_kv * p.chunks;
 
   // Items [0, n_local) form the per-XCD queues: queue `queue` holds items
-  // k * nq + queue.  Workgroup b starts with item b and, where workgroups
-  // hold a reserve, with item (queue_wgs + b / nq) * nq + queue as well, so
-  // the launch makes no atomic traffic.  Claim c of the queue's counter is
-  // item (n_static * queue_wgs + c) * nq + queue, n_static the static items
-  // per workgroup.  Items [n_local, total) form the shared queue: its claim
-  // c is item n_local + c.  A workgroup claims at the start of its current
-  // item's last chunk step, so the claim's latency is hidden.  One that
-  // holds a reserve claims the item after next and streams the next item's
-  // first chunk during the last step.  A CU serves its resident workgroups
-  // by age, though (the youngest runs at about a third of the oldest's rate
-  // while the others are busy), so a reserve held by a slow workgroup
-  // starts late and ends last.  With one query token per sequence no
-  // workgroup holds one: each claims its next item itself and starts it
-  // after a short pause for its first chunk, which the other workgroups on
-  // its CU fill.
+  // k * nq + queue.  Workgroup b starts with item b (no atomic traffic at
+  // launch); claim c of the queue's counter is item (queue_wgs + c) * nq +
+  // queue.  Items [n_local, total) form the shared queue: its claim c is
+  // item n_local + c.  A workgroup claims its next item at the start of the
+  // current item's last chunk step, so the claim's latency is hidden, and
+  // starts it after a short pause for its block ids, Q and first chunk.  A
+  // CU serves its resident workgroups by age (the youngest runs at about a
+  // third of the oldest's rate while the others are busy): that pause is
+  // longest for the young ones, and the other workgroups on the CU fill it.
   const int nq = min(8, (int)gridDim.x);
   const int queue = blockIdx.x % nq;
   const int queue_wgs = ((int)gridDim.x - queue + nq - 1) / nq;
   int* claim_ctr = p.sched + queue * kCounterStride;
   int* shared_ctr = p.sched + 8 * kCounterStride;
   int* done_ctr = p.sched + 9 * kCounterStride;
-  if (tid == 0) {
-    s_next[0] = blockIdx.x;
-    s_next[1] = (queue_wgs + (int)blockIdx.x / nq) * nq + queue;
-  }
+  if (tid == 0) s_next[0] = blockIdx.x;
   if (tid < 4) s_zero[tid] = 0;
   int len[2] = {-1, -1};
   if constexpr (SCAN) scan_begin<MODE>(p, reinterpret_cast<int*>(s_raw), len);
@@ -941,13 +924,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       it = decode_item<BS, SCAN, MODE>(p, first, Y, n_full, order);
       tab_first = fetch_tab<CT, D, BS>(p, it.w, wave, lane);
       q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
-      store_tab(tab_first, s_wtab[0][wave], lane);  // the wave's own slice
+      store_tab(tab_first, s_wtab[wave], lane);  // the wave's own slice
       wave_lds_sync();
       const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
       if (nvalid > wave) {
         const int c0 = it.w.start + wave * Gm::CHUNK;
-        load_v<CT, D, BS>(vs, p, cache, it.w, s_wtab[0][wave], c0, lane);
-        load_k<CT, D, BS>(ks, p, cache, it.w, s_wtab[0][wave], c0, lane);
+        load_v<CT, D, BS>(vs, p, cache, it.w, s_wtab[wave], c0, lane);
+        load_k<CT, D, BS>(ks, p, cache, it.w, s_wtab[wave], c0, lane);
       }
     }
     int n_rag;
@@ -961,32 +944,21 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   // About one shared item per workgroup, and never so many that a static
   // item would fall in the shared range.
   const int n_local = total - max(0, min((int)gridDim.x, total - 2 * (int)gridDim.x - 16));
-  constexpr int n_static = kOneDeep<MODE> ? 1 : 2;
   // Uniform (thread 0 decides, every thread reads it back after barrier
   // Y): this workgroup's own queue is empty and it claims from the shared
   // one.  Kept uniform so its selects stay scalar.
   int use_shared = 0;
   int cur = s_next[0];
-  int nxt = kOneDeep<MODE> ? total : s_next[1];
-  int buf = 0;
-  // Otherwise the first item's block ids and Q and, with a reserve, the
-  // second item's block ids are requested together (one memory round trip
-  // before the first chunk's loads, not three).  The second item's ids
-  // travel in a register until the first item's loop stores them (each
-  // item's are fetched one item ahead).
+  // Otherwise the first item's block ids and Q are requested together (one
+  // memory round trip before the first chunk's loads, not two).
   if (!early) {
     it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, order);
     tab_first = fetch_tab<CT, D, BS>(p, it.w, wave, lane);
     q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
   }
-  int tab_next = 0;
-  if constexpr (!kOneDeep<MODE>)
-    tab_next = fetch_tab<CT, D, BS>(
-        p, decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, order).w, wave,
-        lane);
   if (cur < total) {
-    if (!early) store_tab(tab_first, s_wtab[0][wave], lane);
-    store_q<CT, D>(q_first, it.w, s_qf[0], tid);
+    if (!early) store_tab(tab_first, s_wtab[wave], lane);
+    store_q<CT, D>(q_first, it.w, s_qf, tid);
   }
   __syncthreads();
 
@@ -995,9 +967,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   // none), and the group's partition count.  Uniform.
   int pg = -1, pnp = 0;
   const bool fused = MODE == kModeDecode && p.fused != 0;
-  // Uniform: the item's first chunk is still to be requested (the first
-  // item's, unless it went out before the sort; every claimed one's
-  // without a reserve).
+  // Uniform: the item's first chunk is still to be requested (every item's
+  // but an early first one's, which went out before the sort).
   bool prime = !early;
 
   while (cur < total) {
@@ -1005,22 +976,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
       if (nvalid > wave) {
         const int c0 = it.w.start + wave * Gm::CHUNK;
-        load_v<CT, D, BS>(vs, p, cache, it.w, s_wtab[buf][wave], c0, lane);
-        load_k<CT, D, BS>(ks, p, cache, it.w, s_wtab[buf][wave], c0, lane);
+        load_v<CT, D, BS>(vs, p, cache, it.w, s_wtab[wave], c0, lane);
+        load_k<CT, D, BS>(ks, p, cache, it.w, s_wtab[wave], c0, lane);
       }
     }
     prime = false;
-    // The next item's block ids go to the slice buffer the previous item
-    // used, inside the chunk loop (below).
-    int* wt_nxt = s_wtab[buf ^ 1][wave];
-    // Prefetch the next item's Q.  Nothing reads the other buffers until the
-    // next item.
-    const Item nx = decode_item<BS, SCAN, MODE>(p, min(nxt, total - 1), Y, n_full, order);
-    uint4 q_next = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (!kOneDeep<MODE>) q_next = fetch_q<CT, D, MODE>(p, nx.w, tid);
-    // The claim of the item after the next one (of the next one, without a
-    // reserve), made at the start of wave 0's last step (before its loads)
-    // and used only after barrier X.
+    // The claim of the next item, made at the start of wave 0's last step
+    // (before its loads) and used only after barrier X.
     // (Only thread 0 sets and reads it: initialising it in the other lanes
     // would make the compiler wait for every pending load first.)
     int claim;
@@ -1033,17 +995,11 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     float m = kRunMaxInit, lsum = 0.f;
 
     uint16_t* s_v = reinterpret_cast<uint16_t*>(s_raw) + wave * VTILE;
-    const uint4* qf_cur = s_qf[buf];
-    const bool more = !kOneDeep<MODE> && nxt < total;
     const int nvalid = it.live ? (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK : 0;
-    const int nvalid_n = more && nx.live ? (nx.w.end - nx.w.start + Gm::CHUNK - 1) / Gm::CHUNK : 0;
-    // After its last chunk of this item a wave streams its first chunk of
-    // the next item, so the next item's data arrives during the merge.  A
-    // wave with no chunk of this item runs one fully masked step, which
+    // A wave with no chunk of this item runs one fully masked step, which
     // leaves its state at (kRunMaxInit, 0, 0), so that every wave reaches
     // the loads below.
-    const bool next_mine = nvalid_n > wave;
-    const int* ctab = s_wtab[buf][wave];  // this chunk's block ids
+    const int* ctab = s_wtab[wave];  // this chunk's block ids
     // Causal rows (several query tokens per sequence): token m of a
     // sequence of n cached tokens sits at position n - M + m and sees
     // positions up to it.  With one token per sequence every row sees the
@@ -1072,30 +1028,18 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       }
       if (last && tid == 0) claim = atomicAdd(use_shared ? shared_ctr : claim_ctr, 1);
       // Where the prefetch goes: this wave's next chunk of the item, else
-      // its first chunk of the next item, else the dummy row (scalar
-      // selects, no branch).
-      const bool to_next = last && next_mine;
-      const bool idle = last && !next_mine;
-      const Src src = idle ? dummy : cache;
-      const Part lw = to_next ? nx.w : (idle ? dummy_part : it.w);
-      const int* ntab = to_next ? wt_nxt : (idle ? s_zero : ctab + EPC);
-      const int cn = to_next ? nx.w.start + wave * Gm::CHUNK : (idle ? 0 : c0 + kNW * Gm::CHUNK);
-      // The next item's block ids are written at the wave's second step,
-      // after that step's wait for its V rows: those were requested after
-      // the ids, so the write waits for nothing more.  A wave whose last
-      // step comes first writes them before that step's loads.  (At the top
-      // of the item the write would wait for the previous item's partial
-      // stores as well.)  store_v's wave barrier publishes the write.
-      const bool tab_early = last && ci <= wave + kNW;
-      if (tab_early) wt_nxt[lane] = tab_next;
+      // (last step) the dummy row (scalar selects, no branch).
+      const Src src = last ? dummy : cache;
+      const Part lw = last ? dummy_part : it.w;
+      const int* ntab = last ? s_zero : ctab + EPC;
+      const int cn = last ? 0 : c0 + kNW * Gm::CHUNK;
       store_v<CT, D>(vs, c0, it.w.end, s_v, lane);
-      if (!last && ci == wave + kNW) wt_nxt[lane] = tab_next;
       load_v<CT, D, BS>(vs, p, src, lw, ntab, cn, lane);
       // Keep the scheduler from sinking the prefetch below the products:
       // the loads must be in flight while this chunk is computed.
       __builtin_amdgcn_sched_barrier(0);
       f32x4_t sc[kNT];
-      scores<CT, D>(ks, qf_cur, sc, lane);
+      scores<CT, D>(ks, s_qf, sc, lane);
       float fk[kNT], fv[kNT];
 #pragma unroll
       for (int T = 0; T < kNT; ++T) {
@@ -1115,14 +1059,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
 
-    if (more) store_q<CT, D>(q_next, nx.w, s_qf[buf ^ 1], tid);
-    __syncthreads();  // X: V tiles and s_qf[buf] are free; s_qf[buf^1] is complete
+    __syncthreads();  // X: the V tiles are free
     if (tid == 0) {
       // A claim past the local items moves this workgroup to the shared
       // queue for good; that first shared claim is the only one made here.
       int item;
       if (!use_shared) {
-        item = (n_static * queue_wgs + claim) * nq + queue;
+        item = (queue_wgs + claim) * nq + queue;
         if (item >= n_local) {
           use_shared = 1;
           item = n_local + atomicAdd(shared_ctr, 1);
@@ -1131,7 +1074,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
         item = n_local + claim;
       }
       s_next[0] = item;
-      s_next[2] = use_shared;
+      s_next[1] = use_shared;
     }
     // s_red is free after the prologue: flag of the wave that arrived last.
     if (pg >= 0 && lane == 0) s_red[wave] = arr == kNW * pnp - 1;
@@ -1147,17 +1090,15 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       *reinterpret_cast<f32x4_t*>(&s_acc[(wave * 16 + r) * MS + 16 * md + 4 * q]) = acc[md];
     __syncthreads();  // Y
 
-    // The item after the next one is known now: fetch its block ids, which
-    // are stored during the next item's last chunk.
+    // The next item is known now: its block ids and Q are requested here
+    // and stored after barrier Z, so their latency overlaps the epilogue.
     const int nn = __builtin_amdgcn_readfirstlane(s_next[0]);
-    use_shared = __builtin_amdgcn_readfirstlane(s_next[2]);
+    use_shared = __builtin_amdgcn_readfirstlane(s_next[1]);
     const bool merge_prev =
         pg >= 0 && __builtin_amdgcn_readfirstlane(s_red[0] | s_red[1] | s_red[2] | s_red[3]);
     const Item ni = decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, order);
-    tab_next = fetch_tab<CT, D, BS>(p, ni.w, wave, lane);
-    // Without a reserve nn is the next item: its Q as well, stored after Z.
-    uint4 q_nn = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (kOneDeep<MODE>) q_nn = fetch_q<CT, D, MODE>(p, ni.w, tid);
+    const int tab_nn = fetch_tab<CT, D, BS>(p, ni.w, wave, lane);
+    const uint4 q_nn = fetch_q<CT, D, MODE>(p, ni.w, tid);
 
     // Thread t merges 4 consecutive d of one head: one 16-byte LDS read per
     // wave state and one 16-byte (8-byte for bf16) store, so few stores
@@ -1233,23 +1174,16 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     }
     __syncthreads();  // Z: merge reads of s_raw / s_m / s_l and s_next done
 
-    cur = nxt;
-    nxt = nn;
-    it = nx;
-    buf ^= 1;
-    if constexpr (kOneDeep<MODE>) {
-      // The claimed item is the next one: started as the prologue starts
-      // the first (block ids and Q to this buffer, then, at the loop's top,
-      // every wave's first chunk).
-      cur = nn;
-      nxt = total;
-      it = ni;
-      if (cur < total) {
-        store_tab(tab_next, s_wtab[buf][wave], lane);
-        store_q<CT, D>(q_nn, it.w, s_qf[buf], tid);
-        __syncthreads();
-        prime = true;
-      }
+    // The claimed item starts as the prologue starts the first: block ids
+    // and Q to LDS (every read of the previous item's was before barrier
+    // X), then, at the loop's top, every wave's first chunk.
+    cur = nn;
+    it = ni;
+    if (cur < total) {
+      store_tab(tab_nn, s_wtab[wave], lane);
+      store_q<CT, D>(q_nn, it.w, s_qf, tid);
+      __syncthreads();
+      prime = true;
     }
   }
   // The last item's partials.
