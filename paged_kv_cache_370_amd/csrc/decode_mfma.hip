@@ -112,6 +112,7 @@ struct MfmaParams {
   int slot_off;       // partial slot of partition 0
   int np_stride;      // partial slots per row
   int force_partial;  // write partials even when a context fits one partition
+  int young_from;  // first workgroup that runs only its first item
   float scale_log2;
 };
 
@@ -881,6 +882,10 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   // CU serves its resident workgroups by age (the youngest runs at about a
   // third of the oldest's rate while the others are busy): that pause is
   // longest for the young ones, and the other workgroups on the CU fill it.
+  // With bf16 caches and three or more workgroups per CU the youngest on
+  // each CU (blockIdx.x >= young_from) runs only its first item: it helps
+  // while the queues fill the CU, and an item it claimed later would start
+  // late and end last.
   const int nq = min(8, (int)gridDim.x);
   const int queue = blockIdx.x % nq;
   const int queue_wgs = ((int)gridDim.x - queue + nq - 1) / nq;
@@ -949,6 +954,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   // one.  Kept uniform so its selects stay scalar.
   int use_shared = 0;
   int cur = s_next[0];
+  // Uniform: this workgroup runs its first item and claims no other (only
+  // while every queue keeps a workgroup that claims: workgroup `queue`).
+  const bool stop = (int)blockIdx.x >= p.young_from && p.young_from >= nq;
   // Otherwise the first item's block ids and Q are requested together (one
   // memory round trip before the first chunk's loads, not two).
   if (!early) {
@@ -1026,7 +1034,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
         wait_stores_complete();
         if (lane == 0) arr = arrive(p, pg);
       }
-      if (last && tid == 0) claim = atomicAdd(use_shared ? shared_ctr : claim_ctr, 1);
+      if (last && tid == 0 && !stop) claim = atomicAdd(use_shared ? shared_ctr : claim_ctr, 1);
       // Where the prefetch goes: this wave's next chunk of the item, else
       // (last step) the dummy row (scalar selects, no branch).
       const Src src = last ? dummy : cache;
@@ -1064,7 +1072,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       // A claim past the local items moves this workgroup to the shared
       // queue for good; that first shared claim is the only one made here.
       int item;
-      if (!use_shared) {
+      if (stop) {
+        item = total;  // no claim was made
+      } else if (!use_shared) {
         item = (queue_wgs + claim) * nq + queue;
         if (item >= n_local) {
           use_shared = 1;
@@ -1206,18 +1216,23 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
 }
 
 // Workgroups of a persistent launch: as many as are resident at once (CUs x
-// the kernel's occupancy, a multiple of the 8 XCDs), never more than items.
-// The occupancy query runs once per kernel variant and device.
+// the kernel's occupancy, a multiple of the 8 XCDs), never more than items;
+// *young_from is the first workgroup that runs only its first item.  The
+// occupancy query runs once per kernel variant and device.
 template <typename CT, int D, int BS, bool SCAN, int MODE>
-unsigned persistent_grid(long long items) {
+unsigned persistent_grid(long long items, int* young_from) {
   constexpr int kMaxDev = 64;
   static int resident[kMaxDev];  // per device, for this kernel variant only
+  static int cu_count[kMaxDev];
   const void* kern = reinterpret_cast<const void*>(decode_mfma_kernel<CT, D, BS, SCAN, MODE>);
   int dev = 0;
-  int per_dev = 0;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDev) per_dev = resident[dev];
+  int per_dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDev) {
+    per_dev = resident[dev];
+    cus = cu_count[dev];
+  }
   if (per_dev <= 0) {
-    int cus = 0, blocks = 0;
+    int blocks = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
@@ -1225,22 +1240,36 @@ unsigned persistent_grid(long long items) {
         blocks <= 0)
       blocks = 1;
     per_dev = (cus * blocks + 7) / 8 * 8;
-    if (dev >= 0 && dev < kMaxDev) resident[dev] = per_dev;
+    if (dev >= 0 && dev < kMaxDev) {
+      resident[dev] = per_dev;
+      cu_count[dev] = cus;
+    }
   }
+  // Workgroups are dispatched one per CU at a time, so with three or more
+  // per CU the last `cus` of a full grid are each the youngest on their CU.
+  *young_from = per_dev > 2 * cus ? per_dev - cus : per_dev;
   return (unsigned)(per_dev < items ? per_dev : items);
 }
 
 template <typename CT, int D, int BS, int MODE>
 hipError_t launch_mode(const DecodeArgs& a, const MfmaParams& p, long long items) {
   // The sorted item order packs a context length into 31 - kSeqBits bits.
+  // FP8 caches keep every workgroup claiming: with more vector work per
+  // byte the youngest workgroup on a CU keeps a larger share (about 60% of
+  // the oldest's rate, against a third with bf16 caches) and still adds
+  // throughput after its first item.
+  constexpr bool kStopYoung = Geometry<CT, D>::ELEM == 2;
+  MfmaParams pl = p;
   if (a.S <= kMaxScanSeqs && a.max_ctx < (1 << (31 - kSeqBits))) {
-    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, true, MODE>),
-                       dim3(persistent_grid<CT, D, BS, true, MODE>(items)), dim3(kNW * 64), 0,
-                       a.stream, p);
+    const unsigned grid = persistent_grid<CT, D, BS, true, MODE>(items, &pl.young_from);
+    if (!kStopYoung) pl.young_from = (int)grid;
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, true, MODE>), dim3(grid), dim3(kNW * 64), 0,
+                       a.stream, pl);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, false, MODE>),
-                       dim3(persistent_grid<CT, D, BS, false, MODE>(items)), dim3(kNW * 64), 0,
-                       a.stream, p);
+    const unsigned grid = persistent_grid<CT, D, BS, false, MODE>(items, &pl.young_from);
+    if (!kStopYoung) pl.young_from = (int)grid;
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, D, BS, false, MODE>), dim3(grid), dim3(kNW * 64),
+                       0, a.stream, pl);
   }
   return hipGetLastError();
 }

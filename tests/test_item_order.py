@@ -163,19 +163,20 @@ def test_every_item_exactly_once_random(seed):
     assert set(items) == _expected_items(lens, P, Y)
 
 
-def queue_items(G, total, one_deep, seed=0):
+def queue_items(G, total, one_deep, seed=0, young_from=None):
     """Replay of the decode kernel's work distribution over a grid of G
-    persistent workgroups.  Every workgroup starts with item b.  Holding a
-    reserve (the multi-token and split launches), it also starts with item
-    (queue_wgs + b / nq) * nq + queue and claims the item after next at each
-    item's last step; one deep (one query token per sequence), it claims the
-    next item itself.  Claims come from the workgroup's per-XCD queue (claim
-    c is item (n_static * queue_wgs + c) * nq + queue) until one runs past
-    the local items, then from the shared queue (claim c is item n_local +
-    c), interleaved across workgroups in a seeded random order.  A workgroup
-    runs items while its current one is below total.  Returns the items each
-    workgroup processed, in order, and n_local."""
+    persistent workgroups.  Every workgroup starts with item b.  Workgroups
+    from young_from on run only that item.  Holding a reserve (as the kernel
+    first did), a workgroup also starts with item (queue_wgs + b / nq) * nq +
+    queue and claims the item after next at each item's last step; one deep,
+    it claims the next item itself.  Claims come from the workgroup's
+    per-XCD queue (claim c is item (n_static * queue_wgs + c) * nq + queue)
+    until one runs past the local items, then from the shared queue (claim c
+    is item n_local + c), interleaved across workgroups in a seeded random
+    order.  A workgroup runs items while its current one is below total.
+    Returns the items each workgroup processed, in order, and n_local."""
     rng = np.random.default_rng(seed)
+    young_from = G if young_from is None else young_from
     nq = min(8, G)
     n_local = total - max(0, min(G, total - 2 * G - 16))
     n_static = 1 if one_deep else 2
@@ -186,13 +187,16 @@ def queue_items(G, total, one_deep, seed=0):
         queue = b % nq
         queue_wgs = (G - queue + nq - 1) // nq
         nxt = total if one_deep else (queue_wgs + b // nq) * nq + queue
-        state[b] = dict(cur=b, nxt=nxt, shared=False, done=[], base=n_static * queue_wgs)
+        state[b] = dict(cur=b, nxt=nxt, shared=False, done=[], base=n_static * queue_wgs,
+                        stop=b >= young_from and young_from >= nq)
     active = [b for b in range(G) if state[b]["cur"] < total]
     while active:
         b = active[int(rng.integers(len(active)))]
         st = state[b]
         st["done"].append(st["cur"])
-        if not st["shared"]:
+        if st["stop"]:
+            nn = total
+        elif not st["shared"]:
             claim = local_ctr[b % nq]
             local_ctr[b % nq] += 1
             nn = (st["base"] + claim) * nq + b % nq
@@ -225,6 +229,24 @@ def test_queue_distribution_covers_every_item_once(one_deep, G, total):
         assert set(taken) == set(range(total)), "an item never taken"
 
 
+@pytest.mark.parametrize("G,young_from", [(768, 512), (1024, 768), (96, 64), (7, 4), (13, 0),
+                                          (800, 544)])
+@pytest.mark.parametrize("total", [1, 100, 767, 1553, 3090, 20000])
+def test_young_workgroups_run_only_their_first_item(G, young_from, total):
+    """The youngest workgroups (blockIdx.x >= young_from) take no claims
+    when every per-XCD queue keeps a workgroup that claims (young_from at
+    least the queue count); the others' claims still cover every item
+    exactly once."""
+    for seed in range(3):
+        done, n_local = queue_items(G, total, True, seed, young_from)
+        taken = [i for d in done for i in d]
+        assert len(taken) == len(set(taken)), "an item taken twice"
+        assert set(taken) == set(range(total)), "an item never taken"
+        if young_from >= min(8, G):
+            for b in range(young_from, G):
+                assert done[b] == ([b] if b < total else [])
+
+
 def test_claims_follow_the_static_items():
     """The per-XCD queues' claims start right after the static items: item
     G onwards one deep, 2 G onwards with a reserve (whose static second
@@ -236,9 +258,6 @@ def test_claims_follow_the_static_items():
         assert sorted(d[0] for d in done) == list(range(G))
         if not one_deep:
             assert sorted(d[1] for d in done) == list(range(G, 2 * G))
-        claimed = sorted(i for d in done for i in d[n_static_of(one_deep):] if i < n_local)
+        n_static = 1 if one_deep else 2
+        claimed = sorted(i for d in done for i in d[n_static:] if i < n_local)
         assert claimed[:nq] == list(range(first_claimed, first_claimed + nq))
-
-
-def n_static_of(one_deep):
-    return 1 if one_deep else 2
