@@ -43,9 +43,9 @@ METRIC = "paged-decode attention: KV bytes read GB/s (% of HBM peak); seq-heads/
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOADS = {"tiny-fp32": 1, "7b-decode-bf16": 2, "32k-gqa-bf16": 3,
-             "shared-prefix-bf16": 4, "fp8-kv": 5}
+             "shared-prefix-bf16": 4, "fp8-kv": 5, "shared-prefix-long-bf16": 6}
 DEFAULT_WORKLOAD = "7b-decode-bf16"
-DEFAULT_ALSO = "32k-gqa-bf16,shared-prefix-bf16,fp8-kv"
+DEFAULT_ALSO = "32k-gqa-bf16,shared-prefix-bf16,fp8-kv,shared-prefix-long-bf16"
 CPU_SHARE = 16   # host cores one GPU's jobs may use at most
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
 KERNEL_SOURCES = ("decode_valu.hip", "decode_mfma.hip", "pkv_device.h", "pkv_internal.h")

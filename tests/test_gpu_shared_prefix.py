@@ -54,6 +54,27 @@ def test_shared_prefix_workload_reduced():
         assert err <= TOL["bf16"], (ps, err)
 
 
+def test_long_prefix_workload_reduced():
+    """The long-prefix variant of the shared-prefix workload (the prefix
+    longer than the suffixes): the read-once call and the plain decode, both
+    against the oracle."""
+    w = workloads.make_config(6, reduced=True)
+    prefix = w.shared_blocks * w.block_size
+    assert prefix == workloads.LONG_PREFIX[True]
+    _say(f"case shared-prefix-long reduced S={w.S} prefix={prefix} lens={list(w.context_lens)}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle_decode(w, kc, vc, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    err = max_err(out_f64(dw.decode()), ref)
+    _say(f"  plain decode max_err={err:.3e}")
+    assert err <= TOL["bf16"], err
+    for ps in (0, 256):
+        err = max_err(out_f64(_shared(dw, prefix, ps)), ref)
+        _say(f"  read-once ps={ps} max_err={err:.3e}")
+        assert err <= TOL["bf16"], (ps, err)
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_random_shapes(seed):
     rng = np.random.default_rng(700 + seed)

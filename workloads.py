@@ -25,6 +25,9 @@ seed):
   4 shared-prefix    128 seqs, 512-token shared prefix + U[64,1024], 32/8 heads
   5 fp8-kv           256 seqs, lognormal(median 1024, sigma 1) clipped [16,8192],
                      40/8 heads, D 128, bs 16, e4m3 cache written from bf16
+  6 shared-prefix-long  workload 4 with an 8192-token shared prefix: a KV head's
+                     prefix (4 MiB of K and V) no longer fits the 4 MiB L2 of
+                     the XCD that serves it beside the suffixes
 """
 
 from dataclasses import dataclass, field
@@ -239,11 +242,19 @@ def config_lengths(cfg: int, rng: np.random.Generator, reduced: bool):
         z = rng.standard_normal(S)
         n = np.round(np.exp(np.log(1024.0) + z)).astype(np.int64)
         return np.clip(n, 16, 1200 if reduced else 8192)
+    if cfg == 6:
+        S = 5 if reduced else 128
+        hi = 300 if reduced else 1024
+        return LONG_PREFIX[reduced] + rng.integers(64 if not reduced else 1, hi + 1, size=S)
     raise ValueError(cfg)
 
 
+# Shared prefix of workload 6 (full size, reduced).
+LONG_PREFIX = {False: 8192, True: 1024}
+
+
 CONFIG_NAMES = {1: "tiny-fp32", 2: "7b-decode-bf16", 3: "32k-gqa-bf16",
-                4: "shared-prefix-bf16", 5: "fp8-kv"}
+                4: "shared-prefix-bf16", 5: "fp8-kv", 6: "shared-prefix-long-bf16"}
 
 
 def make_config(cfg: int, reduced: bool = False, seed: Optional[int] = None,
@@ -266,6 +277,9 @@ def make_config(cfg: int, reduced: bool = False, seed: Optional[int] = None,
     if cfg == 5:
         return build_workload(name, len(lens), 40, 8, 128, 16, "bf16", "fp8", lens, seed,
                               fill="write", layout_seed=layout_seed)
+    if cfg == 6:
+        return build_workload(name, len(lens), 32, 8, 128, 16, "bf16", "bf16", lens, seed,
+                              prefix_tokens=LONG_PREFIX[reduced], layout_seed=layout_seed)
     raise ValueError(cfg)
 
 
