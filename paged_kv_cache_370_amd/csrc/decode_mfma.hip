@@ -1253,13 +1253,13 @@ unsigned persistent_grid(long long items, int* young_from) {
 
 template <typename CT, int D, int BS, int MODE>
 hipError_t launch_mode(const DecodeArgs& a, const MfmaParams& p, long long items) {
-  // The sorted item order packs a context length into 31 - kSeqBits bits.
   // FP8 caches keep every workgroup claiming: with more vector work per
   // byte the youngest workgroup on a CU keeps a larger share (about 60% of
   // the oldest's rate, against a third with bf16 caches) and still adds
   // throughput after its first item.
   constexpr bool kStopYoung = Geometry<CT, D>::ELEM == 2;
   MfmaParams pl = p;
+  // The sorted item order packs a context length into 31 - kSeqBits bits.
   if (a.S <= kMaxScanSeqs && a.max_ctx < (1 << (31 - kSeqBits))) {
     const unsigned grid = persistent_grid<CT, D, BS, true, MODE>(items, &pl.young_from);
     if (!kStopYoung) pl.young_from = (int)grid;
