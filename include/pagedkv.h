@@ -270,7 +270,8 @@ size_t paged_attention_prefill_workspace_size(
  * shared, only page-aligned ones per its advice section).  The prefix is
  * read once per KV head for all sequences (rows = every sequence's query
  * heads of that KV head), each sequence's remaining positions as a decode
- * of its own, and the two merged per (sequence, head); the result is
+ * of its own, both in one launch (the prefix's items first), and the two
+ * merged per (sequence, head) by the split reduce; the result is
  * paged_attention_decode's.
  *   prefix_tokens: a multiple of block_size, at most max_context_len; the
  *   first prefix_tokens / block_size entries of every table must name the

@@ -363,7 +363,7 @@ pkv_status_t paged_attention_decode(void* out, const void* query, const void* ke
 // Shared-prefix decode: the prefix's partials (ceil(prefix / P) slots) come
 // before the suffix partitions' in every row; the prefix is cut into
 // partitions of the same P tokens.  (Cutting it finer for more parallel
-// items was measured slower: the prefix launch is not short of items.)
+// items was measured slower.)
 struct PrefixSplit {
   int P = -1, pre_slots = 0, suf_slots = 0;
 };
@@ -518,27 +518,21 @@ pkv_status_t paged_attention_decode_shared_prefix(
   }
   base.np_stride = sp.pre_slots + sp.suf_slots;
   base.force_partial = true;
-  // 1. The prefix once per KV head for all sequences: rows are the (sequence,
-  //    head) pairs, keys the prefix blocks of the first table.
-  DecodeArgs pre = base;
-  pre.S = 1;
-  pre.M = num_seqs;
-  pre.prefix_rows = prefix_tokens;
-  pre.max_ctx = prefix_tokens;
-  pre.NP = sp.pre_slots;
-  pre.slot_off = 0;
-  if (!decode_mfma_supported(pre)) return PKV_ERR_SHAPE;
-  pkv_status_t st = hip_status(launch_decode_mfma(pre));
+  // 1. One launch: the prefix once per KV head for all sequences (items
+  //    whose rows are the (sequence, head) pairs, keys the prefix blocks of
+  //    the first table), then each sequence's positions after the prefix,
+  //    as a decode of its own.
+  DecodeArgs one = base;
+  one.prefix_rows = prefix_tokens;
+  one.prefix_slots = sp.pre_slots;
+  one.len_off = prefix_tokens;  // the suffix items skip the prefix's table entries
+  one.max_ctx = max_context_len - prefix_tokens;
+  one.NP = sp.suf_slots;
+  one.slot_off = sp.pre_slots;
+  if (!decode_mfma_supported(one)) return PKV_ERR_SHAPE;
+  pkv_status_t st = hip_status(launch_decode_mfma(one));
   if (st != PKV_OK) return st;
-  // 2. Each sequence's positions after the prefix, as a decode of its own.
-  DecodeArgs suf = base;
-  suf.len_off = prefix_tokens;  // the kernel skips the prefix's table entries
-  suf.max_ctx = max_context_len - prefix_tokens;
-  suf.NP = sp.suf_slots;
-  suf.slot_off = sp.pre_slots;
-  st = hip_status(launch_decode_mfma(suf));
-  if (st != PKV_OK) return st;
-  // 3. Merge the prefix and suffix partials of every row.
+  // 2. Merge the prefix and suffix partials of every row.
   DecodeArgs red = base;
   red.NP = sp.pre_slots + sp.suf_slots;
   red.prefix_slots = sp.pre_slots;

@@ -108,8 +108,11 @@ struct MfmaParams {
   int tab_off;    // table entry of the launch's position 0 (len_off / bs)
   // Split attention over a shared prefix (zero / plain values otherwise):
   int len_off;        // positions below it are not this launch's: n = lens - len_off
-  int prefix;         // prefix-rows launch: the prefix length (the one "sequence")
-  int slot_off;       // partial slot of partition 0
+  int prefix;         // > 0: the launch also holds the prefix's items, first
+  int pre_items;      // items over the prefix: H_kv x pre_chunks x pre_slots
+  int pre_chunks;     // 16-row chunks of the prefix's rows, the S x G (sequence, head) pairs
+  int pre_slots;      // partial slots of the prefix (its partitions), slots 0 .. of a row
+  int slot_off;       // partial slot of partition 0 (of the positions after the prefix)
   int np_stride;      // partial slots per row
   int force_partial;  // write partials even when a context fits one partition
   int young_from;  // first workgroup that runs only its first item
@@ -117,14 +120,17 @@ struct MfmaParams {
 };
 
 // Item kinds of a launch: one query token per sequence; several causal
-// tokens per sequence; rows that are the (sequence, head) pairs of all
-// sequences over a prefix whose blocks every table shares; or one token per
-// sequence over the positions after that prefix.  The split parameters are
-// read only by the last two, so the others keep their scalar registers.
-enum : int { kModeDecode = 0, kModeCausal = 1, kModePrefixRows = 2, kModeSuffix = 3 };
+// tokens per sequence; or a prefix whose blocks every table shares read once
+// for all sequences, with one token per sequence over the positions after
+// it.  That last kind holds two sorts of items: the prefix's, whose rows are
+// the (sequence, head) pairs of all sequences of a KV head (each masked at
+// its sequence's length), first, then each sequence's own positions; both
+// leave partials that the split reduce merges.  The split parameters are
+// read only by that kind, so the others keep their scalar registers.
+enum : int { kModeDecode = 0, kModeCausal = 1, kModeSplitPrefix = 3 };
 
 template <int MODE>
-constexpr bool kSplit = MODE == kModePrefixRows || MODE == kModeSuffix;
+constexpr bool kSplit = MODE == kModeSplitPrefix;
 
 // Context length the launch sees for sequence i.
 // A length above the launch's bound (a broken caller contract) is cut to
@@ -132,8 +138,7 @@ constexpr bool kSplit = MODE == kModePrefixRows || MODE == kModeSuffix;
 // workspace were sized for.
 template <int MODE>
 __device__ __forceinline__ int seq_len(const MfmaParams& p, int i) {
-  if constexpr (MODE == kModePrefixRows) return p.prefix;
-  if constexpr (MODE == kModeSuffix) return min(max(0, p.lens[i] - p.len_off), p.max_ctx);
+  if constexpr (MODE == kModeSplitPrefix) return min(max(0, p.lens[i] - p.len_off), p.max_ctx);
   return min(p.lens[i], p.max_ctx);
 }
 
@@ -208,15 +213,22 @@ struct Src {
 // An item covers nh <= 16 consecutive rows from r0.
 struct Part {
   int seq, kvh, r0, nh, start, end, first_blk;
+  int pre;  // an item over the shared prefix (split-prefix launches; 0 otherwise)
 };
 
 // Index of a row's [D] vector in q / out ([S][M][H][D]) and of its partial.
 template <int MODE>
 __device__ __forceinline__ size_t row_of(const MfmaParams& p, const Part& w, int rho) {
-  if constexpr (MODE == kModeCausal || MODE == kModePrefixRows) {
+  if constexpr (MODE == kModeCausal) {
     const int m = rho / p.G;
     return ((size_t)w.seq * p.M + m) * p.H + (size_t)w.kvh * p.G + (rho - m * p.G);
   } else {
+    if constexpr (MODE == kModeSplitPrefix) {
+      if (w.pre) {  // row rho of a prefix item: head rho % G of sequence rho / G
+        const int sq = rho / p.G;
+        return (size_t)sq * p.H + (size_t)w.kvh * p.G + (rho - sq * p.G);
+      }
+    }
     return (size_t)w.seq * p.H + (size_t)w.kvh * p.G + rho;
   }
 }
@@ -674,6 +686,29 @@ template <int BS, bool SCAN, int MODE>
 __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y, int n_full,
                                             const Order& o) {
   Item it;
+  it.w.pre = 0;
+  if constexpr (MODE == kModeSplitPrefix) {
+    // Items [0, pre_items) are the prefix's: KV head x 16-row chunk of the
+    // S x G rows (fastest) and prefix partition, over sequence 0's table
+    // (every table holds the prefix's blocks).
+    if (item < p.pre_items) {
+      const int Yp = p.H_kv * p.pre_chunks;
+      const int y = item % Yp;
+      it.part = item / Yp;
+      it.n = p.prefix;
+      it.live = true;
+      it.w.pre = 1;
+      it.w.seq = 0;
+      it.w.kvh = y / p.pre_chunks;
+      it.w.r0 = (y - it.w.kvh * p.pre_chunks) * 16;
+      it.w.nh = min(16, p.S * p.G - it.w.r0);
+      it.w.start = it.part * p.P;
+      it.w.end = min(it.n, it.w.start + p.P);
+      it.w.first_blk = it.w.start / BS;
+      return it;
+    }
+    item -= p.pre_items;
+  }
   const int y = item % Y;
   const int rest = item / Y;
   int seq;
@@ -729,11 +764,13 @@ __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y
 // never used; a suffix launch's positions start tab_off entries into the
 // row, and the clamp keeps every read inside the row.  Plain loads: the compiler tracks them exactly, so they never
 // force a wait on the chunk pipeline.
-template <typename CT, int D, int BS>
+template <typename CT, int D, int BS, int MODE>
 __device__ __forceinline__ int fetch_tab(const MfmaParams& p, const Part& w, int wave, int lane) {
   constexpr int EPC = Geometry<CT, D>::CHUNK / BS;
   const int blk = w.first_blk + (wave + kNW * (lane / EPC)) * EPC + lane % EPC;
-  return p.tables[(size_t)w.seq * p.max_blocks + min(p.tab_off + blk, p.max_blocks - 1)];
+  // a prefix item's positions start at 0
+  const int off = MODE == kModeSplitPrefix && w.pre ? 0 : p.tab_off;
+  return p.tables[(size_t)w.seq * p.max_blocks + min(off + blk, p.max_blocks - 1)];
 }
 
 __device__ __forceinline__ void store_tab(int tab, int* wtab, int lane) {
@@ -871,6 +908,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   const int lane = tid & 63;
   const int q = lane >> 4, r = lane & 15;
   const int Y = p.H_kv * p.chunks;
+  // Items over a shared prefix, numbered before the others (split-prefix
+  // launches).
+  const int n_pre = MODE == kModeSplitPrefix ? p.pre_items : 0;
 
   // Items [0, n_local) form the per-XCD queues: queue `queue` holds items
   // k * nq + queue.  Workgroup b starts with item b (no atomic traffic at
@@ -924,10 +964,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   if constexpr (SCAN) {
     n_full = full_offsets(p, s_full, s_red, len);  // has barriers: s_next is visible
     const int first = __builtin_amdgcn_readfirstlane(s_next[0]);
-    early = first < Y * n_full;
+    if constexpr (MODE == kModeSplitPrefix)
+      early = first >= n_pre && first - n_pre < Y * n_full;
+    else
+      early = first < Y * n_full;
     if (early) {
       it = decode_item<BS, SCAN, MODE>(p, first, Y, n_full, order);
-      tab_first = fetch_tab<CT, D, BS>(p, it.w, wave, lane);
+      tab_first = fetch_tab<CT, D, BS, MODE>(p, it.w, wave, lane);
       q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
       store_tab(tab_first, s_wtab[wave], lane);  // the wave's own slice
       wave_lds_sync();
@@ -941,9 +984,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     int n_rag;
     // has barriers; s_raw is free until the first chunk's V rows are stored
     build_offsets<MODE, BS>(p, s_rag, s_seq, s_red, reinterpret_cast<int*>(s_raw), len, &n_rag);
-    total = Y * (n_full + n_rag);
+    total = Y * (n_full + n_rag) + n_pre;
   } else {
-    total = Y * p.S * p.NP;
+    total = n_pre + Y * p.S * p.NP;
     __syncthreads();
   }
   // About one shared item per workgroup, and never so many that a static
@@ -961,7 +1004,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   // memory round trip before the first chunk's loads, not two).
   if (!early) {
     it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, order);
-    tab_first = fetch_tab<CT, D, BS>(p, it.w, wave, lane);
+    tab_first = fetch_tab<CT, D, BS, MODE>(p, it.w, wave, lane);
     q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
   }
   if (cur < total) {
@@ -1017,12 +1060,14 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       const int base = it.n - p.M + 1;  // end of token 0's row
       row_end = min(it.w.end, base + (it.w.r0 + r) / p.G);
       full_end = min(it.w.end, base + it.w.r0 / p.G);
-    } else if constexpr (MODE == kModePrefixRows) {
-      // Row r belongs to sequence (r0 + r) / G, which sees the prefix only
-      // up to its own length.
-      const int sq = min((it.w.r0 + r) / p.G, p.M - 1);
-      row_end = min(it.w.end, p.lens[sq]);
-      full_end = __all(row_end >= it.w.end) ? it.w.end : it.w.start;
+    } else if constexpr (MODE == kModeSplitPrefix) {
+      if (it.w.pre) {
+        // Row r of a prefix item belongs to sequence (r0 + r) / G, which
+        // sees the prefix only up to its own length.
+        const int sq = min((it.w.r0 + r) / p.G, p.S - 1);
+        row_end = min(it.w.end, p.lens[sq]);
+        full_end = __all(row_end >= it.w.end) ? it.w.end : it.w.start;
+      }
     }
     int ci = wave;
     do {
@@ -1107,7 +1152,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     const bool merge_prev =
         pg >= 0 && __builtin_amdgcn_readfirstlane(s_red[0] | s_red[1] | s_red[2] | s_red[3]);
     const Item ni = decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, order);
-    const int tab_nn = fetch_tab<CT, D, BS>(p, ni.w, wave, lane);
+    const int tab_nn = fetch_tab<CT, D, BS, MODE>(p, ni.w, wave, lane);
     const uint4 q_nn = fetch_q<CT, D, MODE>(p, ni.w, tid);
 
     // Thread t merges 4 consecutive d of one head: one 16-byte LDS read per
@@ -1143,7 +1188,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * D + d) =
               make_uint2(pack_bf16x2(ox, oy), pack_bf16x2(oz, ow));
         } else {
-          const size_t pi = kSplit<MODE> ? row * p.np_stride + it.part + p.slot_off
+          const size_t pi = kSplit<MODE> ? row * p.np_stride + it.part + (it.w.pre ? 0 : p.slot_off)
                                          : row * p.NP + it.part;
           // bf16 partial output (the result is rounded to bf16 anyway);
           // streaming store: the reduce kernel reads the partial once.
@@ -1288,12 +1333,15 @@ hipError_t launch_bs(const DecodeArgs& a) {
   p.max_ctx = a.max_ctx;
   p.tab_off = a.len_off / a.bs;
   p.len_off = a.len_off; p.prefix = a.prefix_rows; p.slot_off = a.slot_off;
+  p.pre_chunks = (a.S * p.G + 15) / 16;
+  p.pre_slots = a.prefix_rows > 0 ? a.prefix_slots : 0;
+  p.pre_items = a.H_kv * p.pre_chunks * p.pre_slots;
   p.np_stride = a.np_stride > 0 ? a.np_stride : a.NP;
   p.force_partial = a.force_partial ? 1 : 0;
   p.scale_log2 = a.scale * kLog2e;
-  const long long items = (long long)a.H_kv * p.chunks * a.S * a.NP;
-  if (a.prefix_rows > 0) return launch_mode<CT, D, BS, kModePrefixRows>(a, p, items);
-  if (a.len_off > 0 || a.force_partial) return launch_mode<CT, D, BS, kModeSuffix>(a, p, items);
+  const long long items = (long long)a.H_kv * p.chunks * a.S * a.NP + p.pre_items;
+  if (a.prefix_rows > 0 || a.len_off > 0 || a.force_partial)
+    return launch_mode<CT, D, BS, kModeSplitPrefix>(a, p, items);
   return a.M > 1 ? launch_mode<CT, D, BS, kModeCausal>(a, p, items)
                  : launch_mode<CT, D, BS, kModeDecode>(a, p, items);
 }

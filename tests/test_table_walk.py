@@ -62,13 +62,13 @@ def test_plain_decode_reads_stay_in_the_table(cfg):
     assert np.array_equal(needs, served)
 
 
-def test_shared_prefix_launches_read_inside_the_table():
+def test_shared_prefix_items_read_inside_the_table():
     lens, bs, max_blocks = _lengths(4)        # 128 sequences, 512-token prefix, bs 16
     prefix, P = 512, 512
-    # prefix launch: sequence 0's table, the prefix positions only
+    # prefix items: sequence 0's table, the prefix positions only
     reads, needs, served = _reads([prefix], max_blocks, bs, P, 0, [0])
     assert reads.max() < max_blocks and np.array_equal(needs, served)
-    # suffix launch: every sequence's positions after the prefix, entries
+    # suffix items: every sequence's positions after the prefix, entries
     # offset by the prefix's blocks
     tab_off = prefix // bs
     reads, needs, served = _reads(lens - prefix, max_blocks, bs, P, tab_off, range(len(lens)))
@@ -76,8 +76,8 @@ def test_shared_prefix_launches_read_inside_the_table():
     assert np.array_equal(needs, served)
 
 
-def test_suffix_launch_of_contexts_ending_at_the_prefix():
-    """Tables no longer than the prefix: the suffix launch's items are empty,
+def test_suffix_items_of_contexts_ending_at_the_prefix():
+    """Tables no longer than the prefix: the suffix items are empty,
     and the clamp keeps the reads on the row's last entry."""
     bs, prefix, max_blocks = 16, 64, 4
     reads, needs, served = _reads(np.array([0, 0, 0]), max_blocks, bs, 512, prefix // bs,
