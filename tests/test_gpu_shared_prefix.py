@@ -109,6 +109,33 @@ def test_random_shapes(seed):
     assert np.all(out[short == 0] == 0)
 
 
+@pytest.mark.parametrize("cache,G,S", [("bf16", 20, 6), ("fp8", 40, 3), ("bf16", 1, 520)])
+def test_wide_groups_and_long_batches(cache, G, S):
+    """Query-head groups wider than 16 (a sequence's heads split across the
+    prefix items' 16-row chunks, and the suffix items' row groups), and a
+    batch past the 512 sequences the kernel sorts in LDS (its plain item
+    order)."""
+    rng = np.random.default_rng(1100 + G)
+    bs, H_kv = 16, 2 if G < 40 else 1
+    prefix = 3 * bs
+    lens = prefix + rng.integers(1, 200, size=S)
+    w = workloads.build_workload(f"shared-wide-{cache}-G{G}-S{S}", S, H_kv * G, H_kv, 64, bs,
+                                 "bf16", cache, lens, 1110 + G, prefix_tokens=prefix,
+                                 fill="write" if cache == "fp8" else "random")
+    short = w.context_lens.copy()
+    short[0] = prefix - 5                    # shorter than the prefix
+    w.context_lens = short
+    _say(f"case shared wide cache={cache} G={G} S={S} prefix={prefix}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle_decode(w, kc, vc, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    for ps in (0, 32):
+        err = max_err(out_f64(_shared(dw, prefix, ps)), ref)
+        _say(f"  ps={ps} max_err={err:.3e}")
+        assert err <= TOL[cache], (ps, err)
+
+
 def test_zero_prefix_is_decode():
     w = workloads.make_config(2, reduced=True)
     dw = DeviceWorkload(w)
