@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", default="prefill-chunk-gqa-bf16",
                     help="chunked-prefill workload timed beside the decode step ('none': skip)")
+    ap.add_argument("--prefill-also", default="prefill-chunk-gqa-fp8",
+                    help="comma-separated further chunked-prefill workloads ('none': skip)")
     ap.add_argument("--beam-fork", default="beam-fork-gqa-bf16",
                     help="multi-query step over forked tables timed beside the decode step "
                          "('none': skip)")
@@ -534,6 +536,13 @@ def main():
     if args.prefill != "none":
         progress(f"prefill {args.prefill}")
         result["prefill"] = prefill_bench(pkv, torch, args.prefill, args.steps)
+        extra = [x for x in args.prefill_also.split(",") if x and x not in ("none", args.prefill)]
+        if extra:
+            result["prefill_workloads"] = {}
+        for name in extra:
+            progress(f"prefill {name}")
+            result["prefill_workloads"][name] = prefill_bench(pkv, torch, name, args.steps)
+            torch.cuda.empty_cache()
     if args.beam_fork != "none":
         progress(f"beams over forked tables {args.beam_fork}")
         result["beam_fork"] = beam_fork_bench(pkv, torch, args.beam_fork, args.steps)
@@ -611,20 +620,29 @@ def prefill_bench(pkv, torch, name, reps):
         return torch.from_numpy(a).to(dev)
 
     q, kc, vc = t(w.q), t(w.key_cache), t(w.value_cache)
+    ks = t(w.key_scale) if w.key_scale is not None else None
+    vs = t(w.value_scale) if w.value_scale is not None else None
     tables, lens = t(w.block_tables), t(w.context_lens)
-    key, value, slots = (t(x) for x in w.writes[-1])
+    writes = [tuple(t(x) for x in wr) for wr in w.writes]
+    key, value, slots = writes[-1]
     out = torch.empty_like(q)
     M = w.query_tokens
+    cc = pkv.dtype_code(kc)
     need = pkv.prefill_workspace_size(w.S, M, w.H, w.H_kv, w.D, w.block_size, w.max_context_len,
-                                      1, 1, 0)
+                                      1, cc, 0)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    wws_bytes = pkv.write_workspace_size(max(len(x[2]) for x in writes), w.H_kv, w.num_blocks, cc)
+    wws = torch.empty(wws_bytes, dtype=torch.uint8, device=dev) if wws_bytes else None
+    # FP8 caches: the positions before the chunk are written once, untimed
+    for k, v, s in writes[:-1]:
+        pkv.paged_kv_cache_write(k, v, kc, vc, s, ks, vs, workspace=wws)
 
     def attn():
-        pkv.paged_attention_prefill(out, q, kc, vc, tables, lens, w.max_context_len, w.scale,
-                                    workspace=ws)
+        pkv.paged_attention_prefill(out, q, kc, vc, tables, lens, w.max_context_len, w.scale, ks,
+                                    vs, workspace=ws)
 
     def step():
-        pkv.paged_kv_cache_write(key, value, kc, vc, slots)
+        pkv.paged_kv_cache_write(key, value, kc, vc, slots, ks, vs, workspace=wws)
         attn()
 
     def timed(fn):
@@ -645,6 +663,7 @@ def prefill_bench(pkv, torch, name, reps):
     tflops = flops / (attn_ms * 1e-3) / 1e12
     return {"workload": w.name, "seqs": w.S, "chunk_tokens": M, "q_heads": w.H,
             "kv_heads": w.H_kv, "head_size": w.D, "block_size": w.block_size,
+            "cache": w.cache_dtype,
             "context": int(w.max_context_len), "workspace_bytes": need,
             "flops_per_step": flops, "ms_per_step": round(step_ms, 5),
             "tokens_per_s": round(w.S * M / (step_ms * 1e-3), 1),
@@ -654,7 +673,9 @@ def prefill_bench(pkv, torch, name, reps):
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": recorded_traffic(w.name, PREFILL_SOURCES),
-                         "kernel": "tiled prefill kernel",
+                         "kernel": "tiled prefill kernel" + (
+                             " (after the FP8 stage to bf16, timed with it)"
+                             if w.cache_dtype == "fp8" else ""),
                          "kernel_sources": kernel_source_hash(PREFILL_SOURCES)}}
 
 
@@ -698,20 +719,29 @@ def beam_fork_bench(pkv, torch, name, reps):
         return torch.from_numpy(a).to(dev)
 
     q, kc, vc = t(w.q), t(w.key_cache), t(w.value_cache)
+    ks = t(w.key_scale) if w.key_scale is not None else None
+    vs = t(w.value_scale) if w.value_scale is not None else None
     tables, lens = t(w.block_tables), t(w.context_lens)
-    key, value, slots = (t(x) for x in w.writes[-1])
+    writes = [tuple(t(x) for x in wr) for wr in w.writes]
+    key, value, slots = writes[-1]
     out = torch.empty_like(q)
     M = w.query_tokens
+    cc = pkv.dtype_code(kc)
     need = pkv.prefill_workspace_size(w.S, M, w.H, w.H_kv, w.D, w.block_size, w.max_context_len,
-                                      1, 1, 0)
+                                      1, cc, 0)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    wws_bytes = pkv.write_workspace_size(max(len(x[2]) for x in writes), w.H_kv, w.num_blocks, cc)
+    wws = torch.empty(wws_bytes, dtype=torch.uint8, device=dev) if wws_bytes else None
+    # FP8 caches: the positions before the chunk are written once, untimed
+    for k, v, s in writes[:-1]:
+        pkv.paged_kv_cache_write(k, v, kc, vc, s, ks, vs, workspace=wws)
 
     def attn():
-        pkv.paged_attention_prefill(out, q, kc, vc, tables, lens, w.max_context_len, w.scale,
-                                    workspace=ws)
+        pkv.paged_attention_prefill(out, q, kc, vc, tables, lens, w.max_context_len, w.scale, ks,
+                                    vs, workspace=ws)
 
     def step():
-        pkv.paged_kv_cache_write(key, value, kc, vc, slots)
+        pkv.paged_kv_cache_write(key, value, kc, vc, slots, ks, vs, workspace=wws)
         attn()
 
     def timed(fn):

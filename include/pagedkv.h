@@ -237,11 +237,17 @@ pkv_status_t paged_attention_decode_reduce(
  *   2^31 (PKV_ERR_SHAPE otherwise).  Other arguments, partitions and the
  *   workspace (paged_attention_prefill_workspace_size bytes, its first 4096
  *   zero) are as for paged_attention_decode, except the library's choice
- *   (partition_size 0): long chunks (M * G >= 64 over a bf16 cache) split a
- *   context only when the grid would leave CUs idle; other calls keep
- *   whole contexts (up to 256 blocks) when there are at least 512
- *   (sequence, KV head, 16-row) items, and otherwise split them as decode
- *   does.
+ *   (partition_size 0): long chunks (M * G >= 64) split a context only
+ *   when the grid would leave CUs idle; other calls keep whole contexts (up
+ *   to 256 blocks) when there are at least 512 (sequence, KV head, 16-row)
+ *   items, and otherwise split them as decode does.
+ *   Long chunks over an FP8 cache: the blocks the sequences reach are first
+ *   dequantised (code * scale, float32, rounded to bf16) into a bf16 pool
+ *   inside the workspace, which therefore also holds, after the partials,
+ *   a table of S * ceil(max_context_len / block_size) int32 entries and two
+ *   pools of that many blocks (K and V, [H_kv][bs][D] bf16 each); S *
+ *   ceil(max_context_len / block_size) must stay below 2^31.  The workspace
+ *   size function includes them.
  */
 pkv_status_t paged_attention_prefill(
     void* out, const void* query,

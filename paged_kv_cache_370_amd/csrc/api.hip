@@ -386,10 +386,10 @@ static size_t shared_prefix_workspace(int S, int H, int D, const PrefixSplit& sp
 }
 
 // Which kernel serves a multi-token call, and its partition size.  Long
-// chunks (at least kTileMinRows (token, head) rows per KV head) over a bf16
-// cache run on the tiled prefill kernel; short ones (and FP8 caches) on the
-// decode kernel's multi-token mode, whose 16-row tiles suit the HBM-bound
-// case.  The tiled kernel's own partition choice keeps whole contexts in one
+// chunks (at least kTileMinRows (token, head) rows per KV head) run on the
+// tiled prefill kernel (an FP8 cache staged to bf16 first); short ones on
+// the decode kernel's multi-token mode, whose 16-row tiles suit the
+// HBM-bound case.  The tiled kernel's own partition choice keeps whole contexts in one
 // partition unless the grid would leave CUs idle (two workgroups per CU on
 // 256 CUs), in partitions of at least 512 keys.
 constexpr int kTileMinRows = 64;
@@ -407,7 +407,7 @@ static PrefillPlan prefill_plan(int S, int M, int H, int H_kv, int D, int bs, in
       q != PKV_BF16)
     return pl;
   const long long rows = (long long)M * (H / H_kv);
-  pl.tiled = c == PKV_BF16 && rows >= kTileMinRows;
+  pl.tiled = rows >= kTileMinRows;
   if (!pl.tiled) {
     // Several tokens per sequence on the decode kernel: an item's partial
     // output is M * G rows wide, so with enough items to give every CU two
@@ -442,6 +442,27 @@ static PrefillPlan prefill_plan(int S, int M, int H, int H_kv, int D, int bs, in
   return pl;
 }
 
+// The FP8 stage after the tiled kernel's workspace: the pool's table
+// ([S][nb] int32), then the bf16 K and V pools of S * nb blocks each.  Pool
+// block ids are 32-bit.
+struct StageLayout {
+  int nb = 0;
+  size_t tab = 0, pool = 0;  // bytes of the table and of one pool
+  size_t bytes() const { return tab + 2 * pool; }
+};
+
+static StageLayout stage_layout(int S, int H_kv, int D, int bs, int max_ctx) {
+  StageLayout l;
+  l.nb = (max_ctx + bs - 1) / bs;
+  if ((long long)S * l.nb >= (1LL << 31)) {
+    l.nb = -1;
+    return l;
+  }
+  l.tab = align256((size_t)S * l.nb * sizeof(int32_t));
+  l.pool = align256((size_t)S * l.nb * H_kv * bs * D * 2);
+  return l;
+}
+
 pkv_status_t paged_attention_prefill(void* out, const void* query, const void* key_cache,
                                      const void* value_cache, const float* key_scale,
                                      const float* value_scale, const int32_t* block_tables,
@@ -468,7 +489,27 @@ pkv_status_t paged_attention_prefill(void* out, const void* query, const void* k
                                true, num_query_tokens);
   if (s.status != PKV_OK || s.empty) return s.status;
   pkv_status_t st;
-  if (plan.tiled) {
+  if (plan.tiled && cache_dtype == PKV_FP8_E4M3) {
+    const StageLayout sl =
+        stage_layout(num_seqs, num_kv_heads, head_size, block_size, max_context_len);
+    if (sl.nb < 0) return PKV_ERR_SHAPE;
+    const size_t base = decode_workspace(num_seqs, num_heads, head_size, max_context_len,
+                                         plan.P, num_query_tokens);
+    if (workspace_bytes < base + sl.bytes()) return PKV_ERR_WORKSPACE;
+    char* ws = reinterpret_cast<char*>(workspace) + base;
+    PrefillStage stage{ws + sl.tab, ws + sl.tab + sl.pool, reinterpret_cast<int32_t*>(ws),
+                       sl.nb};
+    DecodeArgs t = s.a;  // the tiled kernel's view: the bf16 pool and its table
+    t.key_cache = stage.key_pool;
+    t.value_cache = stage.value_pool;
+    t.key_scale = t.value_scale = nullptr;
+    t.tables = stage.tables;
+    t.max_blocks = sl.nb;
+    t.cache_dtype = PKV_BF16;
+    if (!prefill_mfma_supported(t)) return PKV_ERR_SHAPE;
+    st = hip_status(launch_prefill_stage_fp8(s.a, stage));
+    if (st == PKV_OK) st = hip_status(launch_prefill_mfma(t));
+  } else if (plan.tiled) {
     if (!prefill_mfma_supported(s.a)) return PKV_ERR_SHAPE;
     st = hip_status(launch_prefill_mfma(s.a));
   } else {
@@ -567,8 +608,12 @@ size_t paged_attention_prefill_workspace_size(int32_t num_seqs, int32_t num_quer
                                         head_size, block_size, max_context_len, q_dtype,
                                         cache_dtype, partition_size);
   if (plan.P <= 0) return 0;
-  return decode_workspace(num_seqs, num_heads, head_size, max_context_len, plan.P,
-                          num_query_tokens);
+  const size_t base =
+      decode_workspace(num_seqs, num_heads, head_size, max_context_len, plan.P, num_query_tokens);
+  if (!plan.tiled || cache_dtype != PKV_FP8_E4M3) return base;
+  const StageLayout sl = stage_layout(num_seqs, num_kv_heads, head_size, block_size,
+                                      max_context_len);
+  return sl.nb < 0 ? 0 : base + sl.bytes();
 }
 
 }  // extern "C"

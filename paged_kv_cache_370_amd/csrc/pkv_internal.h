@@ -91,12 +91,24 @@ bool decode_mfma_supported(const DecodeArgs& a);
 hipError_t launch_decode_mfma(const DecodeArgs& a);
 hipError_t launch_decode_reduce(const DecodeArgs& a);
 
-// Tiled multi-token kernel (long prefill chunks, bf16 cache): a workgroup
-// owns prefill_tile_rows() rows of one KV head and stages one partition's
-// block ids in LDS, at most kPrefillMaxTable of them.
+// Tiled multi-token kernel (long prefill chunks, bf16 cache, or an FP8 cache
+// staged to bf16 first): a workgroup owns prefill_tile_rows() rows of one KV
+// head and stages one partition's block ids in LDS, at most kPrefillMaxTable
+// of them.
 constexpr int kPrefillMaxTable = 1024;
 int prefill_tile_rows();
 bool prefill_mfma_supported(const DecodeArgs& a);
 hipError_t launch_prefill_mfma(const DecodeArgs& a);
+
+// FP8 caches on the tiled kernel: the blocks the sequences reach, dequantised
+// to bf16 into a pool of S * nb blocks (nb = ceil(max_ctx / bs)), pool block
+// s * nb + j holding logical block j of sequence s, named by tables[s][j].
+struct PrefillStage {
+  void* key_pool;    // [S * nb][H_kv][bs][D] bf16
+  void* value_pool;
+  int32_t* tables;   // [S][nb]
+  int nb;
+};
+hipError_t launch_prefill_stage_fp8(const DecodeArgs& a, const PrefillStage& st);
 
 }  // namespace pkv

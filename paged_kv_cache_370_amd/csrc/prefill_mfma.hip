@@ -67,6 +67,19 @@ struct PrefillParams {
   float scale_log2;
 };
 
+struct StageParams {
+  const uint8_t* kc;  // [num_blocks][H_kv][bs][D] E4M3FN codes
+  const uint8_t* vc;
+  const float* ks;    // [num_blocks][H_kv]
+  const float* vs;
+  const int32_t* tables;
+  const int32_t* lens;
+  uint16_t* sk;       // [S * nb][H_kv][bs][D] bf16 pool
+  uint16_t* sv;
+  int32_t* staged_tab;  // [S][nb]
+  int H_kv, D, bs, max_blocks, max_ctx, nb;
+};
+
 __device__ __forceinline__ bf16x8_v to_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_v, v); }
 
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
@@ -417,7 +430,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
   const int kend = min(pend, base + rlast / p.G);
   const bool single = n <= p.P;
   const int nch = kend > start ? (kend - start + kKC - 1) / kKC : 0;
-  if (nch == 0 && !single) return;  // no row of the tile sees this partition
+  // A context within one partition is finished by partition 0 alone (the
+  // split reduce skips it); otherwise a partition no row of the tile sees
+  // has nothing to add.
+  if (single ? part > 0 : nch == 0) return;
 
   const int t0 = start / BS;
   const int elast = nch > 0 ? (kend - 1) / BS - t0 : 0;  // last table entry used
@@ -586,6 +602,53 @@ hipError_t launch_d(const DecodeArgs& a) {
   }
 }
 
+// FP8 caches on the tiled kernel.  Its K and V rows travel from HBM to LDS
+// by DMA, with no register step to decode them in, so a call over an FP8
+// cache first dequantises the blocks its sequences reach into a bf16 pool
+// (one pool block per (sequence, logical block)) with a table of its own,
+// and the tiled kernel runs on that.  Each element becomes the bf16 nearest
+// to code * scale[block][KV head] (the dequantisation of the FP8 block
+// storage: dpshk.com article, section 3.2), computed in float32.
+// Workgroup w stages logical block j = w % nb of sequence w / nb: table
+// entry w names pool block w; blocks at or past the sequence's length are
+// left unwritten (the tiled kernel reads no position at or past it).
+__global__ __launch_bounds__(256) void stage_fp8_kernel(StageParams p) {
+  const int w = blockIdx.x;
+  const int seq = w / p.nb;
+  const int j = w - seq * p.nb;
+  if (threadIdx.x == 0) p.staged_tab[w] = w;
+  const int n = min(p.lens[seq], p.max_ctx);
+  if (j * p.bs >= n) return;
+  const int b = p.tables[(size_t)seq * p.max_blocks + j];
+  const int per_head = p.bs * p.D;  // codes per (block, KV head), a multiple of 16
+  const size_t per_block = (size_t)p.H_kv * per_head;
+  const uint4* src[2] = {reinterpret_cast<const uint4*>(p.kc + (size_t)b * per_block),
+                         reinterpret_cast<const uint4*>(p.vc + (size_t)b * per_block)};
+  uint4* dst[2] = {reinterpret_cast<uint4*>(p.sk + (size_t)w * per_block),
+                   reinterpret_cast<uint4*>(p.sv + (size_t)w * per_block)};
+  const float* sc[2] = {p.ks + (size_t)b * p.H_kv, p.vs + (size_t)b * p.H_kv};
+  const int pieces = (int)(per_block / 16);
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    for (int i = threadIdx.x; i < pieces; i += 256) {
+      const uint4 c = src[kv][i];
+      const float s = sc[kv][(16 * i) / per_head];
+      const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float f0, f1, f2, f3;
+        fp8x2_to_f32<false>(cw[e], f0, f1);
+        fp8x2_to_f32<true>(cw[e], f2, f3);
+        o[2 * e] = bf16x2_rne(f0 * s, f1 * s);
+        o[2 * e + 1] = bf16x2_rne(f2 * s, f3 * s);
+      }
+      dst[kv][2 * i] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[kv][2 * i + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
 }  // namespace
 
 int prefill_tile_rows() { return kBM; }
@@ -598,6 +661,23 @@ bool prefill_mfma_supported(const DecodeArgs& a) {
 hipError_t launch_prefill_mfma(const DecodeArgs& a) {
   if (a.S == 0) return hipSuccess;
   return a.D == 128 ? launch_d<128>(a) : launch_d<64>(a);
+}
+
+hipError_t launch_prefill_stage_fp8(const DecodeArgs& a, const PrefillStage& st) {
+  if (a.S == 0) return hipSuccess;
+  StageParams p;
+  p.kc = reinterpret_cast<const uint8_t*>(a.key_cache);
+  p.vc = reinterpret_cast<const uint8_t*>(a.value_cache);
+  p.ks = a.key_scale; p.vs = a.value_scale;
+  p.tables = a.tables; p.lens = a.lens;
+  p.sk = reinterpret_cast<uint16_t*>(st.key_pool);
+  p.sv = reinterpret_cast<uint16_t*>(st.value_pool);
+  p.staged_tab = st.tables;
+  p.H_kv = a.H_kv; p.D = a.D; p.bs = a.bs; p.max_blocks = a.max_blocks; p.max_ctx = a.max_ctx;
+  p.nb = st.nb;
+  const unsigned grid = (unsigned)((long long)a.S * st.nb);
+  hipLaunchKernelGGL(stage_fp8_kernel, dim3(grid), dim3(256), 0, a.stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace pkv

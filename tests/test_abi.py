@@ -209,6 +209,24 @@ def test_prefill_workspace_grows_with_tokens():
     assert pkv.prefill_workspace_size(4, 0, 8, 2, 128, 16, 3000, 1, 1, 512) == 0
 
 
+def test_prefill_fp8_stage_workspace():
+    """A long chunk over an FP8 cache needs, after the tiled kernel's own
+    workspace, the bf16 pool it is staged into: a table of S x ceil(max_ctx /
+    bs) int32 entries, then K and V pools of that many blocks."""
+    bf16 = pkv.prefill_workspace_size(4, 16, 8, 2, 128, 16, 3000, 1, 1, 512)  # 64 rows: tiled
+    nb = (3000 + 15) // 16
+    tab = (4 * nb * 4 + 255) // 256 * 256
+    pool = (4 * nb * 2 * 16 * 128 * 2 + 255) // 256 * 256
+    assert pkv.prefill_workspace_size(4, 16, 8, 2, 128, 16, 3000, 1, 2, 512) == bf16 + tab + 2 * pool
+    # short chunks (fewer than 64 rows per KV head) read FP8 in the decode kernel: no pool
+    assert (pkv.prefill_workspace_size(4, 15, 8, 2, 128, 16, 3000, 1, 2, 512) ==
+            pkv.prefill_workspace_size(4, 15, 8, 2, 128, 16, 3000, 1, 1, 512))
+    # the tiled kernel's part alone is too small; nothing is launched
+    big = dict(S=4, M=16, max_ctx=3000, max_blocks=188, ps=512, ws=FAKE)
+    assert _prefill(cd=2, ks=FAKE, vs=FAKE, wsb=bf16 + tab + 2 * pool - 1, **big) == 4
+    assert _prefill(cd=1, wsb=bf16 - 1, **big) == 4
+
+
 def _shared(**kw):
     a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None, tables=FAKE, lens=FAKE, pre=64,
              S=2, H=8, H_kv=2, D=128, bs=16, max_blocks=64, max_ctx=1000, scale=0.1, qd=1, cd=1,

@@ -101,6 +101,63 @@ def test_tiled_shapes(seed):
     assert err <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_tiled_fp8_shapes(seed):
+    """FP8 caches with at least 64 (token, head) rows per KV head: the blocks
+    the sequences reach are staged to bf16, then the tiled kernel runs on
+    them; whole contexts and explicit partitions, every block size, chunks
+    that are the whole sequence, and tables that share blocks."""
+    rng = np.random.default_rng(1300 + seed)
+    D = [128, 64][seed % 2]
+    bs = [16, 8, 32][seed % 3]
+    H_kv = int(rng.integers(1, 3))
+    G = int(rng.choice([1, 2, 4, 8]))
+    M = int(rng.choice([64, 100, 200])) if G == 1 else int(rng.choice([16, 33, 70, 130]))
+    S = int(rng.integers(1, 4))
+    lens = rng.integers(M, M + 900, size=S)
+    if seed % 4 == 1:
+        lens[:] = M
+    ps = [0, 256, 0, 4 * bs, 192, 64][seed % 6]
+    ps = ps - ps % bs
+    w = workloads.build_workload(f"tiled-fp8-{seed}", S, H_kv * G, H_kv, D, bs, "bf16", "fp8",
+                                 lens, seed, fill="write", query_tokens=M)
+    if seed % 4 == 3 and S > 1:  # the first blocks of every table name sequence 0's
+        shared = min(int(lens.min()) - M, 128) // bs
+        w.block_tables[1:, :shared] = w.block_tables[0, :shared]
+    _say(f"case tiled-fp8-{seed} D={D} bs={bs} H_kv={H_kv} G={G} M={M} lens={list(lens)} "
+         f"ps={ps}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle.paged_attention_prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                         bs, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    out = _prefill(dw, ps)
+    err = max_err(out_f64(out), ref)
+    _say(f"  max_err={err:.3e}")
+    assert err <= TOL["fp8"], err
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_tiled_short_contexts_beside_split_ones(cache):
+    """Sequences within one partition beside ones split over several (the
+    grid covers the longest): the short ones are finished by their first
+    partition, and their later, empty partitions leave the output alone."""
+    lens = np.array([64, 900, 70, 64, 513])
+    w = workloads.build_workload(f"tiled-short-{cache}", 5, 16, 2, 128, 16, "bf16", cache, lens,
+                                 17, fill="write" if cache == "fp8" else "random",
+                                 query_tokens=64)
+    _say(f"case tiled short beside split {cache} lens={list(lens)}")
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle.paged_attention_prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                         16, ks, vs)
+    dw = DeviceWorkload(w)
+    dw.write()
+    for ps in (128, 256):
+        err = max_err(out_f64(_prefill(dw, ps)), ref)
+        _say(f"  ps={ps} max_err={err:.3e}")
+        assert err <= TOL[cache], (ps, err)
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 3.0])
 def test_tiled_scale_edge_cases(scale):
     """Negative, zero and large softmax scales on the tiled kernel (a zero
@@ -198,3 +255,24 @@ def test_long_chunk_sampled_tokens(cache):
         err = max_err(out[:, t], ref)
         _say(f"  token {t} max_err={err:.3e}")
         assert err <= TOL[cache], (t, err)
+
+
+@pytest.mark.parametrize("name", sorted(workloads.PREFILL_CONFIGS))
+def test_timed_prefill_workloads_sampled_tokens(name):
+    """The chunked-prefill workloads the benchmark times, at full size and in
+    its launch configuration (the library's partitions; FP8 staged for the
+    tiled kernel): every element of sampled tokens against the oracle."""
+    w = workloads.make_prefill(name)
+    M = w.query_tokens
+    _say(f"case timed prefill {name} S={w.S} M={M} lens={list(w.context_lens)}")
+    kc, vc, ks, vs = oracle_caches(w)
+    dw = DeviceWorkload(w)
+    dw.write()
+    out = out_f64(_prefill(dw, 0))
+    for t in (0, 137, 384, M - 1):
+        ref = oracle.paged_attention_decode(w.q[:, t], kc, vc, w.block_tables,
+                                            w.context_lens - M + t + 1, w.scale, w.block_size,
+                                            ks, vs)
+        err = max_err(out[:, t], ref)
+        _say(f"  token {t} max_err={err:.3e}")
+        assert err <= TOL[w.cache_dtype], (t, err)

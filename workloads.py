@@ -287,6 +287,7 @@ PREFILL_CONFIGS = {
     # name: (S, M, H, H_kv, D, bs, cache, context length per sequence)
     "prefill-chunk-gqa-bf16": (4, 512, 32, 8, 128, 16, "bf16", 4096),
     "prefill-chunk-mha-bf16": (4, 512, 32, 32, 128, 16, "bf16", 4096),
+    "prefill-chunk-gqa-fp8": (4, 512, 32, 8, 128, 16, "fp8", 4096),
 }
 
 
