@@ -45,7 +45,12 @@ typedef __attribute__((address_space(3))) i16x4_v lds_i16x4_v;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBM = 128;        // rows per workgroup tile
-constexpr int kWaves = 4;       // 32 rows per wave
+// 16-row MFMA groups per wave: 2 (4 waves of 32 rows, every K and V fragment
+// read shared by both groups) or 1 (8 waves of 16 rows: half the registers,
+// so twice the waves per SIMD to cover each wave's dependent chain).
+constexpr int kGroups = 2;
+template <int NG>
+struct Waves { static constexpr int N = kBM / (16 * NG); };
 constexpr int kKC = 64;         // keys per LDS chunk
 constexpr float kMaxInit = -1e30f;  // running max before any key (finite: no inf - inf)
 
@@ -148,6 +153,13 @@ __device__ __forceinline__ void lds_read_tab(int (&v)[4], const uint32_t (&ad)[4
       : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
       : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]));
 }
+__device__ __forceinline__ void lds_read_tab(int (&v)[1], const uint32_t (&ad)[1]) {
+  asm volatile(
+      "ds_read_b32 %0, %1\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0])
+      : "v"(ad[0]));
+}
 __device__ __forceinline__ void lds_read_tab(int (&v)[2], const uint32_t (&ad)[2]) {
   asm volatile(
       "ds_read_b32 %0, %2\n"
@@ -198,14 +210,15 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
-template <int D>
+template <int D, int NG>
 struct Layout {
+  static constexpr int NW = Waves<NG>::N;           // waves per workgroup
   static constexpr int PR = D / 8;                  // 16-byte pieces per row
   static constexpr int RB = 256 / (2 * D);          // rows per 256 bytes
   static constexpr int ROW = 2 * D;                 // bytes per row
   static constexpr int TILE = kKC * ROW;            // bytes of a K or V chunk
   static constexpr int CHUNK = 2 * TILE;            // K tile then V tile
-  static constexpr int ROUNDS = kKC * PR / 256;     // DMA rounds per chunk (4 or 2)
+  static constexpr int ROUNDS = kKC * PR / (64 * NW);  // DMA rounds per wave and chunk
   static constexpr int RPI = 64 / PR;               // rows per wave DMA instruction
   static constexpr int NKC = D / 32;                // k-steps of the score products
   static constexpr int NMD = D / 16;                // 16-wide d tiles of O^T
@@ -228,24 +241,24 @@ struct Layout {
 };
 
 // Gathers keys c0 .. c0 + kKC - 1 of KV head kvh into buffer `buf` (K and V
-// tiles).  Wave w, round i fills bytes [(4 i + w) KiB, +1 KiB) of each tile,
-// lane l the physical piece 64 (4 i + w) + l, and fetches the logical piece
+// tiles).  Wave w of NW, round i fills bytes [(NW i + w) KiB, +1 KiB) of each
+// tile, lane l the physical piece 64 (NW i + w) + l, and fetches the logical piece
 // that the swizzle stores there.  One round covers RPI <= 8 rows of one
 // cache block, so its block id is one table entry.  Keys at or past kend
 // are read as key kend - 1 (a real row of the same block; masked later).
-template <int D, int BS>
+template <int D, int BS, int NG>
 __device__ __forceinline__ void issue_chunk(char* buf, const PrefillParams& p, uint32_t tab,
                                             int elast, int kvh, int start, int c0, int kend,
                                             int wave, int lane,
-                                            const uint32_t (&koff)[Layout<D>::ROUNDS],
-                                            const uint32_t (&voff)[Layout<D>::ROUNDS]) {
-  using L = Layout<D>;
+                                            const uint32_t (&koff)[Layout<D, NG>::ROUNDS],
+                                            const uint32_t (&voff)[Layout<D, NG>::ROUNDS]) {
+  using L = Layout<D, NG>;
   int blk[L::ROUNDS];
   uint32_t ta[L::ROUNDS];
   const int cidx = (c0 - start) / BS;
 #pragma unroll
   for (int i = 0; i < L::ROUNDS; ++i)
-    ta[i] = tab + 4 * min(cidx + (L::RPI * (i * kWaves + wave)) / BS, elast);
+    ta[i] = tab + 4 * min(cidx + (L::RPI * (i * L::NW + wave)) / BS, elast);
   lds_read_tab(blk, ta);
   if (c0 + kKC <= kend) {
     // Whole chunk below kend: a uniform row base per round plus the lane's
@@ -256,7 +269,7 @@ __device__ __forceinline__ void issue_chunk(char* buf, const PrefillParams& p, u
       const size_t rb = ((size_t)b * p.H_kv + kvh) * (size_t)(BS * D * 2);
       const char* kb = reinterpret_cast<const char*>(p.kc) + rb;
       const char* vb = reinterpret_cast<const char*>(p.vc) + rb;
-      const int lds = (i * kWaves + wave) * 1024;
+      const int lds = (i * L::NW + wave) * 1024;
       __builtin_amdgcn_global_load_lds(kb + koff[i], (lds_void*)(buf + lds), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vb + voff[i], (lds_void*)(buf + L::TILE + lds), 16, 0, 0);
     }
@@ -264,13 +277,13 @@ __device__ __forceinline__ void issue_chunk(char* buf, const PrefillParams& p, u
   }
 #pragma unroll
   for (int i = 0; i < L::ROUNDS; ++i) {
-    const int k = L::RPI * (i * kWaves + wave) + lane / L::PR;
+    const int k = L::RPI * (i * L::NW + wave) + lane / L::PR;
     const int pp = lane % L::PR;
     const int t = min(c0 + k, kend - 1);
     const size_t row = ((size_t)blk[i] * p.H_kv + kvh) * BS + (t % BS);
     const size_t offk = row * D + 8 * (pp ^ L::swz(k));  // XOR is its own inverse
     const size_t offv = row * D + 8 * (pp ^ L::vswz(k));
-    const int lds = (i * kWaves + wave) * 1024;
+    const int lds = (i * L::NW + wave) * 1024;
     __builtin_amdgcn_global_load_lds(p.kc + offk, (lds_void*)(buf + lds), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(p.vc + offv, (lds_void*)(buf + L::TILE + lds), 16, 0, 0);
   }
@@ -281,17 +294,17 @@ __device__ __forceinline__ void issue_chunk(char* buf, const PrefillParams& p, u
 // logical pieces (D/32) q4 + c); vad: the lane's V address in buffer 0 for
 // d tile 0, XORed with 32 md for tile md.  e[j]: keys below it are visible
 // to this lane's row of group j; full[j] (uniform): no mask for group j.
-template <int D, int SEL>
+template <int D, int NG, int SEL>
 __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uint32_t vad,
-                                              const uint4 (&qf)[2][D / 32],
-                                              f32x4_v (&acc)[2][D / 16], float (&m)[2],
-                                              f32x4_v (&lacc)[2], const int (&e)[2],
-                                              const bool (&full)[2], int c0, float sl,
+                                              const uint4 (&qf)[NG][D / 32],
+                                              f32x4_v (&acc)[NG][D / 16], float (&m)[NG],
+                                              f32x4_v (&lacc)[NG], const int (&e)[NG],
+                                              const bool (&full)[NG], int c0, float sl,
                                               int lane) {
-  using L = Layout<D>;
+  using L = Layout<D, NG>;
   constexpr int KOFF = SEL * L::CHUNK;
   const int q4 = lane >> 4;
-  f32x4_v s[2][4];
+  f32x4_v s[NG][4];
   // S^T = K . Q^T, 16 keys per tile T: lane (q4, r) holds key 16 T + r,
   // contraction elements (D/4) q4 + 8 c .. + 7 (the Q fragments use the same
   // order).  The swizzle of row 16 T + r does not depend on T.
@@ -299,13 +312,11 @@ __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uin
   {                                                                                           \
     uint4 a[L::NKC];                                                                          \
     lds_read_k<KOFF + (T) * 16 * L::ROW>(a, kad);                                             \
-    s[0][T] = f32x4_v{0.f, 0.f, 0.f, 0.f};                                                    \
-    s[1][T] = f32x4_v{0.f, 0.f, 0.f, 0.f};                                                    \
+    _Pragma("unroll") for (int j = 0; j < NG; ++j) s[j][T] = f32x4_v{0.f, 0.f, 0.f, 0.f};    \
     _Pragma("unroll") for (int c = 0; c < L::NKC; ++c) {                                      \
-      s[0][T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(a[c]), to_bf16x8(qf[0][c]), \
-                                                         s[0][T], 0, 0, 0);                   \
-      s[1][T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(a[c]), to_bf16x8(qf[1][c]), \
-                                                         s[1][T], 0, 0, 0);                   \
+      _Pragma("unroll") for (int j = 0; j < NG; ++j) s[j][T] =                                \
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(a[c]), to_bf16x8(qf[j][c]),       \
+                                                  s[j][T], 0, 0, 0);                          \
     }                                                                                         \
   }
   PKV_SCORE_TILE(0)
@@ -319,16 +330,17 @@ __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uin
   // more than 8 (wave-uniform test), so most chunks skip the rescale of the
   // accumulators; the exponents stay below 2^8, and acc and l always share
   // one reference, so the normalised result is unchanged.
-  uint4 pb[2][2];
+  uint4 pb[NG][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NG; ++j) {
     float mc = kNegInf;
     if (!full[j]) {
+      const int rel = e[j] - c0 - 4 * q4;  // keys 16 T + i below it are visible
 #pragma unroll
       for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (!(c0 + 16 * T + 4 * q4 + i < e[j])) s[j][T][i] = kNegInf;
+          if (!(16 * T + i < rel)) s[j][T][i] = kNegInf;
     }
     {
       float t0 = max3f(s[j][0][0], s[j][0][1], s[j][0][2]);
@@ -373,10 +385,10 @@ __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uin
   // products use).
   const bf16x8_v ones = to_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    lacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, to_bf16x8(pb[0][u]), lacc[0], 0, 0, 0);
-    lacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, to_bf16x8(pb[1][u]), lacc[1], 0, 0, 0);
-  }
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+      lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, to_bf16x8(pb[j][u]), lacc[j], 0, 0, 0);
 #pragma unroll
   for (int md = 0; md < L::NMD; md += 2) {
     uint2 v[8];
@@ -387,18 +399,18 @@ __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uin
       for (int u = 0; u < 2; ++u) {
         const uint2 lo = v[4 * h + 2 * u], hi = v[4 * h + 2 * u + 1];
         const bf16x8_v va = to_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-        acc[0][md + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, to_bf16x8(pb[0][u]),
-                                                                  acc[0][md + h], 0, 0, 0);
-        acc[1][md + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, to_bf16x8(pb[1][u]),
-                                                                  acc[1][md + h], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NG; ++j)
+          acc[j][md + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, to_bf16x8(pb[j][u]),
+                                                                    acc[j][md + h], 0, 0, 0);
       }
     }
   }
 }
 
-template <int D, int BS>
-__global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillParams p) {
-  using L = Layout<D>;
+template <int D, int BS, int NG>
+__global__ __launch_bounds__(Waves<NG>::N * 64, 2) void prefill_mfma_kernel(PrefillParams p) {
+  using L = Layout<D, NG>;
   __shared__ int s_tab[kPrefillMaxTable];
   __shared__ __attribute__((aligned(1024))) char s_buf[2 * L::CHUNK];
 
@@ -439,17 +451,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
   const int elast = nch > 0 ? (kend - 1) / BS - t0 : 0;  // last table entry used
   if (nch > 0) {
     const int32_t* trow = p.tables + (size_t)seq * p.max_blocks + t0;
-    for (int i = tid; i <= elast; i += kWaves * 64) s_tab[i] = trow[i];
+    for (int i = tid; i <= elast; i += L::NW * 64) s_tab[i] = trow[i];
   }
 
   // This lane's rows (one per group) and their query fragments.
-  uint4 qf[2][L::NKC];
-  int e[2];
-  size_t orow[2];
-  bool live[2];
+  uint4 qf[NG][L::NKC];
+  int e[NG];
+  size_t orow[NG];
+  bool live[NG];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rho = r0 + 32 * wave + 16 * j + r;
+  for (int j = 0; j < NG; ++j) {
+    const int rho = r0 + 16 * NG * wave + 16 * j + r;
     live[j] = rho <= rlast;
     const int rc = min(rho, rlast);
     const int m = rc / p.G;
@@ -469,8 +481,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
   // tiny positive one: every weight is then 1 up to rounding, as it should).
   const float sl = fmaxf(fabsf(p.scale_log2), 1e-30f);
   // Uniform per group: a group's first row has the smallest end.
-  const int gfull0 = min(pend, base + min(r0 + 32 * wave, rlast) / p.G);
-  const int gfull1 = min(pend, base + min(r0 + 32 * wave + 16, rlast) / p.G);
+  int gfull[NG];
+#pragma unroll
+  for (int j = 0; j < NG; ++j)
+    gfull[j] = min(pend, base + min(r0 + 16 * (NG * wave + j), rlast) / p.G);
 
   // LDS addresses (buffer 0; buffer 1 and the V tile are immediate offsets).
   const uint32_t buf0 = lds_addr(s_buf);
@@ -492,58 +506,66 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
   uint32_t koff[L::ROUNDS], voff[L::ROUNDS];
 #pragma unroll
   for (int i = 0; i < L::ROUNDS; ++i) {
-    const int k = L::RPI * (i * kWaves + wave) + lane / L::PR;
+    const int k = L::RPI * (i * L::NW + wave) + lane / L::PR;
     const int pp = lane % L::PR;
     koff[i] = 2u * (uint32_t)((k % BS) * D + 8 * (pp ^ L::swz(k)));
     voff[i] = 2u * (uint32_t)((k % BS) * D + 8 * (pp ^ L::vswz(k)));
   }
 
-  f32x4_v acc[2][L::NMD];
+  f32x4_v acc[NG][L::NMD];
+  float m[NG];
+  f32x4_v lacc[NG];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NG; ++j) {
 #pragma unroll
     for (int md = 0; md < L::NMD; ++md) acc[j][md] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {kMaxInit, kMaxInit};
-  f32x4_v lacc[2] = {f32x4_v{0.f, 0.f, 0.f, 0.f}, f32x4_v{0.f, 0.f, 0.f, 0.f}};
+    m[j] = kMaxInit;
+    lacc[j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  }
 
   __syncthreads();  // the table slice is in LDS
   if (nch > 0)
-    issue_chunk<D, BS>(s_buf, p, tab, elast, kvh, start, start, kend, wave, lane, koff, voff);
+    issue_chunk<D, BS, NG>(s_buf, p, tab, elast, kvh, start, start, kend, wave, lane, koff, voff);
   for (int ch = 0; ch < nch; ch += 2) {
     {  // even chunk, buffer 0
       const int c0 = start + ch * kKC;
       if (ch + 1 < nch) {
-        issue_chunk<D, BS>(s_buf + L::CHUNK, p, tab, elast, kvh, start, c0 + kKC, kend, wave,
-                           lane, koff, voff);
+        issue_chunk<D, BS, NG>(s_buf + L::CHUNK, p, tab, elast, kvh, start, c0 + kKC, kend, wave,
+                               lane, koff, voff);
         wait_vm_barrier<2 * L::ROUNDS>();
       } else {
         wait_vm_barrier<0>();
       }
-      const bool full[2] = {c0 + kKC <= gfull0, c0 + kKC <= gfull1};
-      compute_chunk<D, 0>(kad, vad, qf, acc, m, lacc, e, full, c0, sl, lane);
+      bool full[NG];
+#pragma unroll
+      for (int j = 0; j < NG; ++j) full[j] = c0 + kKC <= gfull[j];
+      compute_chunk<D, NG, 0>(kad, vad, qf, acc, m, lacc, e, full, c0, sl, lane);
       wait_vm_barrier<63>();  // every wave is done with buffer 0
     }
     if (ch + 1 < nch) {  // odd chunk, buffer 1
       const int c0 = start + (ch + 1) * kKC;
       if (ch + 2 < nch) {
-        issue_chunk<D, BS>(s_buf, p, tab, elast, kvh, start, c0 + kKC, kend, wave, lane, koff, voff);
+        issue_chunk<D, BS, NG>(s_buf, p, tab, elast, kvh, start, c0 + kKC, kend, wave, lane, koff,
+                               voff);
         wait_vm_barrier<2 * L::ROUNDS>();
       } else {
         wait_vm_barrier<0>();
       }
-      const bool full[2] = {c0 + kKC <= gfull0, c0 + kKC <= gfull1};
-      compute_chunk<D, 1>(kad, vad, qf, acc, m, lacc, e, full, c0, sl, lane);
+      bool full[NG];
+#pragma unroll
+      for (int j = 0; j < NG; ++j) full[j] = c0 + kKC <= gfull[j];
+      compute_chunk<D, NG, 1>(kad, vad, qf, acc, m, lacc, e, full, c0, sl, lane);
       wait_vm_barrier<63>();  // every wave is done with buffer 1
     }
   }
 
-  const float l[2] = {lacc[0][0], lacc[1][0]};
   // Lane (q4, r) of group j holds O^T[16 md + 4 q4 + i][row r].
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NG; ++j) {
+    const float l = lacc[j][0];
     if (!live[j]) continue;
     if (single) {
-      const float inv = l[j] > 0.f ? 1.f / l[j] : 0.f;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
       uint16_t* o = p.out + orow[j] * D + 4 * q4;
 #pragma unroll
       for (int md = 0; md < L::NMD; ++md) {
@@ -564,7 +586,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillPar
       }
       if (q4 == 0) {
         p.ws_m[pi] = m[j];
-        p.ws_l[pi] = l[j];
+        p.ws_l[pi] = l;
       }
     }
   }
@@ -588,7 +610,8 @@ hipError_t launch_db(const DecodeArgs& a) {
   p.per_xcd = (int)((total + 7) / 8);
   p.scale_log2 = a.scale * kLog2e;
   const unsigned grid = (unsigned)(8LL * p.per_xcd);
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, BS>), dim3(grid), dim3(kWaves * 64), 0, a.stream, p);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, kGroups>), dim3(grid),
+                     dim3(Waves<kGroups>::N * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 
