@@ -116,6 +116,7 @@ struct MfmaParams {
   int np_stride;      // partial slots per row
   int force_partial;  // write partials even when a context fits one partition
   int young_from;  // first workgroup that runs only its first item
+  int group_major;  // each per-XCD queue takes whole (sequence, partition) groups
   float scale_log2;
 };
 
@@ -682,9 +683,23 @@ struct Order {
   const int* seq;       // n << kSeqBits | sequence, by sorted position
 };
 
+// Items [lo, hi) in super-rows of 8 Y: eight consecutive (sequence,
+// partition) groups of Y row-group items each.  Position j of a super-row
+// becomes row group j / 8 of group j % 8, so the queue that takes every
+// eighth item runs all the row groups of one group; a last, shorter
+// super-row keeps the plain order.
+__device__ __forceinline__ int group_major(int item, int lo, int hi, int Y) {
+  const int span = 8 * Y;
+  const int j = item - lo;
+  const int sr = j / span;
+  if (lo + (sr + 1) * span > hi) return item;
+  const int r = j - sr * span;
+  return lo + sr * span + (r & 7) * Y + (r >> 3);
+}
+
 template <int BS, bool SCAN, int MODE>
 __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y, int n_full,
-                                            const Order& o) {
+                                            int n_items, const Order& o) {
   Item it;
   it.w.pre = 0;
   if constexpr (MODE == kModeSplitPrefix) {
@@ -708,6 +723,14 @@ __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y
       return it;
     }
     item -= p.pre_items;
+  }
+  if constexpr (MODE != kModeSplitPrefix) {
+    if (p.group_major) {
+      // full partitions and last partitions separately: an early first item
+      // (a full partition) is decoded before the last partitions are counted
+      const int fl = SCAN ? Y * n_full : 0;
+      item = item < fl ? group_major(item, 0, fl, Y) : group_major(item, fl, n_items, Y);
+    }
   }
   const int y = item % Y;
   const int rest = item / Y;
@@ -969,7 +992,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     else
       early = first < Y * n_full;
     if (early) {
-      it = decode_item<BS, SCAN, MODE>(p, first, Y, n_full, order);
+      it = decode_item<BS, SCAN, MODE>(p, first, Y, n_full, 0, order);
       tab_first = fetch_tab<CT, D, BS, MODE>(p, it.w, wave, lane);
       q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
       store_tab(tab_first, s_wtab[wave], lane);  // the wave's own slice
@@ -1003,7 +1026,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   // Otherwise the first item's block ids and Q are requested together (one
   // memory round trip before the first chunk's loads, not two).
   if (!early) {
-    it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, order);
+    it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, total - n_pre, order);
     tab_first = fetch_tab<CT, D, BS, MODE>(p, it.w, wave, lane);
     q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
   }
@@ -1151,7 +1174,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     use_shared = __builtin_amdgcn_readfirstlane(s_next[1]);
     const bool merge_prev =
         pg >= 0 && __builtin_amdgcn_readfirstlane(s_red[0] | s_red[1] | s_red[2] | s_red[3]);
-    const Item ni = decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, order);
+    const Item ni =
+        decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, total - n_pre, order);
     const int tab_nn = fetch_tab<CT, D, BS, MODE>(p, ni.w, wave, lane);
     const uint4 q_nn = fetch_q<CT, D, MODE>(p, ni.w, tid);
 
@@ -1338,6 +1362,13 @@ hipError_t launch_bs(const DecodeArgs& a) {
   p.pre_items = a.H_kv * p.pre_chunks * p.pre_slots;
   p.np_stride = a.np_stride > 0 ? a.np_stride : a.NP;
   p.force_partial = a.force_partial ? 1 : 0;
+  // FP8 scales are [num_blocks][H_kv] floats: a block's KV heads share their
+  // scale lines, which one XCD's L2 then serves to all of them (with a KV
+  // head per queue every XCD fetched every line, 6% of the traffic).  The
+  // split-prefix kind keeps a KV head per queue: there the heads' shared
+  // prefix blocks are what the L2 serves.
+  p.group_major = Geometry<CT, D>::ELEM == 1 && !(a.prefix_rows > 0 || a.len_off > 0 ||
+                                                  a.force_partial);
   p.scale_log2 = a.scale * kLog2e;
   const long long items = (long long)a.H_kv * p.chunks * a.S * a.NP + p.pre_items;
   if (a.prefix_rows > 0 || a.len_off > 0 || a.force_partial)

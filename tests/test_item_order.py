@@ -261,3 +261,54 @@ def test_claims_follow_the_static_items():
         n_static = 1 if one_deep else 2
         claimed = sorted(i for d in done for i in d[n_static:] if i < n_local)
         assert claimed[:nq] == list(range(first_claimed, first_claimed + nq))
+
+
+def group_major(item, lo, hi, Y):
+    """Replay of the decode kernel's group-major item order (FP8 caches):
+    in super-rows of 8 Y items, position j becomes row group j // 8 of
+    (sequence, partition) group j % 8; a last, shorter super-row keeps the
+    plain order."""
+    span = 8 * Y
+    j = item - lo
+    sr = j // span
+    if lo + (sr + 1) * span > hi:
+        return item
+    r = j - sr * span
+    return lo + sr * span + (r & 7) * Y + (r >> 3)
+
+
+def _group_major_order(Y, n_full, total):
+    fl = Y * n_full
+    return [group_major(i, 0, fl, Y) if i < fl else group_major(i, fl, total, Y)
+            for i in range(total)]
+
+
+@pytest.mark.parametrize("Y", [1, 3, 8, 32, 40])
+@pytest.mark.parametrize("n_full,n_rag", [(0, 1), (0, 7), (0, 256), (3, 250), (17, 8), (64, 0),
+                                          (9, 13)])
+def test_group_major_order_is_a_permutation(Y, n_full, n_rag):
+    """Every item index maps to exactly one item, full partitions stay full
+    partitions (an early first item is decoded before the last partitions
+    are counted) and last partitions stay last partitions."""
+    total = Y * (n_full + n_rag)
+    order = _group_major_order(Y, n_full, total)
+    assert sorted(order) == list(range(total))
+    fl = Y * n_full
+    assert all((i < fl) == (o < fl) for i, o in enumerate(order))
+
+
+@pytest.mark.parametrize("Y,n_full,n_rag", [(8, 0, 256), (8, 5, 251), (40, 2, 30), (3, 16, 16)])
+def test_group_major_queues_take_whole_groups(Y, n_full, n_rag):
+    """Under the per-XCD queues (every eighth item), each queue's items of a
+    complete super-row are all Y row groups of one (sequence, partition)
+    group, so the KV heads of a block meet on one XCD."""
+    total = Y * (n_full + n_rag)
+    order = _group_major_order(Y, n_full, total)
+    for lo, hi in ((0, Y * n_full), (Y * n_full, total)):
+        for sr in range((hi - lo) // (8 * Y)):
+            base = lo + sr * 8 * Y
+            for q in range(8):
+                items = [order[i] for i in range(base, base + 8 * Y) if (i - lo) % 8 == q]
+                groups = {i // Y for i in items}
+                assert len(groups) == 1 and len(items) == Y
+                assert sorted(i % Y for i in items) == list(range(Y))
