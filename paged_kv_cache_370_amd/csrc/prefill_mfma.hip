@@ -333,7 +333,7 @@ __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uin
   uint4 pb[NG][2];
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
-    float mc = kNegInf;
+    float mt;  // the lane's maximum over its 16 keys, raw units
     if (!full[j]) {
       const int rel = e[j] - c0 - 4 * q4;  // keys 16 T + i below it are visible
 #pragma unroll
@@ -350,11 +350,13 @@ __device__ __forceinline__ void compute_chunk(const uint32_t (&kad)[D / 32], uin
       float t4 = max3f(s[j][3][0], s[j][3][1], s[j][3][2]);
       t0 = max3f(t0, t1, t2);
       t3 = max3f(t3, t4, s[j][3][3]);
-      mc = max4_rows(max2f(t0, t3));
+      mt = max2f(t0, t3);
     }
-    const float mcs = mc * sl;
-    if (__any(mcs > m[j] + 8.f)) {
-      const float m_new = fmaxf(m[j], mcs);
+    // A row's maximum passes m + 8 only where one of its four lanes' does
+    // (the factor is positive and rounding is monotonic), so the row
+    // maximum across lanes is needed only on a rescale.
+    if (__any(mt * sl > m[j] + 8.f)) {
+      const float m_new = fmaxf(m[j], max4_rows(mt) * sl);
       const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
       m[j] = m_new;
       lacc[j] *= alpha;
