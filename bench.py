@@ -18,7 +18,7 @@ back-to-back warm times beside it.
                8 TB/s HBM peak;
   workloads    the 32K-context, shared-prefix and FP8 workloads measured the
                same way, each with its own roofline;
-  ceiling_gbs  a streaming read of 1 GiB (and a 4 KiB-tile gather) by the
+  ceiling_gbs  a streaming read of 1 GiB (and 4 KiB- and 2 KiB-tile gathers) by the
                library's probe kernels: what HBM delivers to a plain read;
   cpu_baseline the CPU oracle (float64 NumPy, untuned) on a bounded sample of
                the headline workload, on every core of this process's CPU share
@@ -427,25 +427,29 @@ def measure_decode(pkv, torch, timer, w, ps, steps, warmup, traffic_key):
 
 def probe_bench(pkv, torch, timer, iters, gib=1):
     """Practical HBM ceiling on this device: a streaming read of a 1 GiB
-    buffer, and a gather of 4 KiB tiles (one (block, KV head) tile of a bf16
-    cache at bs 16, D 128) in random order over the same buffer, flushed per
-    iteration like the decode timings."""
+    buffer, and gathers of whole tiles in random order over the same buffer:
+    4 KiB (one (block, KV head) tile of a bf16 cache at bs 16, D 128) and
+    2 KiB (bf16 at bs 8, or FP8 at bs 16), flushed per iteration like the
+    decode timings."""
     nbytes = gib << 30
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    tile = 4096
     rng = np.random.default_rng(11)
-    ids = rng.permutation(nbytes // tile).astype(np.int32)
-    assert ids.min() >= 0 and (int(ids.max()) + 1) * tile <= nbytes   # every tile inside buf
-    tiles = torch.from_numpy(ids).cuda()
     pkv.hbm_read_probe(buf, sink)
-    pkv.hbm_gather_probe(buf, tiles, tile, sink)
     rd = stats(timer.flushed(lambda: pkv.hbm_read_probe(buf, sink), iters))
-    ga = stats(timer.flushed(lambda: pkv.hbm_gather_probe(buf, tiles, tile, sink), iters))
-    return {"bytes": nbytes,
-            "read_GB_per_s": round(nbytes / (rd["median"] * 1e-3) / 1e9, 1),
-            "gather_4KiB_tiles_GB_per_s": round(nbytes / (ga["median"] * 1e-3) / 1e9, 1),
-            "read_ms": rd, "gather_ms": ga}
+    res = {"bytes": nbytes, "read_GB_per_s": round(nbytes / (rd["median"] * 1e-3) / 1e9, 1),
+           "read_ms": rd}
+    for tile, key in ((4096, "gather_4KiB_tiles"), (2048, "gather_2KiB_tiles")):
+        ids = rng.permutation(nbytes // tile).astype(np.int32)
+        assert ids.min() >= 0 and (int(ids.max()) + 1) * tile <= nbytes   # every tile inside buf
+        tiles = torch.from_numpy(ids).cuda()
+        pkv.hbm_gather_probe(buf, tiles, tile, sink)
+        ga = stats(timer.flushed(lambda: pkv.hbm_gather_probe(buf, tiles, tile, sink), iters))
+        res[key + "_GB_per_s"] = round(nbytes / (ga["median"] * 1e-3) / 1e9, 1)
+        res[key + "_ms"] = ga
+        del tiles
+    res["gather_ms"] = res["gather_4KiB_tiles_ms"]
+    return res
 
 
 def main():

@@ -9,7 +9,8 @@
 //
 //   * rows of a KV head are the (token, head) pairs m * G + g of its G query
 //     heads; a workgroup owns a tile of 128 rows, each of its 4 waves 32 rows
-//     (two 16-row MFMA groups that share every K and V fragment read);
+//     (two 16-row MFMA groups that share every K and V fragment read; or, by
+//     kGroups, 8 waves of 16 rows);
 //   * the workgroup walks its keys in chunks of 64: K and V rows are gathered
 //     through the block table straight into LDS by global_load_lds (no
 //     register staging), double-buffered so chunk c+1 streams in while chunk
@@ -21,10 +22,11 @@
 //     them) so the K fragment reads (ds_read_b128) and the V transposed reads
 //     (ds_read_b64_tr_b16) are free of bank conflicts without padding, which
 //     the DMA cannot insert;
-//   * row maxima cross lanes with the gfx950 permlane swaps, row sums come
-//     from the matrix cores (an all-ones tile times P^T), and the
-//     accumulators are rescaled only when a row maximum grows by more than
-//     2^8.
+//   * row sums come from the matrix cores (an all-ones tile times P^T), and
+//     the accumulators are rescaled only when a row maximum grows by more
+//     than 2^8 (tested on each lane's own maximum; the row maximum crosses
+//     lanes with the gfx950 permlane swaps only then);
+//   * FP8 caches are first dequantised to a bf16 pool (stage_fp8_kernel).
 //
 // A tile needs only the keys below its last row's position; rows of earlier
 // tokens mask the newest keys of the last chunks.  Long contexts may be split
