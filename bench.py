@@ -2,11 +2,15 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7b-decode-bf16]
 
-A step is the whole hot path over one batch: paged_kv_cache_write of each
-sequence's newest token, then paged_attention_decode (one launch when every
-context spans at most 4 partitions: the decode kernel merges the partials
-itself; otherwise the partition kernel and the split reduce).  Inputs are seeded synthetic tensors already resident in
-HBM.  Every GPU figure is a per-iteration HIP-event time with the MALL (256 MB)
+A step is the whole hot path over one batch: the write of each sequence's
+newest token into its paged slot, then the decode over the whole context.
+With bf16 queries and cache it is one call, paged_attention_decode_write (the
+write inside the decode's launch, bit for bit the two calls' result; the two
+calls are timed beside it as step_two_calls); otherwise paged_kv_cache_write,
+then paged_attention_decode.  The decode is one launch when every context
+spans at most 4 partitions (the decode kernel merges the partials itself),
+else the partition kernel and the split reduce.  Inputs are seeded synthetic
+tensors already resident in HBM.  Every GPU figure is a per-iteration HIP-event time with the MALL (256 MB)
 and L2s flushed before the iteration by writing a 512 MiB buffer outside the
 events; the median (with p10/p90) over K iterations is reported, and
 back-to-back warm times beside it.
@@ -371,10 +375,28 @@ def measure_decode(pkv, torch, timer, w, ps, steps, warmup, traffic_key):
         pkv.paged_attention_decode(out, q, kc, vc, tables, lens, w.max_context_len, w.scale, ks,
                                    vs, partition_size=ps, workspace=dws)
 
-    def step():
+    def two_calls():
         write()
         decode()
 
+    # bf16 queries and cache, one new token per sequence at its newest
+    # position: the step is paged_attention_decode_write (the write inside
+    # the decode's launch; bit for bit the two calls' result)
+    k_new, v_new, s_new = step_write
+    newest = np.array([w.block_tables[i, (n - 1) // w.block_size] * w.block_size
+                       + (n - 1) % w.block_size if n > 0 else -1
+                       for i, n in enumerate(w.context_lens)])
+    fused = (qc == pkv.PKV_BF16 and cc == pkv.PKV_BF16 and len(w.writes[-1][2]) == w.S
+             and np.array_equal(w.writes[-1][2], newest))
+
+    def step_fused():
+        pkv.paged_attention_decode_write(out, q, k_new, v_new, kc, vc, s_new, tables, lens,
+                                         w.max_context_len, w.scale, partition_size=ps,
+                                         workspace=dws)
+
+    step = step_fused if fused else two_calls
+    res["step"] = ("paged_attention_decode_write (write fused into the decode launch)" if fused
+                   else "paged_kv_cache_write + paged_attention_decode")
     for _ in range(warmup):
         step()
     step_ms = timer.flushed(step, steps)
@@ -384,6 +406,9 @@ def measure_decode(pkv, torch, timer, w, ps, steps, warmup, traffic_key):
             "write": round(timer.warm(write, steps), 5)}
     st, dc = stats(step_ms), stats(decode_ms)
     flushed = {"step": st, "decode": dc}
+    if fused:  # the same step as two calls, for comparison
+        flushed["step_two_calls"] = stats(timer.flushed(two_calls, steps))
+        warm["step_two_calls"] = round(timer.warm(two_calls, steps), 5)
     if one_launch:
         kernel_ms, kernel_flushed = warm["decode"], dc
     else:
@@ -506,10 +531,10 @@ def main():
         "seq_heads_per_s": head["seq_heads_per_s"],
         "timing": (f"median of per-iteration HIP events; before each iteration, outside the "
                    f"events, the MALL is flushed ({args.flush_mode}, {args.flush_mib} MiB)"),
-        "step": ("paged_kv_cache_write + paged_attention_decode (one launch"
-                 + (", partials merged in the decode kernel)" if head["partitions"] > 1 else ")")
-                 if head["decode_launches"] == 1 else
-                 "paged_kv_cache_write + paged_attention_decode (partition kernel + reduce)"),
+        "step": head["step"] + (" (one launch" + (", partials merged in the decode kernel)"
+                                                  if head["partitions"] > 1 else ")")
+                                if head["decode_launches"] == 1 else
+                                " (partition kernel + reduce)"),
         "flushed_ms": head["flushed_ms"],
         "decode_GB_per_s": head["decode_GB_per_s"],
         "decode_pct_hbm_peak": head["decode_pct_hbm_peak"],

@@ -166,6 +166,47 @@ pkv_status_t paged_attention_decode(
     void* workspace, size_t workspace_bytes,
     void* stream);
 
+/*
+ * paged_attention_decode_write -- a decode step's write and attention in one
+ * call: exactly paged_kv_cache_write(key, value, key_cache, value_cache,
+ * NULL, NULL, slot_mapping, num_tokens = num_seqs, num_kv_heads, head_size,
+ * block_size, num_blocks, src_dtype = cache_dtype, cache_dtype) followed by
+ * paged_attention_decode(...) with the other arguments (the write of the
+ * step's new tokens, then attention over contexts that end with them: the
+ * same two operations the dpshk.com article, sections 2.1-2.2, chains every
+ * decode step).  With bf16 queries and cache on the matrix-core kernel both
+ * run in the decode's launch: the item that holds a sequence's newest
+ * position copies its new rows to their slot, and every item over that
+ * position takes its K and V rows from key / value, which are the values
+ * the write stores (a copy), so the result is bit for bit that of the two
+ * calls.  Other dtype pairs run the two launches.
+ *   key, value: [num_seqs][num_kv_heads][head_size], the cache's dtype;
+ *   slot_mapping[i]: the slot of sequence i's position context_lens[i] - 1
+ *   (block_tables[i][(n-1) / bs] * bs + (n-1) % bs), or outside
+ *   [0, num_blocks * bs) for no write (that position is then read from the
+ *   cache).  Slots must be distinct and the written block must not be read
+ *   by another sequence of the call (copy-on-write before appending to a
+ *   shared block); a slot that breaks this gives an unspecified result.
+ *   Caches: PKV_BF16 or PKV_F32 (PKV_ERR_DTYPE for FP8: use the two calls).
+ *   num_blocks: blocks in the pool.  Other arguments, the workspace
+ *   (paged_attention_decode_workspace_size bytes) and errors are as for
+ *   paged_attention_decode; num_seqs == 0 returns PKV_OK without inspecting
+ *   any pointer.
+ */
+pkv_status_t paged_attention_decode_write(
+    void* out, const void* query,
+    const void* key, const void* value,
+    void* key_cache, void* value_cache,
+    const int32_t* slot_mapping,
+    const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_context_len,
+    float scale, int32_t q_dtype, int32_t cache_dtype,
+    int32_t partition_size,
+    void* workspace, size_t workspace_bytes,
+    void* stream);
+
 /* The partition size paged_attention_decode uses for these arguments
  * (resolves partition_size == 0 to the library's choice); negative on
  * invalid arguments. */

@@ -26,6 +26,7 @@ from ._lib import (
     paged_attention_decode_partitions,
     paged_attention_decode_reduce,
     paged_attention_decode_shared_prefix,
+    paged_attention_decode_write,
     paged_attention_prefill,
     paged_kv_block_copy,
     prefill_workspace_size,
@@ -43,6 +44,7 @@ __all__ = [
     "decode_noalloc_max_workspace", "paged_attention_decode",
     "paged_attention_decode_noalloc", "paged_attention_decode_partitions",
     "paged_attention_decode_reduce", "paged_attention_decode_shared_prefix",
+    "paged_attention_decode_write",
     "paged_attention_prefill", "paged_kv_block_copy", "paged_kv_cache_write",
     "prefill_workspace_size", "shared_prefix_workspace_size",
     "status_string",

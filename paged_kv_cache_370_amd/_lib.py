@@ -24,6 +24,7 @@ EXPORTS = (
     "paged_kv_cache_write",
     "paged_kv_cache_write_workspace_size",
     "paged_attention_decode",
+    "paged_attention_decode_write",
     "paged_attention_decode_partition_size",
     "paged_attention_decode_workspace_size",
     "paged_attention_decode_workspace_counter_bytes",
@@ -73,6 +74,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("paged_attention_decode", "paged_attention_decode_partitions"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = decode_args
+    lib.paged_attention_decode_write.restype = i32
+    lib.paged_attention_decode_write.argtypes = [vp] * 9 + [i32] * 8 + [fp] + [i32] * 3 + [vp, sz,
+                                                                                        vp]
     lib.paged_attention_decode_noalloc.restype = i32
     lib.paged_attention_decode_noalloc.argtypes = decode_args[:-3] + [vp]
     lib.paged_attention_decode_noalloc_max_workspace.restype = sz
@@ -231,6 +235,30 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
                            max_context_len, scale, key_scale, value_scale, partition_size,
                            workspace, stream)
     _check(load().paged_attention_decode(*args), "paged_attention_decode")
+
+
+def paged_attention_decode_write(out, query, key, value, key_cache, value_cache, slot_mapping,
+                                 block_tables, context_lens, max_context_len, scale,
+                                 partition_size=0, workspace=None, stream=None):
+    """A decode step's write and attention in one call: key/value [S][H_kv][D]
+    (the cache dtype, bf16 or fp32) go to slot_mapping [S] (each sequence's
+    newest position, or negative for none), then out/query [S][H][D] attend
+    as paged_attention_decode does."""
+    _contig(key, value, slot_mapping)
+    S, H_kv, D = key.shape
+    num_blocks, _, bs, _ = key_cache.shape
+    if _v.enabled():
+        _v.check_slots("paged_attention_decode_write", slot_mapping, num_blocks, bs)
+        _v.check_newest_slots("paged_attention_decode_write", slot_mapping, context_lens,
+                              block_tables, bs)
+    args, _ = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                           max_context_len, scale, None, None, partition_size, workspace, stream)
+    # (out, query, key_cache, value_cache, ks, vs, tables, lens, S, H, H_kv, D, bs, max_blocks,
+    #  max_ctx, scale, qc, cc, ps, ws, wbytes, stream)
+    st = load().paged_attention_decode_write(
+        args[0], args[1], _ptr(key), _ptr(value), args[2], args[3], _ptr(slot_mapping), args[6],
+        args[7], *args[8:13], num_blocks, *args[13:])
+    _check(st, "paged_attention_decode_write")
 
 
 def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables,

@@ -112,6 +112,26 @@ def check_slots(where, slot_mapping, num_blocks, block_size):
                             f"one call")
 
 
+def check_newest_slots(where, slot_mapping, context_lens, block_tables, block_size):
+    """A write fused into a decode: every written slot is its sequence's
+    newest position (context_lens[i] - 1) through its own table."""
+    slots = _host(slot_mapping).astype(np.int64).reshape(-1)
+    lens = _host(context_lens).astype(np.int64).reshape(-1)
+    tables = _host(block_tables).astype(np.int64)
+    if slots.shape[0] != lens.shape[0]:
+        raise ContractError(f"{where}: slot_mapping holds {slots.shape[0]} slots for "
+                            f"{lens.shape[0]} sequences")
+    for i in np.nonzero(slots >= 0)[0]:
+        n = int(lens[i])
+        if n < 1:
+            raise ContractError(f"{where}: sequence {i} writes slot {int(slots[i])} but holds "
+                                f"no position (context_lens = {n})")
+        want = int(tables[i, (n - 1) // block_size]) * block_size + (n - 1) % block_size
+        if int(slots[i]) != want:
+            raise ContractError(f"{where}: slot_mapping[{i}] = {int(slots[i])} is not the slot "
+                                f"{want} of the sequence's newest position {n - 1}")
+
+
 def check_block_pairs(where, block_pairs, src_blocks, dst_blocks, same_pool):
     pairs = _host(block_pairs).astype(np.int64).reshape(-1, 2)
     src, dst = pairs[:, 0], pairs[:, 1]

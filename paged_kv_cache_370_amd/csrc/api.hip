@@ -360,6 +360,50 @@ pkv_status_t paged_attention_decode(void* out, const void* query, const void* ke
   return hip_status(launch_decode_reduce(s.a));
 }
 
+pkv_status_t paged_attention_decode_write(
+    void* out, const void* query, const void* key, const void* value, void* key_cache,
+    void* value_cache, const int32_t* slot_mapping, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float scale, int32_t q_dtype, int32_t cache_dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (cache_dtype != PKV_BF16 && cache_dtype != PKV_F32) return PKV_ERR_DTYPE;  // copy writes
+  DecodeSetup s = setup_decode(out, query, key_cache, value_cache, nullptr, nullptr,
+                               block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                               head_size, block_size, max_blocks_per_seq, max_context_len, scale,
+                               q_dtype, cache_dtype, partition_size, workspace, workspace_bytes,
+                               stream, true);
+  if (s.status != PKV_OK || s.empty) return s.status;
+  if (!key || !value || !slot_mapping) return PKV_ERR_NULL;
+  WriteArgs w;
+  w.key = key; w.value = value; w.key_cache = key_cache; w.value_cache = value_cache;
+  w.key_scale = nullptr; w.value_scale = nullptr; w.slots = slot_mapping;
+  w.T = num_seqs; w.H_kv = num_kv_heads; w.D = head_size; w.bs = block_size;
+  w.num_blocks = num_blocks; w.src_dtype = cache_dtype; w.cache_dtype = cache_dtype;
+  w.workspace = nullptr; w.stream = s.a.stream;
+  if (!decode_mfma_supported(s.a)) {
+    // fp32 queries (vector-ALU kernel), or partitions past the matrix-core
+    // kernel's table slice: the write, then the decode
+    pkv_status_t st = hip_status(launch_kv_write_copy(w));
+    if (st == PKV_OK) st = hip_status(launch_decode_valu(s.a));
+    if (st != PKV_OK || s.a.NP <= 1) return st;
+    return hip_status(launch_decode_reduce(s.a));
+  }
+  s.a.new_k = key;
+  s.a.new_v = value;
+  s.a.slots = slot_mapping;
+  const long long pool = (long long)num_blocks * block_size;
+  s.a.num_slots = pool > 0x7fffffffLL ? 0x7fffffff : (int)pool;
+  if (s.a.NP > 1 && s.a.NP <= kFusedMaxPartitions && s.a.arrivals) {
+    s.a.fused = true;
+    return hip_status(launch_decode_mfma(s.a));
+  }
+  pkv_status_t st = hip_status(launch_decode_mfma(s.a));
+  if (st != PKV_OK || s.a.NP <= 1) return st;
+  return hip_status(launch_decode_reduce(s.a));
+}
+
 // Shared-prefix decode: the prefix's partials (ceil(prefix / P) slots) come
 // before the suffix partitions' in every row; the prefix is cut into
 // partitions of the same P tokens.  (Cutting it finer for more parallel

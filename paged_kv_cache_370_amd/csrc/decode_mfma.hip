@@ -118,6 +118,14 @@ struct MfmaParams {
   int young_from;  // first workgroup that runs only its first item
   int group_major;  // each per-XCD queue takes whole (sequence, partition) groups
   float scale_log2;
+  // Write fused into a decode (kModeDecodeWrite): sequence s's new K and V
+  // rows ([S][H_kv][D], the cache's element type) go to slot slots[s] (none
+  // outside [0, num_slots)), the slot of its position lens[s] - 1.  (Last,
+  // so the other kinds' argument offsets do not move.)
+  const void* new_k;
+  const void* new_v;
+  const int32_t* slots;
+  int num_slots;  // slots of the pool: a slot at or past it (or negative) is not written
 };
 
 // Item kinds of a launch: one query token per sequence; several causal
@@ -128,7 +136,7 @@ struct MfmaParams {
 // its sequence's length), first, then each sequence's own positions; both
 // leave partials that the split reduce merges.  The split parameters are
 // read only by that kind, so the others keep their scalar registers.
-enum : int { kModeDecode = 0, kModeCausal = 1, kModeSplitPrefix = 3 };
+enum : int { kModeDecode = 0, kModeCausal = 1, kModeSplitPrefix = 3, kModeDecodeWrite = 4 };
 
 template <int MODE>
 constexpr bool kSplit = MODE == kModeSplitPrefix;
@@ -215,6 +223,8 @@ struct Src {
 struct Part {
   int seq, kvh, r0, nh, start, end, first_blk;
   int pre;  // an item over the shared prefix (split-prefix launches; 0 otherwise)
+  int sub;  // position whose K and V rows are read from the new rows, not the
+            // cache (write fused into a decode; -1 otherwise)
 };
 
 // Index of a row's [D] vector in q / out ([S][M][H][D]) and of its partial.
@@ -246,7 +256,7 @@ __device__ __forceinline__ size_t token_row(const MfmaParams& p, const Part& w, 
 // V rows are fetched whole: wave load j covers rows j*RPI .. of the chunk,
 // lane l the 16-byte piece l % PR of row j*RPI + l / PR, so every load
 // instruction reads whole token rows (fully used cache lines).
-template <typename CT, int D, int BS>
+template <typename CT, int D, int BS, int MODE>
 __device__ __forceinline__ void load_v(VStage<CT, D>& st, const MfmaParams& p, const Src& src,
                                        const Part& w, const int* ctab, int c0, int lane) {
   using CS = typename CT::storage;
@@ -259,11 +269,16 @@ __device__ __forceinline__ void load_v(VStage<CT, D>& st, const MfmaParams& p, c
     const int t = min(c0 + j * RPI + lane / PR, w.end - 1);  // clamped: masked later
     const int phys = ctab[(t - c0) / BS];
     const size_t row = ((size_t)phys * p.H_kv + w.kvh) * BS + (t % BS);
-    flat[j] = reinterpret_cast<const uint4*>(vc + row * D)[lane % PR];
+    const CS* vrow = vc + row * D;
+    if constexpr (MODE == kModeDecodeWrite) {
+      if (t == w.sub)  // the new row, as the fused write stores it
+        vrow = reinterpret_cast<const CS*>(p.new_v) + ((size_t)w.seq * p.H_kv + w.kvh) * D;
+    }
+    flat[j] = reinterpret_cast<const uint4*>(vrow)[lane % PR];
   }
 }
 
-template <typename CT, int D, int BS>
+template <typename CT, int D, int BS, int MODE>
 __device__ __forceinline__ void load_k(KStage<CT, D>& st, const MfmaParams& p, const Src& src,
                                        const Part& w, const int* ctab, int c0, int lane) {
   using CS = typename CT::storage;
@@ -273,6 +288,12 @@ __device__ __forceinline__ void load_k(KStage<CT, D>& st, const MfmaParams& p, c
     const int t = min(c0 + 16 * T + (lane & 15), w.end - 1);  // clamped: masked later
     const uint4* krow =
         reinterpret_cast<const uint4*>(kc + token_row<CT, D, BS>(p, w, ctab, c0, t, lane));
+    if constexpr (MODE == kModeDecodeWrite) {
+      if (t == w.sub)  // the new row, as the fused write stores it
+        krow = reinterpret_cast<const uint4*>(
+            reinterpret_cast<const CS*>(p.new_k) + ((size_t)w.seq * p.H_kv + w.kvh) * D +
+            Geometry<CT, D>::DQ * (lane >> 4));
+    }
 #pragma unroll
     for (int i = 0; i < Geometry<CT, D>::KV4; ++i) st.k[T][i] = krow[i];
     if constexpr (Geometry<CT, D>::ELEM == 1) {
@@ -702,6 +723,7 @@ __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y
                                             int n_items, const Order& o) {
   Item it;
   it.w.pre = 0;
+  it.w.sub = -1;
   if constexpr (MODE == kModeSplitPrefix) {
     // Items [0, pre_items) are the prefix's: KV head x 16-row chunk of the
     // S x G rows (fastest) and prefix partition, over sequence 0's table
@@ -775,6 +797,12 @@ __device__ __forceinline__ Item decode_item(const MfmaParams& p, int item, int Y
   it.w.start = it.part * p.P;
   it.w.end = min(it.n, it.w.start + p.P);
   it.w.first_blk = it.w.start / BS;
+  if constexpr (MODE == kModeDecodeWrite) {
+    // the partition holding the sequence's newest position reads that
+    // position's rows from the new rows (when the call writes them)
+    const int slot = p.slots[seq];
+    if (it.n > 0 && it.w.end == it.n && slot >= 0 && slot < p.num_slots) it.w.sub = it.n - 1;
+  }
   return it;
 }
 
@@ -965,6 +993,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   const Src cache{p.kc, p.vc, p.ks, p.vs};
   Part dummy_part{};  // token 0 of block 0, KV head 0: row 0 of the dummy
   dummy_part.end = 1;
+  dummy_part.sub = -1;
 
   KStage<CT, D> ks;
   VStage<CT, D> vs;
@@ -1000,8 +1029,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
       if (nvalid > wave) {
         const int c0 = it.w.start + wave * Gm::CHUNK;
-        load_v<CT, D, BS>(vs, p, cache, it.w, s_wtab[wave], c0, lane);
-        load_k<CT, D, BS>(ks, p, cache, it.w, s_wtab[wave], c0, lane);
+        load_v<CT, D, BS, MODE>(vs, p, cache, it.w, s_wtab[wave], c0, lane);
+        load_k<CT, D, BS, MODE>(ks, p, cache, it.w, s_wtab[wave], c0, lane);
       }
     }
     int n_rag;
@@ -1040,7 +1069,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   // whose partials this workgroup stored and has not yet counted in (-1:
   // none), and the group's partition count.  Uniform.
   int pg = -1, pnp = 0;
-  const bool fused = MODE == kModeDecode && p.fused != 0;
+  const bool fused = (MODE == kModeDecode || MODE == kModeDecodeWrite) && p.fused != 0;
   // Uniform: the item's first chunk is still to be requested (every item's
   // but an early first one's, which went out before the sort).
   bool prime = !early;
@@ -1050,11 +1079,31 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
       if (nvalid > wave) {
         const int c0 = it.w.start + wave * Gm::CHUNK;
-        load_v<CT, D, BS>(vs, p, cache, it.w, s_wtab[wave], c0, lane);
-        load_k<CT, D, BS>(ks, p, cache, it.w, s_wtab[wave], c0, lane);
+        load_v<CT, D, BS, MODE>(vs, p, cache, it.w, s_wtab[wave], c0, lane);
+        load_k<CT, D, BS, MODE>(ks, p, cache, it.w, s_wtab[wave], c0, lane);
       }
     }
     prime = false;
+    if constexpr (MODE == kModeDecodeWrite) {
+      // The fused write: the item holding a sequence's newest position
+      // (its first row chunk) copies the new K and V rows of its KV head to
+      // their slot.  Nothing in this launch reads that slot: the items over
+      // the position take the rows from new_k / new_v.  After the first
+      // chunk's loads, so the copy's wait is the one the first step makes.
+      if (it.live && it.w.sub >= 0 && it.w.r0 == 0 && wave == 0) {
+        constexpr int PR = Gm::PR;  // 16-byte pieces per row
+        if (lane < 2 * PR) {
+          const int slot = p.slots[it.w.seq];
+          const size_t dst = (((size_t)(slot / BS) * p.H_kv + it.w.kvh) * BS + slot % BS) * D;
+          const size_t srow = ((size_t)it.w.seq * p.H_kv + it.w.kvh) * D;
+          using CS = typename CT::storage;
+          const bool isv = lane >= PR;
+          const CS* from = reinterpret_cast<const CS*>(isv ? p.new_v : p.new_k) + srow;
+          CS* to = const_cast<CS*>(reinterpret_cast<const CS*>(isv ? p.vc : p.kc)) + dst;
+          reinterpret_cast<uint4*>(to)[lane % PR] = reinterpret_cast<const uint4*>(from)[lane % PR];
+        }
+      }
+    }
     // The claim of the next item, made at the start of wave 0's last step
     // (before its loads) and used only after barrier X.
     // (Only thread 0 sets and reads it: initialising it in the other lanes
@@ -1110,7 +1159,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       const int* ntab = last ? s_zero : ctab + EPC;
       const int cn = last ? 0 : c0 + kNW * Gm::CHUNK;
       store_v<CT, D>(vs, c0, it.w.end, s_v, lane);
-      load_v<CT, D, BS>(vs, p, src, lw, ntab, cn, lane);
+      load_v<CT, D, BS, MODE>(vs, p, src, lw, ntab, cn, lane);
       // Keep the scheduler from sinking the prefetch below the products:
       // the loads must be in flight while this chunk is computed.
       __builtin_amdgcn_sched_barrier(0);
@@ -1126,7 +1175,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
           fv[T] = ks.vsc[T];
         }
       }
-      load_k<CT, D, BS>(ks, p, src, lw, ntab, cn, lane);
+      load_k<CT, D, BS, MODE>(ks, p, src, lw, ntab, cn, lane);
       __builtin_amdgcn_sched_barrier(0);
       softmax_pv<D>(sc, fk, fv, Gm::ELEM == 1, c0, full_end, row_end, s_v, acc, m, lsum, lane);
       ci += kNW;
@@ -1369,8 +1418,14 @@ hipError_t launch_bs(const DecodeArgs& a) {
   // prefix blocks are what the L2 serves.
   p.group_major = Geometry<CT, D>::ELEM == 1 && !(a.prefix_rows > 0 || a.len_off > 0 ||
                                                   a.force_partial);
+  p.new_k = a.new_k; p.new_v = a.new_v; p.slots = a.slots; p.num_slots = a.num_slots;
   p.scale_log2 = a.scale * kLog2e;
   const long long items = (long long)a.H_kv * p.chunks * a.S * a.NP + p.pre_items;
+  if (a.new_k) {  // write fused into a one-token decode: copies, so bf16 caches only
+    if constexpr (Geometry<CT, D>::ELEM == 2)
+      return launch_mode<CT, D, BS, kModeDecodeWrite>(a, p, items);
+    return hipErrorInvalidValue;
+  }
   if (a.prefix_rows > 0 || a.len_off > 0 || a.force_partial)
     return launch_mode<CT, D, BS, kModeSplitPrefix>(a, p, items);
   return a.M > 1 ? launch_mode<CT, D, BS, kModeCausal>(a, p, items)

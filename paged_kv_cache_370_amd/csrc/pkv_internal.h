@@ -64,6 +64,12 @@ struct DecodeArgs {
   int* arrivals;  // [S][H_kv x row groups] partition arrivals (split partials
                   // merged by the partition kernel), zero between calls
   bool fused = false;  // the partition kernel merges the partials: no reduce launch
+  // A write fused into a one-token decode (matrix-core kernel, bf16 cache):
+  // sequence s's new rows new_k/new_v[s][H_kv][D] go to slot slots[s].
+  const void* new_k = nullptr;
+  const void* new_v = nullptr;
+  const int32_t* slots = nullptr;
+  int num_slots = 0;  // slots of the pool (num_blocks x bs): others are not written
   hipStream_t stream;
 };
 

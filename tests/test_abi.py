@@ -275,3 +275,35 @@ def test_noalloc_checks_return_before_any_launch():
     assert call(out=None) == 1
     assert call(cd=2) == 1                       # FP8 cache without scales
     assert call(S=0) == 0
+
+
+def _dwrite(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, slots=FAKE, tables=FAKE,
+             lens=FAKE, S=2, H=8, H_kv=2, D=128, bs=16, nb=64, max_blocks=8, max_ctx=100,
+             scale=0.1, qd=1, cd=1, ps=0, ws=None, wsb=0)
+    a.update(kw)
+    return pkv.load().paged_attention_decode_write(
+        a["out"], a["q"], a["k"], a["v"], a["kc"], a["vc"], a["slots"], a["tables"], a["lens"],
+        a["S"], a["H"], a["H_kv"], a["D"], a["bs"], a["nb"], a["max_blocks"], a["max_ctx"],
+        a["scale"], a["qd"], a["cd"], a["ps"], a["ws"], a["wsb"], None)
+
+
+def test_decode_write_argument_checks():
+    """The fused write + decode call rejects what either half would, before
+    any launch: FP8 caches (the write would quantise), an empty pool, missing
+    new rows or slots, and the decode's own checks."""
+    ws = dict(ws=FAKE, wsb=1 << 20)
+    assert _dwrite(cd=2, **ws) == 3                   # FP8: use the write, then the decode
+    assert _dwrite(qd=1, cd=0, **ws) == 3             # bf16 queries over an fp32 cache
+    assert _dwrite(nb=0, **ws) == 2
+    assert _dwrite(k=None, **ws) == 1
+    assert _dwrite(v=None, **ws) == 1
+    assert _dwrite(slots=None, **ws) == 1
+    assert _dwrite(tables=None, **ws) == 1
+    assert _dwrite(D=96, **ws) == 2
+    assert _dwrite(max_ctx=1000, **ws) == 2           # longer than the tables
+    assert _dwrite() == 4                             # no workspace
+    # nothing to do: no pointer is inspected
+    assert _dwrite(S=0, out=None, q=None, k=None, v=None, kc=None, vc=None, slots=None,
+                   tables=None, lens=None) == 0
+

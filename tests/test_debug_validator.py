@@ -160,3 +160,45 @@ def test_copy_on_write_destination_that_is_a_source():
     pairs = torch.tensor([[0, 3], [3, 5]], dtype=torch.int32)
     with pytest.raises(pkv.ContractError, match="both a source and a destination"):
         pkv.paged_kv_block_copy(pool, pool, pool, pool, pairs)
+
+
+def _decode_write(q, kc, tables, lens, slots, max_ctx):
+    S, _, D = q.shape
+    key = torch.zeros(S, kc.shape[1], D, dtype=kc.dtype)
+    pkv.paged_attention_decode_write(torch.empty_like(q), q, key, key, kc, kc, slots, tables,
+                                     lens, max_ctx, 0.125)
+
+
+def _newest(tables, lens, bs=16):
+    return torch.tensor([int(tables[i, (int(n) - 1) // bs]) * bs + (int(n) - 1) % bs
+                         for i, n in enumerate(lens)], dtype=torch.int32)
+
+
+def test_fused_write_slots_must_be_the_newest_positions():
+    q, kc, tables, lens = _decode_inputs()
+    slots = _newest(tables, lens)
+    _validate.check_newest_slots("t", slots, lens, tables, 16)  # passes
+    slots[1] += 1                                                # the next row of the block
+    with pytest.raises(pkv.ContractError, match=r"slot_mapping\[1\]"):
+        _decode_write(q, kc, tables, lens, slots, 40)
+
+
+def test_fused_write_to_an_empty_sequence():
+    q, kc, tables, lens = _decode_inputs(lens=(20, 0, 5))
+    slots = torch.tensor([int(_newest(tables, lens[:1])[0]), 7, -1], dtype=torch.int32)
+    slots[2] = int(tables[2, 0]) * 16 + 4
+    with pytest.raises(pkv.ContractError, match=r"sequence 1 writes slot 7"):
+        _decode_write(q, kc, tables, lens, slots, 40)
+
+
+def test_fused_write_negative_slots_write_nothing():
+    q, kc, tables, lens = _decode_inputs()
+    slots = _newest(tables, lens)
+    slots[0] = -1
+    _validate.check_newest_slots("t", slots, lens, tables, 16)
+
+
+def test_fused_write_slot_count_matches_the_sequences():
+    q, kc, tables, lens = _decode_inputs()
+    with pytest.raises(pkv.ContractError, match=r"holds 2 slots for 3 sequences"):
+        _validate.check_newest_slots("t", torch.tensor([0, 1], dtype=torch.int32), lens, tables, 16)
