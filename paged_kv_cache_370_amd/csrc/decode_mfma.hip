@@ -928,6 +928,34 @@ __device__ __forceinline__ void merge_group(const MfmaParams& p, int group, int 
   }
 }
 
+// The fused write's share of an item (kModeDecodeWrite): the item holding a
+// sequence's newest position, in its first row chunk, copies the new K and
+// V rows of its KV head to their slot; lanes [0, PR) of wave 0 hold the K
+// row's 16-byte pieces and lanes [PR, 2 PR) the V row's.  The pieces are
+// requested with the item's block ids, so they have arrived when the item
+// stores them.
+template <typename CT, int D, int MODE>
+__device__ __forceinline__ bool copies_row(const Item& it, int wave, int lane) {
+  return MODE == kModeDecodeWrite && it.live && it.w.sub >= 0 && it.w.r0 == 0 && wave == 0 &&
+         lane < 2 * Geometry<CT, D>::PR;
+}
+
+template <typename CT, int D, int MODE>
+__device__ __forceinline__ uint4 fetch_new_row(const MfmaParams& p, const Item& it, int wave,
+                                               int lane) {
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (MODE == kModeDecodeWrite) {
+    if (copies_row<CT, D, MODE>(it, wave, lane)) {
+      using CS = typename CT::storage;
+      constexpr int PR = Geometry<CT, D>::PR;
+      const CS* from = reinterpret_cast<const CS*>(lane >= PR ? p.new_v : p.new_k) +
+                       ((size_t)it.w.seq * p.H_kv + it.w.kvh) * D;
+      v = reinterpret_cast<const uint4*>(from)[lane % PR];
+    }
+  }
+  return v;
+}
+
 template <typename CT, int D, int BS, bool SCAN, int MODE>
 __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   using Gm = Geometry<CT, D>;
@@ -1008,6 +1036,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
   Item it{};
   int tab_first = 0;
   uint4 q_first = make_uint4(0u, 0u, 0u, 0u);
+  uint4 new_row = make_uint4(0u, 0u, 0u, 0u);  // the fused write's pieces of the item
   // Uniform: the first item is a full partition, found from the full
   // offsets alone; its block ids and Q are fetched and its first chunk's
   // loads issued before the sort of the last partitions, which then runs
@@ -1024,6 +1053,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
       it = decode_item<BS, SCAN, MODE>(p, first, Y, n_full, 0, order);
       tab_first = fetch_tab<CT, D, BS, MODE>(p, it.w, wave, lane);
       q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
+      new_row = fetch_new_row<CT, D, MODE>(p, it, wave, lane);
       store_tab(tab_first, s_wtab[wave], lane);  // the wave's own slice
       wave_lds_sync();
       const int nvalid = (it.w.end - it.w.start + Gm::CHUNK - 1) / Gm::CHUNK;
@@ -1058,6 +1088,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     it = decode_item<BS, SCAN, MODE>(p, min(cur, total - 1), Y, n_full, total - n_pre, order);
     tab_first = fetch_tab<CT, D, BS, MODE>(p, it.w, wave, lane);
     q_first = fetch_q<CT, D, MODE>(p, it.w, tid);
+    new_row = fetch_new_row<CT, D, MODE>(p, it, wave, lane);
   }
   if (cur < total) {
     if (!early) store_tab(tab_first, s_wtab[wave], lane);
@@ -1085,23 +1116,14 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     }
     prime = false;
     if constexpr (MODE == kModeDecodeWrite) {
-      // The fused write: the item holding a sequence's newest position
-      // (its first row chunk) copies the new K and V rows of its KV head to
-      // their slot.  Nothing in this launch reads that slot: the items over
-      // the position take the rows from new_k / new_v.  After the first
-      // chunk's loads, so the copy's wait is the one the first step makes.
-      if (it.live && it.w.sub >= 0 && it.w.r0 == 0 && wave == 0) {
-        constexpr int PR = Gm::PR;  // 16-byte pieces per row
-        if (lane < 2 * PR) {
-          const int slot = p.slots[it.w.seq];
-          const size_t dst = (((size_t)(slot / BS) * p.H_kv + it.w.kvh) * BS + slot % BS) * D;
-          const size_t srow = ((size_t)it.w.seq * p.H_kv + it.w.kvh) * D;
-          using CS = typename CT::storage;
-          const bool isv = lane >= PR;
-          const CS* from = reinterpret_cast<const CS*>(isv ? p.new_v : p.new_k) + srow;
-          CS* to = const_cast<CS*>(reinterpret_cast<const CS*>(isv ? p.vc : p.kc)) + dst;
-          reinterpret_cast<uint4*>(to)[lane % PR] = reinterpret_cast<const uint4*>(from)[lane % PR];
-        }
+      // The fused write's store (nothing in this launch reads the slot: the
+      // items over the position take the rows from new_k / new_v).
+      if (copies_row<CT, D, MODE>(it, wave, lane)) {
+        using CS = typename CT::storage;
+        const int slot = p.slots[it.w.seq];
+        const size_t dst = (((size_t)(slot / BS) * p.H_kv + it.w.kvh) * BS + slot % BS) * D;
+        CS* to = const_cast<CS*>(reinterpret_cast<const CS*>(lane >= Gm::PR ? p.vc : p.kc)) + dst;
+        reinterpret_cast<uint4*>(to)[lane % Gm::PR] = new_row;
       }
     }
     // The claim of the next item, made at the start of wave 0's last step
@@ -1225,6 +1247,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
         pg >= 0 && __builtin_amdgcn_readfirstlane(s_red[0] | s_red[1] | s_red[2] | s_red[3]);
     const Item ni =
         decode_item<BS, SCAN, MODE>(p, min(nn, total - 1), Y, n_full, total - n_pre, order);
+    const uint4 row_nn = fetch_new_row<CT, D, MODE>(p, ni, wave, lane);
     const int tab_nn = fetch_tab<CT, D, BS, MODE>(p, ni.w, wave, lane);
     const uint4 q_nn = fetch_q<CT, D, MODE>(p, ni.w, tid);
 
@@ -1307,6 +1330,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(MfmaParams p) {
     // X), then, at the loop's top, every wave's first chunk.
     cur = nn;
     it = ni;
+    new_row = row_nn;
     if (cur < total) {
       store_tab(tab_nn, s_wtab[wave], lane);
       store_q<CT, D>(q_nn, it.w, s_qf, tid);
