@@ -331,7 +331,7 @@ def measure_decode(pkv, torch, timer, w, ps, steps, warmup, traffic_key):
                                          w.max_context_len, qc, cc, ps)
     dws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")  # counters start at 0
     wws_bytes = pkv.write_workspace_size(max(len(x[2]) for x in writes), w.H_kv, w.num_blocks, cc)
-    wws = torch.empty(max(wws_bytes, 1), dtype=torch.uint8, device="cuda") if wws_bytes else None
+    wws = torch.zeros(wws_bytes, dtype=torch.uint8, device="cuda") if wws_bytes else None
 
     res = {"workload": w.name, "seqs": w.S, "q_heads": w.H, "kv_heads": w.H_kv,
            "head_size": w.D, "block_size": w.block_size, "cache": w.cache_dtype,
@@ -661,7 +661,7 @@ def prefill_bench(pkv, torch, name, reps):
                                       1, cc, 0)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     wws_bytes = pkv.write_workspace_size(max(len(x[2]) for x in writes), w.H_kv, w.num_blocks, cc)
-    wws = torch.empty(wws_bytes, dtype=torch.uint8, device=dev) if wws_bytes else None
+    wws = torch.zeros(wws_bytes, dtype=torch.uint8, device=dev) if wws_bytes else None
     # FP8 caches: the positions before the chunk are written once, untimed
     for k, v, s in writes[:-1]:
         pkv.paged_kv_cache_write(k, v, kc, vc, s, ks, vs, workspace=wws)
@@ -760,7 +760,7 @@ def beam_fork_bench(pkv, torch, name, reps):
                                       1, cc, 0)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     wws_bytes = pkv.write_workspace_size(max(len(x[2]) for x in writes), w.H_kv, w.num_blocks, cc)
-    wws = torch.empty(wws_bytes, dtype=torch.uint8, device=dev) if wws_bytes else None
+    wws = torch.zeros(wws_bytes, dtype=torch.uint8, device=dev) if wws_bytes else None
     # FP8 caches: the positions before the chunk are written once, untimed
     for k, v, s in writes[:-1]:
         pkv.paged_kv_cache_write(k, v, kc, vc, s, ks, vs, workspace=wws)

@@ -93,7 +93,9 @@ typedef enum {
  *     the E4M3FN code of the float32 quotient x / scale, rounded to nearest
  *     even, saturated to +-448 (NaN -> 0x7F).  A block's first write must
  *     include its offset 0.  Requires workspace of at least
- *     paged_kv_cache_write_workspace_size(...) bytes (any contents).
+ *     paged_kv_cache_write_workspace_size(...) bytes, zero before the first
+ *     call that uses it (allocate it zero-filled); every call leaves it zero
+ *     again, and calls that may run at the same time must not share it.
  *
  * Slots within one call must be distinct; duplicate slots race.
  * num_tokens == 0 returns PKV_OK after the size and dtype checks without

@@ -163,12 +163,15 @@ def paged_kv_cache_write(key, value, key_cache, value_cache, slot_mapping, key_s
     _contig(key, value, key_cache, value_cache, slot_mapping, key_scale, value_scale)
     T, H_kv, D = key.shape
     num_blocks, _, bs, _ = key_cache.shape
+    cdt = dtype_code(key_cache)
     if _v.enabled():
         _v.check_slots("paged_kv_cache_write", slot_mapping, num_blocks, bs)
-    cdt = dtype_code(key_cache)
+        if cdt == PKV_FP8_E4M3:
+            _v.check_write_workspace("paged_kv_cache_write", workspace)
     if workspace is None:
         need = write_workspace_size(T, H_kv, num_blocks, cdt)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=key.device) if need else None
+        # zero-filled: the library's per-block entries start (and end) at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=key.device) if need else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load().paged_kv_cache_write(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
                                      _ptr(key_scale), _ptr(value_scale), _ptr(slot_mapping), T,

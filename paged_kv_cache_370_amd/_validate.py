@@ -132,6 +132,22 @@ def check_newest_slots(where, slot_mapping, context_lens, block_tables, block_si
                                 f"{want} of the sequence's newest position {n - 1}")
 
 
+def check_write_workspace(where, workspace):
+    """An FP8 write's workspace holds per-block entries that must be zero at
+    the call (every call leaves them zero): a non-zero count or maximum would
+    give a block a wrong scale."""
+    if workspace is None:
+        return
+    if isinstance(workspace, np.ndarray):
+        data = workspace.reshape(-1).view(np.uint8)
+    else:
+        import torch
+        data = workspace.reshape(-1).view(torch.uint8).cpu().numpy()
+    if np.any(data != 0):
+        raise ContractError(f"{where}: the FP8 write workspace must be zero at the call (byte "
+                            f"{_first(data != 0)} is {int(data[_first(data != 0)])})")
+
+
 def check_block_pairs(where, block_pairs, src_blocks, dst_blocks, same_pool):
     pairs = _host(block_pairs).astype(np.int64).reshape(-1, 2)
     src, dst = pairs[:, 0], pairs[:, 1]

@@ -49,27 +49,20 @@ int pool_slots(const WriteArgs& a) {
 }
 
 // ---------------------------------------------------------------- FP8 path
-// Workspace: fresh[num_blocks] (int32) then amax[num_blocks][H_kv][2]
-// (float bits; index 0 = K, 1 = V).  Three launches:
-//   1. clear the entries of every block this call touches;
-//   2. mark blocks whose offset 0 is written ("fresh") and take amax per
-//      (block, KV head, K|V) with atomicMax on the float bits (non-negative
-//      floats order like their unsigned bit patterns);
-//   3. pick the scale (fresh: from amax; else the stored one) and encode.
-
-// One thread per token (tokens of one block write the same zeros).
-__global__ __launch_bounds__(256) void fp8_clear_kernel(
-    const int32_t* __restrict__ slots, int T, int bs, int H_kv, int num_slots,
-    int32_t* __restrict__ fresh, uint32_t* __restrict__ amax) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  const int s = slots[t];
-  if (s < 0 || s >= num_slots) return;
-  const int b = s / bs;
-  uint32_t* a = amax + (size_t)b * 2 * H_kv;
-  for (int i = 0; i < 2 * H_kv; ++i) a[i] = 0u;
-  fresh[b] = 0;
-}
+// Workspace: one entry per (block, KV head) of four 32-bit words: amax of K
+// and of V (float bits), the call's rows in it, and "fresh" (its offset 0 is
+// written).  All zero between calls.  Two launches:
+//   1. per (token, KV head) row: atomicMax of the row's |K| and |V| on the
+//      float bits (non-negative floats order like their unsigned bit
+//      patterns), count the row in, and mark the entry fresh at offset 0;
+//   2. per row: pick the scale (fresh: from amax; else the stored one) and
+//      encode; then count the row out, and the entry's last row returns it
+//      to zero.  A row counts out only after its own read of the entry has
+//      returned (an explicit wait), so the last one clears it after every
+//      read; no cache maintenance is needed (the entry's words change only
+//      at the L2, by atomics and by the last row's store).
+constexpr int kEntryWords = 4;  // amax K, amax V, rows, fresh
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt not waited for
 
 // Row geometry of the FP8 write kernels: a lane handles VEC consecutive
 // source elements (one 16-byte load), LPR lanes cover a (token, KV head) row
@@ -113,7 +106,7 @@ template <typename ST, int D>
 __global__ __launch_bounds__(256) void fp8_amax_kernel(
     const ST* __restrict__ key, const ST* __restrict__ value,
     const int32_t* __restrict__ slots, int T, int bs, int H_kv, int num_slots,
-    int32_t* __restrict__ fresh, uint32_t* __restrict__ amax) {
+    uint32_t* __restrict__ entries) {
   using R = Fp8Rows<ST, D>;
   const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
@@ -144,9 +137,11 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(
     const int o = s - b * bs;
     const uint32_t bk = nk > 0.f ? 0x7fc00000u : __float_as_uint(mk);
     const uint32_t bv = nv > 0.f ? 0x7fc00000u : __float_as_uint(mv);
-    atomicMax(&amax[((size_t)b * H_kv + h) * 2 + 0], bk);
-    atomicMax(&amax[((size_t)b * H_kv + h) * 2 + 1], bv);
-    if (o == 0 && h == 0) fresh[b] = 1;
+    uint32_t* e = entries + ((size_t)b * H_kv + h) * kEntryWords;
+    atomicMax(&e[0], bk);
+    atomicMax(&e[1], bv);
+    atomicAdd(&e[2], 1u);
+    if (o == 0) atomicOr(&e[3], 1u);
   }
 }
 
@@ -165,7 +160,7 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(
     uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
     float* __restrict__ key_scale, float* __restrict__ value_scale,
     const int32_t* __restrict__ slots, int T, int bs, int H_kv, int num_slots,
-    const int32_t* __restrict__ fresh, const uint32_t* __restrict__ amax) {
+    uint32_t* __restrict__ entries) {
   using R = Fp8Rows<ST, D>;
   const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
@@ -183,9 +178,11 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(
   load_src<ST>(key + (size_t)row * D + part * R::VEC, xk);
   load_src<ST>(value + (size_t)row * D + part * R::VEC, xv);
   float sk, sv;
-  if (fresh[b]) {
-    sk = fp8_scale_from_amax(amax[sidx * 2 + 0]);
-    sv = fp8_scale_from_amax(amax[sidx * 2 + 1]);
+  uint32_t* e = entries + sidx * kEntryWords;
+  const uint4 ent = *reinterpret_cast<const uint4*>(e);  // amax K, amax V, rows, fresh
+  if (ent.w) {
+    sk = fp8_scale_from_amax(ent.x);
+    sv = fp8_scale_from_amax(ent.y);
     if (part == 0) {  // every token of the block stores the same value
       key_scale[sidx] = sk;
       value_scale[sidx] = sv;
@@ -193,6 +190,14 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(
   } else {
     sk = key_scale[sidx];
     sv = value_scale[sidx];
+  }
+  if (part == 0) {
+    // Count the row out once the wave's read of the entry has returned;
+    // the entry's last row returns it to zero for the next call.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    asm volatile("" ::: "memory");
+    if (atomicSub(&e[2], 1u) == 1u) *reinterpret_cast<uint4*>(e) = make_uint4(0u, 0u, 0u, 0u);
   }
   // Correctly rounded float32 quotient: the double quotient rounded once more
   // to float equals the float quotient (53 >= 2*24 + 2).
@@ -220,30 +225,26 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(
 
 template <typename ST, int D>
 hipError_t fp8_launch(const WriteArgs& a) {
-  int32_t* fresh = reinterpret_cast<int32_t*>(a.workspace);
-  uint32_t* amax = reinterpret_cast<uint32_t*>(fresh + ((a.num_blocks + 63) / 64) * 64);
+  uint32_t* entries = reinterpret_cast<uint32_t*>(a.workspace);
   const ST* key = reinterpret_cast<const ST*>(a.key);
   const ST* value = reinterpret_cast<const ST*>(a.value);
   const int num_slots = pool_slots(a);  // slots past the pool are skipped
-  hipLaunchKernelGGL(fp8_clear_kernel, dim3((a.T + 255) / 256), dim3(256), 0, a.stream, a.slots,
-                     a.T, a.bs, a.H_kv, num_slots, fresh, amax);
   const int rows = a.T * a.H_kv;
   const int waves = (rows + Fp8Rows<ST, D>::RPW - 1) / Fp8Rows<ST, D>::RPW;
   const int blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((fp8_amax_kernel<ST, D>), dim3(blocks), dim3(256), 0, a.stream, key, value,
-                     a.slots, a.T, a.bs, a.H_kv, num_slots, fresh, amax);
+                     a.slots, a.T, a.bs, a.H_kv, num_slots, entries);
   hipLaunchKernelGGL((fp8_quant_kernel<ST, D>), dim3(blocks), dim3(256), 0, a.stream, key, value,
                      reinterpret_cast<uint8_t*>(a.key_cache),
                      reinterpret_cast<uint8_t*>(a.value_cache), a.key_scale, a.value_scale,
-                     a.slots, a.T, a.bs, a.H_kv, num_slots, fresh, amax);
+                     a.slots, a.T, a.bs, a.H_kv, num_slots, entries);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t kv_write_fp8_workspace(int num_blocks, int H_kv) {
-  const size_t fresh = ((size_t)(num_blocks + 63) / 64) * 64 * sizeof(int32_t);
-  return fresh + (size_t)num_blocks * H_kv * 2 * sizeof(uint32_t);
+  return (size_t)num_blocks * H_kv * kEntryWords * sizeof(uint32_t);
 }
 
 hipError_t launch_kv_write_copy(const WriteArgs& a) {

@@ -202,3 +202,11 @@ def test_fused_write_slot_count_matches_the_sequences():
     q, kc, tables, lens = _decode_inputs()
     with pytest.raises(pkv.ContractError, match=r"holds 2 slots for 3 sequences"):
         _validate.check_newest_slots("t", torch.tensor([0, 1], dtype=torch.int32), lens, tables, 16)
+
+
+def test_fp8_write_workspace_must_be_zero():
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    _validate.check_write_workspace("t", ws)
+    ws[100] = 3
+    with pytest.raises(pkv.ContractError, match=r"byte 100 is 3"):
+        _validate.check_write_workspace("t", ws)
