@@ -12,9 +12,9 @@
 //     (two 16-row MFMA groups that share every K and V fragment read; or, by
 //     kGroups, 8 waves of 16 rows);
 //   * the workgroup walks its keys in chunks of 64: K and V rows are gathered
-//     through the block table straight into LDS by global_load_lds (no
-//     register staging), double-buffered so chunk c+1 streams in while chunk
-//     c is multiplied;
+//     through the block table straight into LDS by loads to LDS (no register
+//     staging), double-buffered so chunk c+1 streams in while chunk c is
+//     multiplied;
 //   * S^T = K . Q^T and O^T += V^T . P^T on v_mfma_f32_16x16x32_bf16, with
 //     the online softmax between them in registers (the decode kernel's
 //     formulation: a lane holds one row, so row reductions are two swizzles);
@@ -242,6 +242,14 @@ struct Layout {
   __device__ static __forceinline__ int vswz(int k) { return 2 * ((k / RB) & (PR / 2 - 1)); }
 };
 
+// Buffer descriptor of one cache block's (KV head) tile: base, no stride,
+// records up to 2^31 bytes (a tile is at most 8 KiB), and the gfx9 word 3
+// (raw buffer: 32-bit data, no format conversion).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+
 // Gathers keys c0 .. c0 + kKC - 1 of KV head kvh into buffer `buf` (K and V
 // tiles).  Wave w of NW, round i fills bytes [(NW i + w) KiB, +1 KiB) of each
 // tile, lane l the physical piece 64 (NW i + w) + l, and fetches the logical piece
@@ -272,8 +280,12 @@ __device__ __forceinline__ void issue_chunk(char* buf, const PrefillParams& p, u
       const char* kb = reinterpret_cast<const char*>(p.kc) + rb;
       const char* vb = reinterpret_cast<const char*>(p.vc) + rb;
       const int lds = (i * L::NW + wave) * 1024;
-      __builtin_amdgcn_global_load_lds(kb + koff[i], (lds_void*)(buf + lds), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + voff[i], (lds_void*)(buf + L::TILE + lds), 16, 0, 0);
+      // Buffer loads: the block's base in a scalar descriptor, the lane's
+      // 32-bit offset as is (no 64-bit vector address arithmetic).
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(block_rsrc(kb), (lds_void*)(buf + lds), 16, koff[i],
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(block_rsrc(vb), (lds_void*)(buf + L::TILE + lds), 16,
+                                               voff[i], 0, 0, 0);
     }
     return;
   }
