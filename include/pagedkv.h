@@ -20,10 +20,10 @@
  *     row-major and densely packed in the layouts given below.
  *   - The caller owns and allocates every buffer, including the pool and the
  *     workspace; the library allocates and frees nothing and keeps no state
- *     between calls other than what a workspace holds.  Workspaces are
- *     256-byte aligned (as hipMalloc returns them); the other arrays are
- *     aligned to 16 bytes (rows of the caches, queries and new K/V are read
- *     and written 16 bytes at a time).
+ *     between calls other than what a workspace holds.  Arrays are 16-byte
+ *     aligned (hipMalloc returns 256): rows of the caches, queries and new
+ *     K/V are read and written 16 bytes at a time, and so are parts of the
+ *     workspaces (a workspace that is not is PKV_ERR_WORKSPACE).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and the call returns without synchronising.  Buffers must stay alive
  *     until the stream has passed the call.  Calls are thread-safe.

@@ -150,7 +150,7 @@ DecodeSetup setup_decode(void* out, const void* query, const void* key_cache,
     }
   }
   const size_t need = decode_workspace(S, H, D, max_ctx, P, M);
-  if (!workspace || workspace_bytes < need) {
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0) {
     r.status = PKV_ERR_WORKSPACE;
     return r;
   }
@@ -222,7 +222,8 @@ pkv_status_t paged_kv_cache_write(const void* key, const void* value, void* key_
   if (fp8 && (!key_scale || !value_scale)) return PKV_ERR_NULL;
   if (fp8) {
     const size_t need = kv_write_fp8_workspace(num_blocks, num_kv_heads);
-    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return PKV_ERR_WORKSPACE;
   }
   WriteArgs a;
   a.key = key; a.value = value; a.key_cache = key_cache; a.value_cache = value_cache;

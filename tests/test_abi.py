@@ -307,3 +307,13 @@ def test_decode_write_argument_checks():
     assert _dwrite(S=0, out=None, q=None, k=None, v=None, kc=None, vc=None, slots=None,
                    tables=None, lens=None) == 0
 
+
+
+def test_misaligned_workspaces_are_refused():
+    """Workspaces are read and written 16 bytes at a time: a pointer that is
+    not 16-byte aligned is PKV_ERR_WORKSPACE, before any launch."""
+    odd = ctypes.c_void_p(0x1008)
+    assert _decode(max_ctx=128, ps=16, ws=odd, wsb=1 << 20) == 4
+    assert _write(sd=1, cd=2, ks=FAKE, vs=FAKE, ws=odd, wsb=1 << 20) == 4
+    assert _prefill(M=16, ws=odd, wsb=1 << 24) == 4
+    assert _dwrite(ws=odd, wsb=1 << 20) == 4
