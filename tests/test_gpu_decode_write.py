@@ -156,3 +156,16 @@ def test_timed_workloads_bitwise(cfg):
     two, one = _both(w, w.partition_size)
     _assert_same(two, one, w.name)
     _say("  bitwise equal")
+
+
+@pytest.mark.parametrize("ps", [0, 64])
+def test_batch_beyond_the_scan_limit(ps):
+    """More sequences than the decode kernel sorts in LDS (512): its plain
+    item order, with the fused write, equals the two calls bit for bit."""
+    rng = np.random.default_rng(61)
+    lens = rng.integers(1, 300, size=600)
+    w = workloads.build_workload("dw-wide", 600, 8, 2, 128, 16, "bf16", "bf16", lens, 61)
+    _say(f"case 600 sequences ps={ps}")
+    two, one = _both(w, ps)
+    _assert_same(two, one, f"600 sequences ps {ps}")
+    _say("  bitwise equal")
