@@ -73,7 +73,29 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    _build_c_abi_program()
     return LIB
+
+
+# A C99 program that runs a decode step through the C ABI alone (its GPU test
+# checks it against the oracle); built beside the library.
+C_ABI_SRC = os.path.join(ROOT, "tests", "c_abi_decode.c")
+C_ABI_EXE = os.path.join(PKG, "c_abi_decode")
+
+
+def _build_c_abi_program() -> None:
+    if not os.path.exists(C_ABI_SRC):
+        return
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = C_ABI_EXE + ".tmp"
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(rocm, "include"), C_ABI_SRC,
+           "-o", tmp, "-L" + PKG, "-l:libpagedkv.so", "-Wl,-rpath,$ORIGIN",
+           "-L" + os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C ABI program failed to build:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, C_ABI_EXE)
 
 
 if __name__ == "__main__":
