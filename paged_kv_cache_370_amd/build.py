@@ -84,7 +84,7 @@ C_ABI_EXE = os.path.join(PKG, "c_abi_decode")
 
 
 def _build_c_abi_program() -> None:
-    if not os.path.exists(C_ABI_SRC):
+    if not os.path.exists(C_ABI_SRC) or shutil.which("gcc") is None:
         return
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     tmp = C_ABI_EXE + ".tmp"
